@@ -1,0 +1,423 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU reference for the scaled FP8
+ * down-projection path (fused activation + BF16 copy + scaled FP8 cast +
+ * running amax + saturation count, delayed-scaling history, scaled FP8 GEMM).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * never calls it, and it shares no code, header, table or constant generator
+ * with the HIP library: every rule below is written out again from its
+ * definition.
+ *
+ * Sources (page title -- section):
+ *   [FP8T] "FP8 training: what it is and how it works"
+ *          -- "FP8 training from first principles" (definitions of scaling
+ *             factor and amax), "Step 1: Choose the 8-bit format",
+ *             "Step 2: Scale the tensor into range", "Step 3: Multiply in FP8
+ *             and add up in higher precision", "Trade-offs and edge cases".
+ *   [FP8I] "FP8 Training & Inference"
+ *          -- "FP8 Formats: E4M3 vs E5M2", "Per-Tensor Scaling for FP8",
+ *             "Delayed Scaling".
+ *   [PARA] "Paradigma Details FP8 and Optimizer Tricks Behind NanoGPT
+ *          Records" -- the fused-kernel paragraph (BF16 copy, FP8 copy,
+ *          running maxima, previous step's amax times a safety margin).
+ *   [PRE]  "Pretraining at scale" -- 4a "What a floating-point number is"
+ *          (sign/exponent/fraction value formula, round to nearest,
+ *          subnormals, underflow below half the smallest subnormal).
+ *
+ * Precision: the formats are bit-exact definitions; the scale and the scaled
+ * value are computed in IEEE binary32 with round-to-nearest-even (the
+ * precision the kernel uses, one operation at a time, no fused multiply-add);
+ * the GEMM reference is float64 over the dequantized codes.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (see oracle/build.py).  No threads, no SIMD intrinsics.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_E4M3 0
+#define ORC_E5M2 1
+#define ORC_ACT_IDENTITY 0
+#define ORC_ACT_RELU2 1
+#define ORC_PER_TENSOR 0
+#define ORC_PER_GROUP128 1
+#define ORC_GROUP 128
+#define ORC_MAX_HIST 16
+
+/* ------------------------------------------------------------------------ */
+/* Format description.  [FP8T] Step 1 and [FP8I] "FP8 Formats": E4M3 is      */
+/* 1 sign + 4 exponent + 3 mantissa bits, largest value 448, no infinity;    */
+/* E5M2 is 1 + 5 + 2 bits, largest value 57344, with infinities.  Biases are */
+/* the usual 2^(ebits-1) - 1.                                               */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int ebits, mbits, bias;
+  int emin;          /* exponent of the smallest normal binade: 1 - bias    */
+  double maxval;     /* largest finite magnitude                             */
+  uint8_t max_code;  /* code (without sign) of the largest finite magnitude  */
+} orc_format;
+
+static orc_format orc_fmt(int fmt) {
+  orc_format f;
+  if (fmt == ORC_E4M3) {
+    f.ebits = 4; f.mbits = 3; f.bias = 7;
+    /* 0x7F is the NaN pattern, so the largest finite code is 0x7E:
+       exponent field 15, mantissa 6 -> 2^8 * 1.75 = 448. */
+    f.max_code = 0x7E;
+  } else {
+    f.ebits = 5; f.mbits = 2; f.bias = 15;
+    /* exponent field 31 is infinity/NaN, so the largest finite code is
+       exponent 30, mantissa 3 -> 2^15 * 1.75 = 57344. */
+    f.max_code = 0x7B;
+  }
+  f.emin = 1 - f.bias;
+  /* both maxima are 1.75 * 2^(top exponent field - bias): 2^8 and 2^15 */
+  f.maxval = ldexp(1.75, (fmt == ORC_E4M3 ? 15 : 30) - f.bias);
+  return f;
+}
+
+static uint32_t f2u(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float u2f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+/* Value of an FP8 code: (-1)^S * 2^(E - bias) * (1 + M / 2^mbits) for a
+   normal code, (-1)^S * 2^(1 - bias) * (M / 2^mbits) for a subnormal one
+   ([PRE] 4a gives the formula; [FP8T]/[FP8I] give the bit counts). */
+double oracle_fp8_decode(uint8_t code, int fmt) {
+  orc_format f = orc_fmt(fmt);
+  int sign = code >> 7;
+  int e = (code >> f.mbits) & ((1 << f.ebits) - 1);
+  int m = code & ((1 << f.mbits) - 1);
+  double v;
+  if (fmt == ORC_E4M3 && e == 15 && m == 7) return NAN;      /* S.1111.111 */
+  if (fmt == ORC_E5M2 && e == 31) {
+    if (m != 0) return NAN;
+    return sign ? -INFINITY : INFINITY;
+  }
+  if (e == 0)
+    v = ldexp((double)m / (1 << f.mbits), f.emin);
+  else
+    v = ldexp(1.0 + (double)m / (1 << f.mbits), e - f.bias);
+  return sign ? -v : v;
+}
+
+/* Round |x| (finite, double, exactly a binary32 value) to the format's grid,
+   ignoring the upper range limit: returns the grid multiple n and the
+   exponent e of the grid cell, so the rounded magnitude is n * 2^(e-mbits).
+   Round to nearest, ties to even n ([PRE] 4a: "rounds ... to the nearest
+   value"; ties to even is the IEEE default). */
+static void round_to_grid(double ax, const orc_format* f, int* e_out, double* n_out) {
+  int e;
+  if (ax == 0.0) {
+    e = f->emin;
+  } else {
+    (void)frexp(ax, &e);   /* ax = frac * 2^e, frac in [0.5, 1) */
+    e -= 1;                /* ax in [2^e, 2^(e+1)) */
+    if (e < f->emin) e = f->emin;   /* subnormal cells share the emin spacing */
+  }
+  double q = ldexp(1.0, e - f->mbits);
+  *n_out = nearbyint(ax / q);       /* exact division by a power of two */
+  *e_out = e;
+}
+
+/* Saturating round-to-nearest-even cast of a binary32 value to FP8.
+   NaN -> 0x7F with the sign kept; |x| >= max (infinity included) -> +-max;
+   otherwise the nearest grid value, which also gives signed zero for
+   |x| <= half the smallest subnormal (a tie there goes to the even code 0). */
+uint8_t oracle_fp8_encode(float x, int fmt) {
+  orc_format f = orc_fmt(fmt);
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  double ax = fabs((double)x);
+  if (ax >= f.maxval) return sign | f.max_code;
+  int e; double n;
+  round_to_grid(ax, &f, &e, &n);
+  int full = 1 << f.mbits;
+  int ni = (int)n;                  /* 0 .. 2*full */
+  if (e == f.emin && ni < full) return sign | (uint8_t)ni;   /* subnormal or zero */
+  if (ni == 2 * full) { e += 1; ni = full; }                  /* carried into next binade */
+  int efield = e + f.bias;
+  return sign | (uint8_t)((efield << f.mbits) | (ni - full));
+}
+
+/* Saturation predicate: the value is counted when a cast that does NOT
+   saturate would have produced a non-finite result, i.e. when |x| is infinite
+   or its unbounded round-to-nearest-even rounding lies above the format
+   maximum.  NaN inputs are not counted ([FP8I] "Delayed Scaling": overflow is
+   what the safety check must detect). */
+int oracle_fp8_saturates(float x, int fmt) {
+  orc_format f = orc_fmt(fmt);
+  if (isnan(x)) return 0;
+  if (isinf(x)) return 1;
+  double ax = fabs((double)x);
+  if (ax <= f.maxval) return 0;
+  int e; double n;
+  round_to_grid(ax, &f, &e, &n);
+  return ldexp(n, e - f.mbits) > f.maxval;
+}
+
+/* BF16 (1 sign + 8 exponent + 7 fraction bits, [PRE] 4a) round to nearest,
+   ties to even, from binary32.  NaN keeps its sign and top payload bits and
+   is made quiet; overflow rounds to infinity as IEEE rounding does. */
+uint16_t oracle_bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040);
+  double ax = fabs((double)x);
+  int sign = (u >> 31) != 0;
+  if (isinf(x)) return (uint16_t)(sign ? 0xFF80 : 0x7F80);
+  int e;
+  if (ax == 0.0) {
+    e = -126;
+  } else {
+    (void)frexp(ax, &e);
+    e -= 1;
+    if (e < -126) e = -126;                 /* binary32/BF16 subnormal range */
+  }
+  double q = ldexp(1.0, e - 7);             /* BF16 keeps 7 fraction bits */
+  double r = nearbyint(ax / q) * q;         /* exact in double */
+  float rf = (float)r;                      /* exact, or +inf past the top */
+  uint16_t out = (uint16_t)(f2u(rf) >> 16);
+  return sign ? (uint16_t)(out | 0x8000) : out;
+}
+
+float oracle_bf16_to_f32(uint16_t b) { return u2f((uint32_t)b << 16); }
+
+/* Scale rule ([FP8T] Step 2: scaling factor = format maximum / amax;
+   [PARA]: the amax used is the previous step's value times a safety
+   margin).  binary32 arithmetic: d = amax * margin, s = max / d.  A value of
+   d that is not a positive finite number, or a quotient that is not finite,
+   leaves nothing to scale by: the scale falls back to 1. */
+float oracle_scale_from_amax(float amax, float margin, int fmt) {
+  float fmax = (fmt == ORC_E4M3) ? 448.0f : 57344.0f;
+  float d = amax * margin;
+  float s = fmax / d;
+  if (!(d > 0.0f) || isinf(d) || !isfinite(s)) return 1.0f;
+  return s;
+}
+
+float oracle_recip_f32(float s) { float r = 1.0f / s; return r; }
+
+/* Activation applied to one BF16 input value, result rounded to BF16.
+   Identity keeps the input bits unchanged (no rounding step happens).
+   Squared ReLU: a = h*h when h > 0, else +0 (NaN and -0 give +0); the
+   product of two BF16 values is computed in binary32 and then rounded to
+   BF16 -- the copy written for the backward pass ([PARA]). */
+static uint16_t act_bf16(uint16_t h, int act) {
+  if (act == ORC_ACT_IDENTITY) return h;
+  float x = oracle_bf16_to_f32(h);
+  float a = (x > 0.0f) ? x * x : 0.0f;
+  return oracle_bf16_rne(a);
+}
+
+/* One quantization call over a row-major [rows x cols] BF16 tensor.
+ *   act  : ORC_ACT_IDENTITY / ORC_ACT_RELU2
+ *   mode : ORC_PER_TENSOR  -> every element is multiplied by `scale`
+ *          ORC_PER_GROUP128 -> each run of 128 consecutive elements of a row
+ *                              gets s_g = max / amax_g (current scaling,
+ *                              margin 1) and group_scale_inv[g] = 1 / s_g
+ *                              ([FP8T] "Fine-grained quantization"; the
+ *                              1-by-128 activation tile of "Trade-offs").
+ *   bf16_out, fp8_out, group_scale_inv may be NULL.
+ * Outputs amax as the binary32 bit pattern of max |b| (the maximum of the
+ * magnitude bit patterns, compared as unsigned integers), and the number of
+ * saturating elements.
+ */
+void oracle_quantize(const uint16_t* h, int64_t rows, int64_t cols, int act, int fmt, int mode,
+                     float scale, uint16_t* bf16_out, uint8_t* fp8_out, float* group_scale_inv,
+                     uint32_t* amax_bits_out, uint64_t* sat_out) {
+  int64_t n = rows * cols;
+  uint32_t amax = 0;
+  uint64_t sat = 0;
+  if (mode == ORC_PER_TENSOR) {
+    for (int64_t i = 0; i < n; ++i) {
+      uint16_t b = act_bf16(h[i], act);
+      if (bf16_out) bf16_out[i] = b;
+      uint32_t mag = ((uint32_t)(b & 0x7FFF)) << 16;
+      if (mag > amax) amax = mag;
+      float v = oracle_bf16_to_f32(b) * scale;
+      if (fp8_out) fp8_out[i] = oracle_fp8_encode(v, fmt);
+      sat += (uint64_t)oracle_fp8_saturates(v, fmt);
+    }
+  } else {
+    int64_t groups = n / ORC_GROUP;
+    for (int64_t g = 0; g < groups; ++g) {
+      const uint16_t* hg = h + g * ORC_GROUP;
+      uint32_t gmax = 0;
+      for (int j = 0; j < ORC_GROUP; ++j) {
+        uint32_t mag = ((uint32_t)(act_bf16(hg[j], act) & 0x7FFF)) << 16;
+        if (mag > gmax) gmax = mag;
+      }
+      if (gmax > amax) amax = gmax;
+      float sg = oracle_scale_from_amax(u2f(gmax), 1.0f, fmt);
+      if (group_scale_inv) group_scale_inv[g] = oracle_recip_f32(sg);
+      for (int j = 0; j < ORC_GROUP; ++j) {
+        uint16_t b = act_bf16(hg[j], act);
+        if (bf16_out) bf16_out[g * ORC_GROUP + j] = b;
+        float v = oracle_bf16_to_f32(b) * sg;
+        if (fp8_out) fp8_out[g * ORC_GROUP + j] = oracle_fp8_encode(v, fmt);
+        sat += (uint64_t)oracle_fp8_saturates(v, fmt);
+      }
+    }
+  }
+  if (amax_bits_out) *amax_bits_out = amax;
+  if (sat_out) *sat_out = sat;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Delayed scaling state ([PARA]: previous step's amax times a safety margin; */
+/* [FP8T] "Trade-offs": delayed scaling keeps a stored history of earlier    */
+/* amax values; [FP8I] "Delayed Scaling": detect overflow).                   */
+/* The history holds hist_len amax values; the scale for the next step uses  */
+/* the largest of them.                                                      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  float scale;            /* multiplier for the next step's cast             */
+  float scale_inv;        /* 1/scale                                          */
+  float scale_inv_used;   /* 1/scale of the step most recently consumed       */
+  uint32_t amax_acc;      /* running amax bits of the current step            */
+  uint64_t sat_acc;       /* running saturation count of the current step     */
+  uint64_t sat_last;      /* saturation count of the step most recently consumed */
+  uint32_t overflow;      /* 1 when that step saturated                       */
+  float margin;
+  int32_t hist_len;
+  int32_t hist_pos;
+  uint32_t steps;
+  int32_t fmt;
+  float history[ORC_MAX_HIST];
+} oracle_state;
+
+int64_t oracle_state_size(void) { return (int64_t)sizeof(oracle_state); }
+
+static float history_max(const oracle_state* st) {
+  uint32_t m = 0;
+  for (int i = 0; i < st->hist_len; ++i) {
+    uint32_t b = f2u(st->history[i]) & 0x7FFFFFFFu;
+    if (b > m) m = b;
+  }
+  return u2f(m);
+}
+
+int oracle_state_init(oracle_state* st, int fmt, int hist_len, float margin, float initial_amax) {
+  if (hist_len < 1 || hist_len > ORC_MAX_HIST) return -1;
+  memset(st, 0, sizeof(*st));
+  st->fmt = fmt;
+  st->margin = margin;
+  st->hist_len = hist_len;
+  for (int i = 0; i < hist_len; ++i) st->history[i] = initial_amax;
+  st->scale = oracle_scale_from_amax(history_max(st), margin, fmt);
+  st->scale_inv = oracle_recip_f32(st->scale);
+  st->scale_inv_used = st->scale_inv;
+  return 0;
+}
+
+/* Consume the step: record its amax in the history, publish the inverse of
+   the scale that step was cast with, derive the next scale, flag overflow,
+   and clear the running accumulators. */
+void oracle_history_update(oracle_state* st) {
+  st->history[st->hist_pos] = u2f(st->amax_acc);
+  st->hist_pos = (st->hist_pos + 1) % st->hist_len;
+  st->scale_inv_used = st->scale_inv;
+  st->scale = oracle_scale_from_amax(history_max(st), st->margin, st->fmt);
+  st->scale_inv = oracle_recip_f32(st->scale);
+  st->sat_last = st->sat_acc;
+  st->overflow = st->sat_acc > 0 ? 1u : 0u;
+  st->amax_acc = 0;
+  st->sat_acc = 0;
+  st->steps += 1;
+}
+
+/* Fold one quantization call's amax bits and saturation count into the state. */
+void oracle_state_accumulate(oracle_state* st, uint32_t amax_bits, uint64_t sat) {
+  if (amax_bits > st->amax_acc) st->amax_acc = amax_bits;
+  st->sat_acc += sat;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reference GEMM ([FP8T] Step 3: FP8 inputs, wide accumulation; [FP8I]      */
+/* "Per-Tensor Scaling": the scales are factored out of the product and the  */
+/* output is rescaled).                                                      */
+/*   a : [M x K] codes, b : [N x K] codes (row-major, K contiguous)           */
+/*   mode PER_TENSOR : sa[0], sb[0] are the cast multipliers s_a, s_b          */
+/*   mode PER_GROUP128: sa is [M x K/128] (one per 1x128 activation tile),    */
+/*                     sb is [N/128 x K/128] (one per 128x128 weight block)   */
+/* ref[m,n] = sum over 128-wide K blocks g (one block = all of K per tensor)  */
+/*            of S_g / (s_a * s_b), S_g = sum_k dec(a[m,k]) * dec(b[n,k]);   */
+/* absref likewise with |dec * dec|.  Rows listed in `rows` (nrows of them)  */
+/* are computed; rows == NULL means all M rows.                              */
+/* ------------------------------------------------------------------------ */
+void oracle_gemm_f64(const uint8_t* a, int fa, const uint8_t* b, int fb, int64_t M, int64_t N,
+                     int64_t K, int mode, const float* sa, const float* sb, const int64_t* rows,
+                     int64_t nrows, double* ref, double* absref) {
+  double da[256], db[256];
+  for (int c = 0; c < 256; ++c) {
+    da[c] = oracle_fp8_decode((uint8_t)c, fa);
+    db[c] = oracle_fp8_decode((uint8_t)c, fb);
+  }
+  int64_t count = rows ? nrows : M;
+  int64_t kg = (mode == ORC_PER_TENSOR) ? K : ORC_GROUP;
+  int64_t ngroups = K / kg;
+  for (int64_t r = 0; r < count; ++r) {
+    int64_t m = rows ? rows[r] : r;
+    const uint8_t* arow = a + m * K;
+    for (int64_t nn = 0; nn < N; ++nn) {
+      const uint8_t* brow = b + nn * K;
+      double total = 0.0, total_abs = 0.0;
+      for (int64_t g = 0; g < ngroups; ++g) {
+        double s = 0.0, sabs = 0.0;
+        for (int64_t k = g * kg; k < (g + 1) * kg; ++k) {
+          double p = da[arow[k]] * db[brow[k]];
+          s += p;
+          sabs += fabs(p);
+        }
+        double sa_v, sb_v;
+        if (mode == ORC_PER_TENSOR) {
+          sa_v = sa[0];
+          sb_v = sb[0];
+        } else {
+          sa_v = sa[m * ngroups + g];
+          sb_v = sb[(nn / ORC_GROUP) * ngroups + g];
+        }
+        double denom = sa_v * sb_v;
+        total += s / denom;
+        total_abs += sabs / denom;
+      }
+      ref[r * N + nn] = total;
+      if (absref) absref[r * N + nn] = total_abs;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batch helpers (the per-element functions above applied to arrays).        */
+/* ------------------------------------------------------------------------ */
+void oracle_fp8_encode_batch(const float* x, int64_t n, int fmt, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_encode(x[i], fmt);
+}
+
+void oracle_fp8_saturates_batch(const float* x, int64_t n, int fmt, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_fp8_saturates(x[i], fmt);
+}
+
+void oracle_bf16_rne_batch(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(x[i]);
+}
+
+void oracle_scale_batch(const float* amax, int64_t n, float margin, int fmt, float* scale,
+                        float* scale_inv) {
+  for (int64_t i = 0; i < n; ++i) {
+    scale[i] = oracle_scale_from_amax(amax[i], margin, fmt);
+    if (scale_inv) scale_inv[i] = oracle_recip_f32(scale[i]);
+  }
+}
+
+/* Encode every binary32 bit pattern in [lo, hi) (as uint32 values) and
+   write the codes; used to compare a device cast against all 2^32 inputs
+   in chunks. */
+void oracle_fp8_encode_range(uint64_t lo, uint64_t hi, int fmt, uint8_t* out) {
+  for (uint64_t u = lo; u < hi; ++u) out[u - lo] = oracle_fp8_encode(u2f((uint32_t)u), fmt);
+}
+
+void oracle_bf16_rne_range(uint64_t lo, uint64_t hi, uint16_t* out) {
+  for (uint64_t u = lo; u < hi; ++u) out[u - lo] = oracle_bf16_rne(u2f((uint32_t)u));
+}
