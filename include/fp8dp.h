@@ -1,0 +1,227 @@
+/*
+ * fp8dp.h -- C ABI of libfp8dp.so: scaled FP8 quantization for an MLP
+ * down-projection on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *
+ *  - "Paradigma Details FP8 and Optimizer Tricks Behind NanoGPT Records",
+ *    the FP8 section: one fused kernel applies the activation, writes the BF16
+ *    copy the backward pass needs, emits the FP8 copy and keeps small running
+ *    maxima, so the large tensor is never read again; the scale uses the
+ *    previous step's maximum times a safety margin (delayed scaling); the
+ *    down-projection then runs in FP8 in the forward pass only.
+ *  - "FP8 training: what it is and how it works", Step 1 (E4M3 max 448,
+ *    E5M2 max 57344), Step 2 (scale = format max / amax, applied before
+ *    rounding and divided out afterwards), Step 3 (FP8 inputs, wide
+ *    accumulation), Trade-offs (delayed scaling keeps a history of amaxes;
+ *    1 x 128 activation tiles and 128 x 128 weight blocks).
+ *  - "FP8 Training & Inference", FP8 Formats (E4M3 for weights/activations,
+ *    E5M2 for gradients), Per-Tensor Scaling (scales factored out of the
+ *    matmul, output rescaled), Delayed Scaling (detect overflow).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory; the library never allocates device memory.
+ *  - Every call is enqueued on `stream` and returns without waiting for the
+ *    GPU; outputs are valid once the stream reaches the call.
+ *  - Return value: 0 on success, FP8DP_EINVAL (-1) for an invalid argument,
+ *    FP8DP_EUNSUPPORTED (-2) for an unsupported combination, FP8DP_EHIP (-3)
+ *    when a HIP launch fails.  fp8dp_last_error() describes the last failure
+ *    of the calling thread.  Nothing is enqueued when a call fails argument
+ *    checks.
+ *  - BF16 values are passed as uint16_t bit patterns, FP8 values as uint8_t
+ *    codes (OCP E4M3 "fn" or OCP E5M2), scales as IEEE binary32.
+ *  - Matrices are row-major.  Vector I/O needs every tensor pointer to be
+ *    16-byte aligned.
+ */
+#ifndef FP8DP_H
+#define FP8DP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8DP_OK 0
+#define FP8DP_EINVAL (-1)
+#define FP8DP_EUNSUPPORTED (-2)
+#define FP8DP_EHIP (-3)
+
+/* OCP E4M3 (1/4/3 bits, bias 7, max 448, no infinity, NaN = S.1111.111) and
+   OCP E5M2 (1/5/2 bits, bias 15, max 57344, with infinities). */
+typedef enum { FP8DP_E4M3 = 0, FP8DP_E5M2 = 1 } fp8dp_format;
+
+/* Activation applied before the copies are written.  RELU2: a = h*h for
+   h > 0, else +0 (NaN and -0 give +0), rounded to BF16 nearest-even.
+   IDENTITY: the input value unchanged. */
+typedef enum { FP8DP_ACT_IDENTITY = 0, FP8DP_ACT_RELU2 = 1 } fp8dp_act;
+
+/* PER_TENSOR: one multiplier for the whole tensor, read from the delayed-
+   scaling state.  PER_GROUP128: each run of 128 consecutive elements of a row
+   gets its own multiplier max / amax_group computed in the kernel (current
+   scaling, no margin); weights use 128 x 128 blocks. */
+typedef enum { FP8DP_PER_TENSOR = 0, FP8DP_PER_GROUP128 = 1 } fp8dp_scale_mode;
+
+#define FP8DP_MAX_HIST 16
+#define FP8DP_ACC_SLOTS 64
+
+/* One running-accumulator slot (64 bytes).  Quantization calls fold their
+   results into slot (block index % FP8DP_ACC_SLOTS) with one atomic max and
+   one atomic add per thread block; amax_history_update reduces the slots. */
+typedef struct fp8dp_acc_slot {
+  uint32_t amax;      /* binary32 bits of the running max |b| (unsigned compare) */
+  uint32_t reserved0;
+  uint64_t sat;       /* running count of saturating elements */
+  uint8_t reserved[48];
+} fp8dp_acc_slot;
+
+/* Delayed-scaling state of one tensor (4288 bytes, 64-byte aligned, in
+   device memory; allocate it, e.g. as a uint8 tensor, and initialise it with
+   fp8dp_state_init).  It is plain data: copying it out and back resumes the
+   scaling sequence exactly. */
+typedef struct fp8dp_tensor_state {
+  float scale;            /* multiplier the next PER_TENSOR cast uses            */
+  float scale_inv;        /* binary32 1/scale                                     */
+  float scale_inv_used;   /* 1/scale of the step most recently consumed           */
+  uint32_t overflow;      /* 1 when the step most recently consumed saturated     */
+  uint64_t sat_last;      /* saturation count of that step                        */
+  float amax_last;        /* amax of that step                                    */
+  float margin;           /* safety margin (1.0 = plain current-style scale)      */
+  int32_t hist_len;       /* 1 .. FP8DP_MAX_HIST amax values kept                  */
+  int32_t hist_pos;       /* ring position of the next history write              */
+  uint32_t steps;         /* steps consumed so far                                */
+  int32_t fmt;            /* fp8dp_format the state was initialised for           */
+  float history[FP8DP_MAX_HIST];
+  uint8_t reserved[80];   /* pads the header to 192 bytes: acc starts on a 64-byte line */
+  fp8dp_acc_slot acc[FP8DP_ACC_SLOTS];   /* running accumulators of the current step */
+} fp8dp_tensor_state;
+
+/* Size in bytes of fp8dp_tensor_state (for callers allocating raw bytes). */
+int64_t fp8dp_state_size(void);
+
+/* Initialise a state: history filled with initial_amax, accumulators zeroed,
+   scale = max / (initial_amax * margin) (1.0 if that is not a positive finite
+   number), scale_inv = 1/scale.  Runs as a one-thread kernel on `stream`.
+   Errors: EINVAL for st == NULL, misaligned st, bad fmt, hist_len outside
+   1..FP8DP_MAX_HIST, or a margin that is not positive and finite. */
+int fp8dp_state_init(fp8dp_tensor_state* st, fp8dp_format fmt, int32_t hist_len, float margin,
+                     float initial_amax, hipStream_t stream);
+
+/* The fused quantizer (the Paradigma FP8 kernel; "FP8 training ...", Step 2).
+ *   h        [rows x cols] BF16 input (pre-activation), contiguous
+ *   act      activation applied first
+ *   fmt      FP8 output format
+ *   mode     PER_TENSOR: every element b is cast as sat_rne(b * st->scale)
+ *            PER_GROUP128: cols % 128 == 0; group g (128 consecutive elements
+ *            of a row) is cast with s_g = max / amax_g and
+ *            group_scale_inv[g] = 1/s_g is written, [rows x cols/128] row-major
+ *   st       PER_TENSOR: required (its scale is read); PER_GROUP128: optional.
+ *            When given, the call folds max |b| and the number of saturating
+ *            elements into st's running accumulators (consumed by
+ *            amax_history_update), so several calls may form one step.
+ *   bf16_out [rows x cols] BF16 copy of the activation output, or NULL
+ *   fp8_out  [rows x cols] FP8 codes, or NULL (an amax-only scan)
+ * The cast is binary32 b * s rounded to nearest-even, then FP8 rounding to
+ * nearest-even with saturation to +-max (infinity included); NaN stays NaN
+ * (0x7F | sign).  An element "saturates" when a cast without saturation would
+ * have overflowed (E4M3: |b*s| > 464; E5M2: |b*s| >= 61440).
+ * Errors: EINVAL for NULL h, rows or cols < 1, misaligned pointers, missing
+ * st in PER_TENSOR mode, cols % 128 != 0 or a NULL group_scale_inv in
+ * PER_GROUP128 mode with fp8_out given. */
+int quantize_fused(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                   fp8dp_format fmt, fp8dp_scale_mode mode, fp8dp_tensor_state* st,
+                   uint16_t* bf16_out, uint8_t* fp8_out, float* group_scale_inv,
+                   hipStream_t stream);
+
+/* Close a step of delayed scaling ("Paradigma ...": previous step's amax times
+ * a safety margin; "FP8 training ...", Trade-offs: a stored amax history;
+ * "FP8 Training & Inference", Delayed Scaling: detect overflow).  One
+ * single-wave kernel, no host round trip:
+ *   amax_t = max of the accumulator slots; history[hist_pos] = amax_t;
+ *   scale_inv_used = scale_inv (the inverse of the scale step t was cast with);
+ *   scale = max / (max(history) * margin) (1.0 when not a positive finite
+ *   number), scale_inv = 1/scale; sat_last = sum of the slots;
+ *   overflow = sat_last > 0; amax_last = amax_t; slots cleared; steps += 1.
+ * Errors: EINVAL for a NULL or misaligned st. */
+int amax_history_update(fp8dp_tensor_state* st, hipStream_t stream);
+
+/* Scaled FP8 x FP8 GEMM with FP32 accumulation and BF16 output ("FP8
+ * training ...", Step 3; "FP8 Training & Inference", Per-Tensor Scaling):
+ *   a [M x K] codes (format fa), b [N x K] codes (format fb), the weight in
+ *   the layout of a linear layer (K contiguous), y [M x N] BF16.
+ *   PER_TENSOR : y = bf16_rne(sum_k dec(a) dec(b) * a_scale_inv[0] * b_scale_inv[0])
+ *   PER_GROUP128: y = bf16_rne(sum_g (sum_{k in g} dec(a) dec(b))
+ *                              * a_scale_inv[m, g] * b_scale_inv[n/128, g]),
+ *                 a_scale_inv [M x K/128], b_scale_inv [N/128 x K/128]
+ *                 (each 128-wide partial sum is promoted into the FP32
+ *                 accumulator with its scales, as the FP32 promotion every
+ *                 128 elements of Step 3 describes).
+ * For delayed scaling, pass &st_a->scale_inv when the GEMM is enqueued before
+ * amax_history_update of that step, or &st_a->scale_inv_used after it.
+ * Errors: EINVAL for NULL pointers, M, N or K not positive multiples of 128,
+ * misaligned pointers, bad formats or mode. */
+int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
+                    int64_t M, int64_t N, int64_t K, fp8dp_scale_mode mode,
+                    const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
+                    hipStream_t stream);
+
+/* Weight cast with current scaling ("FP8 training ...", Step 4: the 8-bit
+ * copies are cast from the master weights at every step; Trade-offs: 128 x
+ * 128 weight blocks).  w [N x K] BF16 -> w8 [N x K] codes.
+ *   PER_TENSOR : scale_out is 2 floats: [0] = 1/s, [1] = s, s = max / amax(w)
+ *   PER_GROUP128: N % 128 == K % 128 == 0; block (i, j) = rows 128i.., cols
+ *                 128j.. is cast with s_ij = max / amax_ij and
+ *                 scale_out[i * (K/128) + j] = 1/s_ij.
+ * Errors: EINVAL for NULL pointers, bad sizes or alignment. */
+int quantize_weight(const uint16_t* w, int64_t N, int64_t K, fp8dp_format fmt,
+                    fp8dp_scale_mode mode, uint8_t* w8, float* scale_out, hipStream_t stream);
+
+/* (host) Message for the last failing call on this thread ("" if none). */
+const char* fp8dp_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Comparison and diagnostic entry points.
+ *
+ * The naive three-pass quantizer the Paradigma page contrasts with the fused
+ * kernel (write the whole intermediate, scan it for the max, read it again to
+ * convert): a caller runs fp8dp_bench_act_bf16, fp8dp_bench_amax,
+ * amax_history_update (margin 1, history 1: current scaling) and
+ * fp8dp_bench_cast.  n is the element count; all pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+/* Pass 1: out = bf16(act(h)); no amax. */
+int fp8dp_bench_act_bf16(const uint16_t* h, int64_t n, fp8dp_act act, uint16_t* out,
+                         hipStream_t stream);
+/* Pass 2: fold max |x| into st's accumulators (x read once). */
+int fp8dp_bench_amax(const uint16_t* x, int64_t n, fp8dp_tensor_state* st, hipStream_t stream);
+/* Pass 3: out = sat_rne(x * st->scale), saturation count folded into st. */
+int fp8dp_bench_cast(const uint16_t* x, int64_t n, fp8dp_format fmt, fp8dp_tensor_state* st,
+                     uint8_t* out, hipStream_t stream);
+/* Plain 16-byte-vector device copy (bandwidth ceiling and counter
+   calibration); bytes % 16 == 0. */
+int fp8dp_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+/* Device conversion routines applied to arbitrary binary32 inputs, for
+ * exhaustive comparison with a reference.  target 0: E4M3 codes (uint8 out),
+ * 1: E5M2 codes (uint8 out), 2: BF16 round-to-nearest-even (uint16 out).
+ * 3: saturation predicate for E4M3, 4: for E5M2 (uint8 0/1 out). */
+int fp8dp_convert_f32(const float* x, int64_t n, int32_t target, void* out, hipStream_t stream);
+
+/* Device scale rule on n amax values: scale[i] = max / (amax[i] * margin)
+   with the fallback to 1, scale_inv[i] = 1/scale[i]. */
+int fp8dp_scale_rule(const float* amax, int64_t n, float margin, fp8dp_format fmt, float* scale,
+                     float* scale_inv, hipStream_t stream);
+
+/* (host) Process-wide tuning and diagnostic switches; they change how the
+   work is scheduled or which bit-exact conversion routine runs, never the
+   results.  grid_limit: maximum thread blocks of the element-wise kernels
+   (0 = automatic).  codec: 0 = hardware conversion instructions, 1 = integer
+   bit-manipulation routines.  Return the previous value. */
+int32_t fp8dp_set_grid_limit(int32_t blocks);
+int32_t fp8dp_set_codec(int32_t codec);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8DP_H */

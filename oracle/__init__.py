@@ -36,6 +36,7 @@ PINNED = {
     "scale_from_amax": "amax 3.2 -> 140 and amax 0.8 -> 560 worked examples; Python float32 division",
     "quantize": "worked outlier experiment (16.24% zeroed, 12.78% / 3.41% RMSE); numpy brute force",
     "state/history": "closed-form delayed recurrence on the tiny workload",
+    "quantize_weight_blocks": "brute force composition per block (numpy + nearest-code search)",
     "gemm_f64": "exact rational arithmetic (fractions) on small cases; identity and constant cases",
 }
 
@@ -91,7 +92,8 @@ def lib() -> ctypes.CDLL:
     L.oracle_recip_f32.argtypes = [ctypes.c_float]
     L.oracle_quantize.restype = None
     L.oracle_quantize.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_int, ctypes.c_float, _u16p, _u8p, _f32p, _u32p, _u64p]
+                                  ctypes.c_int, ctypes.c_float, _u16p, _u8p, _f32p, _f32p, _u32p,
+                                  _u64p]
     L.oracle_state_size.restype = ctypes.c_int64
     L.oracle_state_init.restype = ctypes.c_int
     L.oracle_state_init.argtypes = [ctypes.POINTER(_State), ctypes.c_int, ctypes.c_int,
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
     L.oracle_bf16_rne_batch.argtypes = [_f32p, ctypes.c_int64, _u16p]
     L.oracle_scale_batch.argtypes = [_f32p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, _f32p,
                                      _f32p]
+    L.oracle_quantize_weight_blocks.restype = None
+    L.oracle_quantize_weight_blocks.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                _u8p, _f32p, _f32p]
     L.oracle_fp8_encode_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, _u8p]
     L.oracle_bf16_rne_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _u16p]
     if L.oracle_state_size() != ctypes.sizeof(_State):
@@ -189,6 +194,7 @@ class QuantResult:
     group_scale_inv: Optional[np.ndarray]  # float32 [rows, cols/128] (group mode) or None
     amax_bits: int                    # binary32 bits of max |b|
     sat: int                          # saturating element count
+    group_scale: Optional[np.ndarray] = None  # the multipliers s_g themselves (group mode)
 
     @property
     def amax(self) -> float:
@@ -207,11 +213,36 @@ def quantize(h: np.ndarray, act: int, fmt: int, mode: int, scale: float = 1.0,
     bf = np.empty_like(h) if want_bf16 else None
     q = np.empty(h.shape, dtype=np.uint8) if want_fp8 else None
     gsi = np.empty((rows, cols // GROUP), dtype=np.float32) if mode == PER_GROUP128 else None
+    gs = np.empty((rows, cols // GROUP), dtype=np.float32) if mode == PER_GROUP128 else None
     amax = ctypes.c_uint32(0)
     sat = ctypes.c_uint64(0)
     lib().oracle_quantize(_ptr(h, _u16p), rows, cols, act, fmt, mode, scale, _ptr(bf, _u16p),
-                          _ptr(q, _u8p), _ptr(gsi, _f32p), ctypes.byref(amax), ctypes.byref(sat))
-    return QuantResult(bf, q, gsi, int(amax.value), int(sat.value))
+                          _ptr(q, _u8p), _ptr(gsi, _f32p), _ptr(gs, _f32p), ctypes.byref(amax),
+                          ctypes.byref(sat))
+    return QuantResult(bf, q, gsi, int(amax.value), int(sat.value), gs)
+
+
+def quantize_weight_blocks(w: np.ndarray, fmt: int, with_scale: bool = False):
+    """128 x 128-block current-scaled cast of a BF16 [N, K] weight: (codes, scale_inv)
+    or, with_scale=True, (codes, scale_inv, scale)."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    N, K = w.shape
+    if N % GROUP or K % GROUP:
+        raise ValueError("weight blocks need N % 128 == 0 and K % 128 == 0")
+    q = np.empty_like(w, dtype=np.uint8)
+    si = np.empty((N // GROUP, K // GROUP), dtype=np.float32)
+    sc = np.empty((N // GROUP, K // GROUP), dtype=np.float32)
+    lib().oracle_quantize_weight_blocks(_ptr(w, _u16p), N, K, fmt, _ptr(q, _u8p), _ptr(si, _f32p),
+                                        _ptr(sc, _f32p))
+    return (q, si, sc) if with_scale else (q, si)
+
+
+def quantize_weight_tensor(w: np.ndarray, fmt: int):
+    """Per-tensor current-scaled cast of a BF16 weight: (codes, scale, scale_inv)."""
+    amax = quantize(w, ACT_IDENTITY, fmt, PER_TENSOR, 1.0, want_bf16=False, want_fp8=False).amax
+    s, si = scale_from_amax(amax, 1.0, fmt)
+    r = quantize(w, ACT_IDENTITY, fmt, PER_TENSOR, float(s[0]), want_bf16=False)
+    return r.fp8, float(s[0]), float(si[0])
 
 
 class State:

@@ -218,14 +218,15 @@ static uint16_t act_bf16(uint16_t h, int act) {
  *                              margin 1) and group_scale_inv[g] = 1 / s_g
  *                              ([FP8T] "Fine-grained quantization"; the
  *                              1-by-128 activation tile of "Trade-offs").
- *   bf16_out, fp8_out, group_scale_inv may be NULL.
+ *   bf16_out, fp8_out, group_scale_inv, group_scale (the multipliers s_g
+ *   themselves) may be NULL.
  * Outputs amax as the binary32 bit pattern of max |b| (the maximum of the
  * magnitude bit patterns, compared as unsigned integers), and the number of
  * saturating elements.
  */
 void oracle_quantize(const uint16_t* h, int64_t rows, int64_t cols, int act, int fmt, int mode,
                      float scale, uint16_t* bf16_out, uint8_t* fp8_out, float* group_scale_inv,
-                     uint32_t* amax_bits_out, uint64_t* sat_out) {
+                     float* group_scale, uint32_t* amax_bits_out, uint64_t* sat_out) {
   int64_t n = rows * cols;
   uint32_t amax = 0;
   uint64_t sat = 0;
@@ -251,6 +252,7 @@ void oracle_quantize(const uint16_t* h, int64_t rows, int64_t cols, int act, int
       if (gmax > amax) amax = gmax;
       float sg = oracle_scale_from_amax(u2f(gmax), 1.0f, fmt);
       if (group_scale_inv) group_scale_inv[g] = oracle_recip_f32(sg);
+      if (group_scale) group_scale[g] = sg;
       for (int j = 0; j < ORC_GROUP; ++j) {
         uint16_t b = act_bf16(hg[j], act);
         if (bf16_out) bf16_out[g * ORC_GROUP + j] = b;
@@ -262,6 +264,37 @@ void oracle_quantize(const uint16_t* h, int64_t rows, int64_t cols, int act, int
   }
   if (amax_bits_out) *amax_bits_out = amax;
   if (sat_out) *sat_out = sat;
+}
+
+/* Weight cast with current scaling over 128 x 128 blocks of a row-major
+   [N x K] BF16 weight ([FP8T] "Trade-offs": DeepSeek-V3 gives each 128 by
+   128 weight block its own scale).  Block (i, j) covers rows 128i..128i+127
+   and columns 128j..128j+127; its multiplier is max / amax_block (margin 1)
+   and scale_inv[i * (K/128) + j] = 1 / that multiplier (scale[] receives the
+   multiplier itself when given).  Per-tensor weights
+   use oracle_quantize with the multiplier from the tensor's amax. */
+void oracle_quantize_weight_blocks(const uint16_t* w, int64_t N, int64_t K, int fmt, uint8_t* w8,
+                                   float* scale_inv, float* scale) {
+  int64_t kb = K / ORC_GROUP;
+  for (int64_t bi = 0; bi < N / ORC_GROUP; ++bi) {
+    for (int64_t bj = 0; bj < kb; ++bj) {
+      uint32_t m = 0;
+      for (int64_t r = 0; r < ORC_GROUP; ++r)
+        for (int64_t c = 0; c < ORC_GROUP; ++c) {
+          uint32_t mag = ((uint32_t)(w[(bi * ORC_GROUP + r) * K + bj * ORC_GROUP + c] & 0x7FFF)) << 16;
+          if (mag > m) m = mag;
+        }
+      float s = oracle_scale_from_amax(u2f(m), 1.0f, fmt);
+      scale_inv[bi * kb + bj] = oracle_recip_f32(s);
+      if (scale) scale[bi * kb + bj] = s;
+      for (int64_t r = 0; r < ORC_GROUP; ++r)
+        for (int64_t c = 0; c < ORC_GROUP; ++c) {
+          int64_t idx = (bi * ORC_GROUP + r) * K + bj * ORC_GROUP + c;
+          float v = oracle_bf16_to_f32(w[idx]) * s;
+          w8[idx] = oracle_fp8_encode(v, fmt);
+        }
+    }
+  }
 }
 
 /* ------------------------------------------------------------------------ */

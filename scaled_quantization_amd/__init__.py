@@ -1,0 +1,237 @@
+"""scaled_quantization_amd -- scaled FP8 quantization for an MLP down-projection on MI355X.
+
+A thin ctypes binding over ``libfp8dp.so`` (C ABI declared in
+``include/fp8dp.h``).  Every step of the path runs in the library's HIP
+kernels; this module only marshals torch device tensors into pointers, sizes
+and the current HIP stream, and turns nonzero return codes into exceptions.
+It raises if the library has not been built; there is no CPU fallback.
+
+Entry points (same names as the C ABI):
+    fp8dp_state_init, quantize_fused, amax_history_update, fp8_gemm_scaled,
+    quantize_weight, and the comparison / diagnostic calls fp8dp_bench_*,
+    fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit, fp8dp_set_codec.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+from typing import Optional, Union
+
+import torch
+
+E4M3, E5M2 = 0, 1
+ACT_IDENTITY, ACT_RELU2 = 0, 1
+PER_TENSOR, PER_GROUP128 = 0, 1
+MAX_HIST = 16
+ACC_SLOTS = 64
+STATE_BYTES = 4288
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8dp.so")
+_lib: Optional[ctypes.CDLL] = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+_SIGS = {
+    "fp8dp_state_size": ([], _i64),
+    "fp8dp_state_init": ([_vp, _i32, _i32, _f32, _f32, _vp], ctypes.c_int),
+    "quantize_fused": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "amax_history_update": ([_vp, _vp], ctypes.c_int),
+    "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
+                        ctypes.c_int),
+    "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8dp_last_error": ([], ctypes.c_char_p),
+    "fp8dp_bench_act_bf16": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "fp8dp_bench_amax": ([_vp, _i64, _vp, _vp], ctypes.c_int),
+    "fp8dp_bench_cast": ([_vp, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8dp_bench_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
+    "fp8dp_convert_f32": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "fp8dp_scale_rule": ([_vp, _i64, _f32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8dp_set_grid_limit": ([_i32], _i32),
+    "fp8dp_set_codec": ([_i32], _i32),
+}
+
+
+class Fp8dpError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp8dp.so.  Raises if it has not been built (no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Fp8dpError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    if L.fp8dp_state_size() != STATE_BYTES:
+        raise Fp8dpError("fp8dp_tensor_state size differs from the binding's layout")
+    _lib = L
+    return L
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        msg = lib().fp8dp_last_error().decode(errors="replace")
+        raise Fp8dpError(f"{name} failed ({rc}): {msg}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+Ptr = Union[torch.Tensor, int, None]
+
+
+def _p(t: Ptr) -> Optional[int]:
+    """Device address of a tensor (must be on a GPU and contiguous) or a raw int."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise Fp8dpError("expected a device tensor")
+    if not t.is_contiguous():
+        raise Fp8dpError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+# --------------------------------------------------------------------------- state
+# Field offsets of fp8dp_tensor_state (include/fp8dp.h).
+_HDR = struct.Struct("<fffIQffiiIi16f")          # 112 bytes of header fields
+_SLOT = struct.Struct("<IIQ48x")                 # 64-byte accumulator slot
+_OFF = {"scale": 0, "scale_inv": 4, "scale_inv_used": 8, "acc": 192}
+
+
+class TensorState:
+    """Device-resident delayed-scaling state (a uint8 tensor of STATE_BYTES)."""
+
+    def __init__(self, fmt: int = E4M3, hist_len: int = 1, margin: float = 1.25,
+                 initial_amax: float = 1.0, device="cuda", stream=None):
+        self.buf = torch.empty(STATE_BYTES, dtype=torch.uint8, device=device)
+        self.fmt = fmt
+        fp8dp_state_init(self, fmt, hist_len, margin, initial_amax, stream)
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def field_ptr(self, name: str) -> int:
+        return self.ptr + _OFF[name]
+
+    def read(self) -> dict:
+        """Copy the state to the host and decode it (synchronizes the stream)."""
+        raw = self.buf.cpu().numpy().tobytes()
+        f = _HDR.unpack_from(raw, 0)
+        d = dict(scale=f[0], scale_inv=f[1], scale_inv_used=f[2], overflow=f[3], sat_last=f[4],
+                 amax_last=f[5], margin=f[6], hist_len=f[7], hist_pos=f[8], steps=f[9],
+                 fmt=f[10], history=list(f[11:11 + MAX_HIST]))
+        amax_acc, sat_acc = 0, 0
+        for i in range(ACC_SLOTS):
+            a, _, s = _SLOT.unpack_from(raw, _OFF["acc"] + 64 * i)
+            amax_acc = max(amax_acc, a)
+            sat_acc += s
+        d["amax_acc"] = amax_acc
+        d["sat_acc"] = sat_acc
+        return d
+
+    def raw(self) -> bytes:
+        return self.buf.cpu().numpy().tobytes()
+
+
+def _state_ptr(st) -> Optional[int]:
+    if st is None:
+        return None
+    if isinstance(st, TensorState):
+        return st.ptr
+    return _p(st)
+
+
+# --------------------------------------------------------------------------- entry points
+def fp8dp_state_init(st, fmt: int, hist_len: int, margin: float, initial_amax: float,
+                     stream=None) -> None:
+    _check(lib().fp8dp_state_init(_state_ptr(st), fmt, hist_len, margin, initial_amax,
+                                  _stream(stream)), "fp8dp_state_init")
+
+
+def quantize_fused(h: torch.Tensor, act: int, fmt: int, mode: int, st=None,
+                   bf16_out: Ptr = None, fp8_out: Ptr = None, group_scale_inv: Ptr = None,
+                   stream=None) -> None:
+    """h: BF16 (or 16-bit) device tensor [rows, cols] (1-D counts as one row)."""
+    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    _check(lib().quantize_fused(_p(h), rows, cols, act, fmt, mode, _state_ptr(st), _p(bf16_out),
+                                _p(fp8_out), _p(group_scale_inv), _stream(stream)),
+           "quantize_fused")
+
+
+def amax_history_update(st, stream=None) -> None:
+    _check(lib().amax_history_update(_state_ptr(st), _stream(stream)), "amax_history_update")
+
+
+def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: int,
+                    a_scale_inv: Ptr, b_scale_inv: Ptr, y: torch.Tensor, stream=None) -> None:
+    """a [M, K] codes, b [N, K] codes, y [M, N] BF16; scales are device pointers/tensors."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(y.shape) != (M, N):
+        raise Fp8dpError("fp8_gemm_scaled: shape mismatch")
+    _check(lib().fp8_gemm_scaled(_p(a), fa, _p(b), fb, M, N, K, mode, _p(a_scale_inv),
+                                 _p(b_scale_inv), _p(y), _stream(stream)), "fp8_gemm_scaled")
+
+
+def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,
+                    stream=None) -> None:
+    N, K = w.shape
+    _check(lib().quantize_weight(_p(w), N, K, fmt, mode, _p(w8), _p(scale_out), _stream(stream)),
+           "quantize_weight")
+
+
+def fp8dp_bench_act_bf16(h: torch.Tensor, act: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().fp8dp_bench_act_bf16(_p(h), h.numel(), act, _p(out), _stream(stream)),
+           "fp8dp_bench_act_bf16")
+
+
+def fp8dp_bench_amax(x: torch.Tensor, st, stream=None) -> None:
+    _check(lib().fp8dp_bench_amax(_p(x), x.numel(), _state_ptr(st), _stream(stream)),
+           "fp8dp_bench_amax")
+
+
+def fp8dp_bench_cast(x: torch.Tensor, fmt: int, st, out: torch.Tensor, stream=None) -> None:
+    _check(lib().fp8dp_bench_cast(_p(x), x.numel(), fmt, _state_ptr(st), _p(out),
+                                  _stream(stream)), "fp8dp_bench_cast")
+
+
+def fp8dp_bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().fp8dp_bench_copy(_p(src), _p(dst), nbytes, _stream(stream)), "fp8dp_bench_copy")
+
+
+def fp8dp_convert_f32(x: torch.Tensor, target: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().fp8dp_convert_f32(_p(x), x.numel(), target, _p(out), _stream(stream)),
+           "fp8dp_convert_f32")
+
+
+def fp8dp_scale_rule(amax: torch.Tensor, margin: float, fmt: int, scale: torch.Tensor,
+                     scale_inv: Ptr = None, stream=None) -> None:
+    _check(lib().fp8dp_scale_rule(_p(amax), amax.numel(), margin, fmt, _p(scale), _p(scale_inv),
+                                  _stream(stream)), "fp8dp_scale_rule")
+
+
+def fp8dp_set_grid_limit(blocks: int) -> int:
+    return lib().fp8dp_set_grid_limit(blocks)
+
+
+def fp8dp_set_codec(codec: int) -> int:
+    return lib().fp8dp_set_codec(codec)

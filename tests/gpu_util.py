@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: device transfer and chunked oracle calls.
+
+The oracle itself is single-threaded; for large inputs the tests call it on
+independent row ranges from several host threads (ctypes releases the GIL)
+and combine the per-range results exactly (max of amax, sum of counts,
+concatenation of element outputs).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import oracle as O
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+DEV = "cuda"
+
+
+def to_dev_bf16(h: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def to_dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def u8_np(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def _ranges(rows: int, parts: int):
+    step = max(1, (rows + parts - 1) // parts)
+    return [(r, min(rows, r + step)) for r in range(0, rows, step)]
+
+
+def oracle_quantize(h: np.ndarray, act: int, fmt: int, mode: int, scale: float = 1.0,
+                    want_bf16: bool = True, want_fp8: bool = True) -> O.QuantResult:
+    """O.quantize over row ranges in parallel; identical to one call over all rows."""
+    h = np.ascontiguousarray(h)
+    if h.ndim == 1:
+        h = h.reshape(1, -1)
+    rows = h.shape[0]
+    if rows < 4 * THREADS:
+        return O.quantize(h, act, fmt, mode, scale, want_bf16, want_fp8)
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda rg: O.quantize(h[rg[0]:rg[1]], act, fmt, mode, scale,
+                                                  want_bf16, want_fp8),
+                            _ranges(rows, 4 * THREADS)))
+    return O.QuantResult(
+        np.concatenate([p.bf16 for p in parts]) if want_bf16 else None,
+        np.concatenate([p.fp8 for p in parts]) if want_fp8 else None,
+        np.concatenate([p.group_scale_inv for p in parts]) if mode == O.PER_GROUP128 else None,
+        max(p.amax_bits for p in parts),
+        sum(p.sat for p in parts),
+        np.concatenate([p.group_scale for p in parts]) if mode == O.PER_GROUP128 else None,
+    )
+
+
+def oracle_gemm_rows(a, fa, b, fb, mode, sa, sb, rows):
+    rows = np.asarray(rows, dtype=np.int64)
+    chunks = np.array_split(rows, min(THREADS, len(rows)))
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda rr: O.gemm_f64(a, fa, b, fb, mode, sa, sb, rows=rr), chunks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def within_bound(y: np.ndarray, ref: np.ndarray, absref: np.ndarray) -> np.ndarray:
+    """The GEMM acceptance bound: |y - ref| <= 2^-8 |ref| + 1e-5 * sum_k |a_k b_k|."""
+    y = np.asarray(y, dtype=np.float64)
+    return np.abs(y - ref) <= (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
+
+
+def encode_range_parallel(lo: int, hi: int, fmt: int) -> np.ndarray:
+    n = hi - lo
+    step = (n + THREADS - 1) // THREADS
+    out = np.empty(n, dtype=np.uint8)
+
+    def job(i):
+        a = lo + i * step
+        b = min(hi, a + step)
+        if a < b:
+            out[a - lo:b - lo] = O.fp8_encode_range(a, b, fmt)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(job, range(THREADS)))
+    return out
+
+
+def device_arange_f32(lo: int, n: int) -> torch.Tensor:
+    """Binary32 values whose bit patterns are lo, lo+1, ..., lo+n-1 (no wrap inside)."""
+    base = lo - (1 << 32) if lo >= (1 << 31) else lo
+    t = torch.arange(n, dtype=torch.int32, device=DEV) + base
+    return t.view(torch.float32)

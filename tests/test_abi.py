@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every symbol include/fp8dp.h declares;
+argument checks reject bad calls before anything is enqueued (CPU only: no
+call here reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_quantization_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8dp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\*?([A-Za-z_]\w*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sq.LIB_PATH):
+        pytest.skip("libfp8dp.so not built")
+    return sq.lib()
+
+
+def test_header_declares_the_named_entry_points():
+    names = declared_functions()
+    for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
+              "quantize_weight", "fp8dp_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_state_layout_matches_binding(L):
+    assert L.fp8dp_state_size() == sq.STATE_BYTES == 192 + 64 * sq.ACC_SLOTS
+
+
+def test_argument_checks_reject_without_launching(L):
+    # every call below fails its host-side checks, so nothing reaches HIP
+    rc = L.quantize_fused(None, 4, 8, 0, 0, 0, None, None, None, None, None)
+    assert rc == -1 and b"non-NULL" in L.fp8dp_last_error()
+    rc = L.quantize_fused(16, 4, 8, 0, 0, 0, None, None, None, None, None)
+    assert rc == -1 and b"scaling state" in L.fp8dp_last_error()
+    rc = L.quantize_fused(16, 4, 100, 0, 0, 1, None, None, 32, None, None)
+    assert rc == -1 and b"128" in L.fp8dp_last_error()
+    rc = L.quantize_fused(18, 4, 8, 0, 0, 0, 16, None, None, None, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.quantize_fused(16, 4, 8, 7, 0, 0, 16, None, None, None, None)
+    assert rc == -1
+    rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 100, 0, 16, 16, 16, None)
+    assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled(16, 0, 16, 3, 128, 128, 128, 0, 16, 16, 16, None)
+    assert rc == -1 and b"format" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled(None, 0, 16, 0, 128, 128, 128, 0, 16, 16, 16, None)
+    assert rc == -1
+    rc = L.fp8dp_state_init(16, 0, 0, 1.25, 1.0, None)
+    assert rc == -1 and b"hist_len" in L.fp8dp_last_error()
+    rc = L.fp8dp_state_init(16, 0, 1, -1.0, 1.0, None)
+    assert rc == -1 and b"margin" in L.fp8dp_last_error()
+    rc = L.fp8dp_state_init(16, 2, 1, 1.0, 1.0, None)
+    assert rc == -1
+    rc = L.amax_history_update(None, None)
+    assert rc == -1
+    rc = L.quantize_weight(16, 100, 128, 0, 1, 16, 16, None)
+    assert rc == -1 and b"128" in L.fp8dp_last_error()
+    rc = L.fp8dp_convert_f32(16, 12, 0, 16, None)
+    assert rc == -1
+    rc = L.fp8dp_bench_copy(16, 16, 24, None)
+    assert rc == -1
+
+
+def test_switches_return_previous_value(L):
+    prev = L.fp8dp_set_grid_limit(7)
+    assert L.fp8dp_set_grid_limit(prev) == 7
+    prev = L.fp8dp_set_codec(1)
+    assert L.fp8dp_set_codec(prev) == 1
+
+
+def test_binding_refuses_host_tensors(L):
+    import torch
+    h = torch.zeros(8, 128, dtype=torch.bfloat16)
+    with pytest.raises(sq.Fp8dpError):
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, None, None, None, None,
+                          stream=0)

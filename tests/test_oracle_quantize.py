@@ -196,3 +196,33 @@ def test_state_rejects_bad_history_length():
         O.State(O.E4M3, hist_len=0)
     with pytest.raises(ValueError):
         O.State(O.E4M3, hist_len=O.MAX_HIST + 1)
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_weight_blocks_vs_brute_force(fmt):
+    w = workloads.normal(31, 256, 384, std=0.02)
+    w[0, 0] = R.torch_bf16(np.array([3.0], dtype=np.float32))[0]       # outlier in block (0, 0)
+    w[200, 300] = 0x7F80                                                # +inf in block (1, 2)
+    q, si = O.quantize_weight_blocks(w, fmt)
+    for bi in range(2):
+        for bj in range(3):
+            blk = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            amax = np.float32(np.abs(R.f32_from_bf16(blk)).max())
+            s = R.np_scale(amax, 1.0, fmt)
+            with np.errstate(all="ignore"):
+                assert si[bi, bj].view(np.uint32) == (np.float32(1) / s).view(np.uint32)
+                v = (R.f32_from_bf16(blk) * s).astype(np.float32)
+            exp = R.nearest_code(v, fmt).reshape(128, 128)
+            assert np.array_equal(q[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128], exp)
+    # only the block with the infinity falls back to scale 1
+    assert si[1, 2] == 1.0 and np.all(si[0] != 1.0)
+
+
+def test_weight_tensor_current_scaling():
+    w = workloads.normal(32, 128, 256, std=0.02)
+    q, s, si = O.quantize_weight_tensor(w, O.E4M3)
+    amax = np.float32(np.abs(R.f32_from_bf16(w)).max())
+    assert s == R.np_scale(amax, 1.0, O.E4M3) and si == np.float32(1) / np.float32(s)
+    assert ((q & 0x7F) == 0x7E).sum() >= 1
+    exp = R.nearest_code((R.f32_from_bf16(w) * np.float32(s)).astype(np.float32), O.E4M3)
+    assert np.array_equal(q, exp.reshape(q.shape))
