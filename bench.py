@@ -181,6 +181,7 @@ def main():
     if not args.no_naive:
         out["naive_three_pass"] = naive(sq, torch, H, A16[0], A8[0], n_in, args, dev, q_bytes,
                                         elems, q_mean)
+    out["gemm_exact_accumulation"] = gemm_exact(sq, torch, A8[0], w8, st_a, wsc, Y, args, flops)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -213,6 +214,25 @@ def naive(sq, torch, H, a16, a8, n_in, args, dev, q_bytes, elems, fused_ms):
     return {"ms": round(ms, 5), "GB/s_of_its_own_traffic": round(naive_bytes / (ms * 1e-3) / 1e9, 1),
             "bytes_per_pass": naive_bytes,
             "fused_speedup": round(ms / fused_ms, 3)}
+
+
+def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):
+    """The same GEMM with FP16-widened operands (FP32-accurate accumulation)."""
+    stream = torch.cuda.current_stream()
+    call = lambda: sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                                      st.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1), "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
 
 
 def copy_ceiling(sq, torch, dev):

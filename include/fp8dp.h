@@ -64,6 +64,19 @@ typedef enum { FP8DP_ACT_IDENTITY = 0, FP8DP_ACT_RELU2 = 1 } fp8dp_act;
    scaling, no margin); weights use 128 x 128 blocks. */
 typedef enum { FP8DP_PER_TENSOR = 0, FP8DP_PER_GROUP128 = 1 } fp8dp_scale_mode;
 
+/* How the GEMM sums products.
+   MFMA_FP8: the FP8 matrix instructions.  Measured on gfx950, they sum
+   products in groups of 8 consecutive k, each product truncated toward zero
+   to a multiple of 2^(E-13), where E is the largest exponent sum e_a + e_b in
+   its group.  Products within 7 binades of the group's largest are exact.
+   Group sums and the FP32 accumulator are combined at FP32 precision.  This
+   is the same kind of limited tensor-core accumulation that "FP8 training:
+   what it is and how it works", Step 3, reports for another GPU.
+   EXACT: FP8 operands are widened to FP16 in registers (every E4M3 and E5M2
+   value is exact in FP16) and summed by the FP16 matrix instructions with
+   FP32-accurate accumulation, at the FP16 instruction rate. */
+typedef enum { FP8DP_ACCUM_MFMA_FP8 = 0, FP8DP_ACCUM_EXACT = 1 } fp8dp_accum;
+
 #define FP8DP_MAX_HIST 16
 #define FP8DP_ACC_SLOTS 64
 
@@ -158,12 +171,13 @@ int amax_history_update(fp8dp_tensor_state* st, hipStream_t stream);
  *                 (each 128-wide partial sum is promoted into the FP32
  *                 accumulator with its scales, as the FP32 promotion every
  *                 128 elements of Step 3 describes).
+ * accum selects how products are summed (fp8dp_accum above).
  * For delayed scaling, pass &st_a->scale_inv when the GEMM is enqueued before
  * amax_history_update of that step, or &st_a->scale_inv_used after it.
  * Errors: EINVAL for NULL pointers, M, N or K not positive multiples of 128,
- * misaligned pointers, bad formats or mode. */
+ * misaligned pointers, bad formats, mode or accum. */
 int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
-                    int64_t M, int64_t N, int64_t K, fp8dp_scale_mode mode,
+                    int64_t M, int64_t N, int64_t K, fp8dp_scale_mode mode, fp8dp_accum accum,
                     const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
                     hipStream_t stream);
 

@@ -23,6 +23,7 @@ import torch
 E4M3, E5M2 = 0, 1
 ACT_IDENTITY, ACT_RELU2 = 0, 1
 PER_TENSOR, PER_GROUP128 = 0, 1
+ACCUM_MFMA_FP8, ACCUM_EXACT = 0, 1
 MAX_HIST = 16
 ACC_SLOTS = 64
 STATE_BYTES = 4288
@@ -41,8 +42,8 @@ _SIGS = {
     "fp8dp_state_init": ([_vp, _i32, _i32, _f32, _f32, _vp], ctypes.c_int),
     "quantize_fused": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "amax_history_update": ([_vp, _vp], ctypes.c_int),
-    "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
-                        ctypes.c_int),
+    "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                         _vp], ctypes.c_int),
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "fp8dp_last_error": ([], ctypes.c_char_p),
     "fp8dp_bench_act_bf16": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
@@ -181,13 +182,15 @@ def amax_history_update(st, stream=None) -> None:
 
 
 def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: int,
-                    a_scale_inv: Ptr, b_scale_inv: Ptr, y: torch.Tensor, stream=None) -> None:
-    """a [M, K] codes, b [N, K] codes, y [M, N] BF16; scales are device pointers/tensors."""
+                    a_scale_inv: Ptr, b_scale_inv: Ptr, y: torch.Tensor,
+                    accum: int = ACCUM_MFMA_FP8, stream=None) -> None:
+    """a [M, K] codes, b [N, K] codes, y [M, N] BF16; scales are device pointers/tensors;
+    accum: ACCUM_MFMA_FP8 (FP8 matrix instructions) or ACCUM_EXACT (FP16 widening)."""
     M, K = a.shape
     N = b.shape[0]
     if b.shape[1] != K or tuple(y.shape) != (M, N):
         raise Fp8dpError("fp8_gemm_scaled: shape mismatch")
-    _check(lib().fp8_gemm_scaled(_p(a), fa, _p(b), fb, M, N, K, mode, _p(a_scale_inv),
+    _check(lib().fp8_gemm_scaled(_p(a), fa, _p(b), fb, M, N, K, mode, accum, _p(a_scale_inv),
                                  _p(b_scale_inv), _p(y), _stream(stream)), "fp8_gemm_scaled")
 
 

@@ -29,6 +29,33 @@ namespace fp8dp {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+
+// Widens the 32 FP8 codes of an MFMA fragment into four groups of 8 FP16
+// values (exact: every E4M3 and E5M2 value is an FP16 value); group j holds
+// bytes 8j .. 8j+7 in order.
+template <int F>
+__device__ __forceinline__ void widen_fp8(const v8i_t& x, v8h_t out[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v2h_t p0, p1, p2, p3;
+    if constexpr (F == 0) {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j], 1.0f, false);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j], 1.0f, true);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j + 1], 1.0f, false);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j + 1], 1.0f, true);
+    } else {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j], 1.0f, false);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j], 1.0f, true);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j + 1], 1.0f, false);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j + 1], 1.0f, true);
+    }
+    out[j] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                     __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                     5, 6, 7);
+  }
+}
 
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGemmThreads = 256;
@@ -44,7 +71,7 @@ __device__ __forceinline__ int tile_of_block(int b, int ntiles) {
   return (b % 8) * per + b / 8;
 }
 
-template <int FA, int FB, int MODE>
+template <int FA, int FB, int MODE, bool EXACT>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restrict__ A,
                                                           const uint8_t* __restrict__ B, int M,
                                                           int N, int K,
@@ -148,17 +175,39 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
         fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+      if constexpr (EXACT) {
+        v8h_t ha[2][4], hb[2][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if constexpr (MODE == FP8DP_PER_GROUP128)
-            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], part[i][j],
-                                                                        FA, FB, 0, 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j],
-                                                                       FA, FB, 0, 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+          widen_fp8<FA>(fa[t], ha[t]);
+          widen_fp8<FB>(fb[t], hb[t]);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              if constexpr (MODE == FP8DP_PER_GROUP128)
+                part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i][q], hb[j][q], part[i][j],
+                                                                    0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i][q], hb[j][q], acc[i][j],
+                                                                   0, 0, 0);
+            }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (MODE == FP8DP_PER_GROUP128)
+              part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  fa[i], fb[j], part[i][j], FA, FB, 0, 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  fa[i], fb[j], acc[i][j], FA, FB, 0, 0, 0, 0);
+          }
+      }
     }
     if constexpr (MODE == FP8DP_PER_GROUP128) {
       // promote the 128-wide partial sums with their scales
@@ -196,17 +245,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
       }
 }
 
+template <int FA, int FB, int MODE, bool EXACT>
+static void launch_gemm_t(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                          const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((M / kBM) * (N / kBN));
+  hipLaunchKernelGGL((k_gemm<FA, FB, MODE, EXACT>), dim3(blocks), dim3(kGemmThreads), 0, stream,
+                     a, b, (int)M, (int)N, (int)K, sa, sb, y);
+}
+
 template <int FA, int FB>
 static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                       fp8dp_scale_mode mode, const float* sa, const float* sb, uint16_t* y,
-                       hipStream_t stream) {
-  const unsigned blocks = (unsigned)((M / kBM) * (N / kBN));
-  if (mode == FP8DP_PER_TENSOR)
-    hipLaunchKernelGGL((k_gemm<FA, FB, FP8DP_PER_TENSOR>), dim3(blocks), dim3(kGemmThreads), 0,
-                       stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
-  else
-    hipLaunchKernelGGL((k_gemm<FA, FB, FP8DP_PER_GROUP128>), dim3(blocks), dim3(kGemmThreads), 0,
-                       stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
+                       fp8dp_scale_mode mode, fp8dp_accum accum, const float* sa, const float* sb,
+                       uint16_t* y, hipStream_t stream) {
+  const bool exact = accum == FP8DP_ACCUM_EXACT;
+  if (mode == FP8DP_PER_TENSOR) {
+    if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);
+    else launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a, b, M, N, K, sa, sb, y, stream);
+  } else {
+    if (exact) launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, true>(a, b, M, N, K, sa, sb, y, stream);
+    else launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, false>(a, b, M, N, K, sa, sb, y, stream);
+  }
   return check_launch("fp8_gemm_scaled");
 }
 
@@ -216,8 +274,9 @@ using namespace fp8dp;
 
 extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
                                fp8dp_format fb, int64_t M, int64_t N, int64_t K,
-                               fp8dp_scale_mode mode, const float* a_scale_inv,
-                               const float* b_scale_inv, uint16_t* y, hipStream_t stream) {
+                               fp8dp_scale_mode mode, fp8dp_accum accum,
+                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
+                               hipStream_t stream) {
   if (a == nullptr || b == nullptr || y == nullptr || a_scale_inv == nullptr ||
       b_scale_inv == nullptr) {
     set_error("fp8_gemm_scaled: NULL pointer argument");
@@ -234,8 +293,9 @@ extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t*
     return FP8DP_EINVAL;
   }
   if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
-      (mode != FP8DP_PER_TENSOR && mode != FP8DP_PER_GROUP128)) {
-    set_error("fp8_gemm_scaled: unknown format or scale mode");
+      (mode != FP8DP_PER_TENSOR && mode != FP8DP_PER_GROUP128) ||
+      (accum != FP8DP_ACCUM_MFMA_FP8 && accum != FP8DP_ACCUM_EXACT)) {
+    set_error("fp8_gemm_scaled: unknown format, scale mode or accumulation mode");
     return FP8DP_EINVAL;
   }
   if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
@@ -245,10 +305,10 @@ extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t*
     return FP8DP_EINVAL;
   }
   if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_gemm<0, 0>(a, b, M, N, K, mode, a_scale_inv, b_scale_inv, y, stream);
+    return launch_gemm<0, 0>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
   if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_gemm<0, 1>(a, b, M, N, K, mode, a_scale_inv, b_scale_inv, y, stream);
+    return launch_gemm<0, 1>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_gemm<1, 0>(a, b, M, N, K, mode, a_scale_inv, b_scale_inv, y, stream);
-  return launch_gemm<1, 1>(a, b, M, N, K, mode, a_scale_inv, b_scale_inv, y, stream);
+    return launch_gemm<1, 0>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
+  return launch_gemm<1, 1>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
 }

@@ -56,12 +56,14 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.quantize_fused(16, 4, 8, 7, 0, 0, 16, None, None, None, None)
     assert rc == -1
-    rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 100, 0, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 100, 0, 0, 16, 16, 16, None)
     assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled(16, 0, 16, 3, 128, 128, 128, 0, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled(16, 0, 16, 3, 128, 128, 128, 0, 0, 16, 16, 16, None)
     assert rc == -1 and b"format" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled(None, 0, 16, 0, 128, 128, 128, 0, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled(None, 0, 16, 0, 128, 128, 128, 0, 0, 16, 16, 16, None)
     assert rc == -1
+    rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 128, 0, 5, 16, 16, 16, None)
+    assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
     rc = L.fp8dp_state_init(16, 0, 0, 1.25, 1.0, None)
     assert rc == -1 and b"hist_len" in L.fp8dp_last_error()
     rc = L.fp8dp_state_init(16, 0, 1, -1.0, 1.0, None)
