@@ -245,6 +245,155 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
       }
 }
 
+// ------------------------------------------------------------------ large tiles
+// Per-tensor FP8 path for large problems.  A workgroup of WM x WN waves owns a
+// BM x BN tile (256 x 192, 256 x 256 or 256 x 128 with 4 x 2 waves: 64 x 96,
+// 64 x 128 or 64 x 64 per wave, as 32 x 32 MFMA tiles), two waves per SIMD so
+// one wave's LDS reads overlap the other's MFMAs.  K advances 128 bytes per
+// stage through two LDS stages: the copies of stage t+1 are issued before the
+// MFMAs of stage t.  Global memory is copied straight into LDS with
+// global_load_lds_dwordx4 (no register staging): one instruction moves 64
+// lanes x 16 bytes = 8 rows of 128 bytes, lane i landing at byte 16 i; lane i
+// therefore fetches global chunk (i % 8) ^ (i / 8) of row i / 8, which is the
+// same XOR swizzle as the small-tile kernel (chunk c of row r at c ^ (r & 7)).
+// The epilogue pairs adjacent output columns between neighbour lanes (one DPP
+// swap) and stores BF16 pairs straight to Y.
+// Measured alternatives (GPT-2 shape): 64-byte stages with a 4-5 deep ring,
+// and fragment reads interleaved between MFMAs, were both slower on gfx950.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int FA, int FB, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ B,
+                                                              int M, int N, int K,
+                                                              const float* __restrict__ sa,
+                                                              const float* __restrict__ sb,
+                                                              uint16_t* __restrict__ Y) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;     // 32 x 32 MFMA tiles per wave
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiling");
+  constexpr int STAGE = (BM + BN) * kBK;                  // bytes of one LDS stage
+  constexpr int A_LOADS = BM / 8 / NW, B_LOADS = BN / 8 / NW;   // 1-KiB copies per wave
+  static_assert(A_LOADS * 8 * NW == BM && B_LOADS * 8 * NW == BN, "copy split");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int tiles_n = N / BN;
+  const int ntiles = (M / BM) * tiles_n;
+  const int tile = tile_of_block(blockIdx.x, ntiles);
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = (wave / WN) * (BM / WM);
+  const int wc = (wave % WN) * (BN / WN);
+  const int KT = K / kBK;
+
+  // this lane's source within each 8-row copy: row lane / 8, chunk (lane % 8) ^ (lane / 8)
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + lchunk * 16;
+  const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + lchunk * 16;
+  const size_t rstep = (size_t)(8 * NW) * K;              // the waves cover 8 NW rows per round
+
+  auto issue = [&](int kt) {
+    const size_t k0 = (size_t)kt * kBK;
+    uint8_t* base = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(gA + i * rstep + k0,
+                                       (lds_void_t*)(base + (i * 8 * NW + wave * 8) * kBK), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(
+          gB + i * rstep + k0, (lds_void_t*)(base + BM * kBK + (i * 8 * NW + wave * 8) * kBK),
+          16, 0, 0);
+  };
+
+  v16f_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int frow = lane & 31;
+  const int fhalf = (lane >> 5) * 2;
+  issue(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // This wave's copies of stage kt have landed; the barrier makes every
+    // wave's copies visible, and shows every wave is done with stage kt-1,
+    // whose slot the copies of stage kt+1 refill.  (A full __syncthreads()
+    // would be equivalent here: nothing else is in flight.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (kt + 1 < KT) issue(kt + 1);
+    const uint8_t* sA = lds + (kt & 1) * STAGE;
+    const uint8_t* sB = sA + BM * kBK;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c0 = ks * 4 + fhalf;
+      v8i_t fa[TM], fb[TN];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int r = wr + t * 32 + frow;
+        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
+        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 1));
+        fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wc + t * 32 + frow;
+        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
+        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 1));
+        fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], FA,
+                                                                     FB, 0, 0, 0, 0);
+    }
+  }
+
+  // epilogue: scale, round to BF16 and store pairs of adjacent columns.  In a
+  // 32 x 32 MFMA tile the lane holds column lane % 32 and register r holds row
+  // 8 (r / 4) + 4 (lane / 32) + r % 4; swapping one value with the neighbour
+  // lane (DPP quad_perm 1,0,3,2) gives the even lane columns (c, c+1) of row
+  // r and the odd lane the same columns of row r+1.
+  const float f = sa[0] * sb[0];
+  const bool odd = lane & 1;
+  const int colp = (lane & 31) & ~1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
+        const float give = odd ? v0 : v1;
+        const float got = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
+                                               false));
+        const uint32_t packed = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
+        const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
+        const int col = n0 + wc + j * 32 + colp;
+        *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = packed;
+      }
+}
+
+template <int FA, int FB, int BM, int BN>
+static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                      const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, BM, BN, 4, 2>), dim3((unsigned)((M / BM) * (N / BN))),
+                     dim3(64 * 8), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
+  return check_launch("fp8_gemm_scaled");
+}
+
 template <int FA, int FB, int MODE, bool EXACT>
 static void launch_gemm_t(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                           const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
@@ -258,6 +407,12 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
                        fp8dp_scale_mode mode, fp8dp_accum accum, const float* sa, const float* sb,
                        uint16_t* y, hipStream_t stream) {
   const bool exact = accum == FP8DP_ACCUM_EXACT;
+  if (mode == FP8DP_PER_TENSOR && !exact && M % 256 == 0) {
+    // the largest tile with at most one workgroup per compute unit at a time
+    if (N % 192 == 0) return launch_big<FA, FB, 256, 192>(a, b, M, N, K, sa, sb, y, stream);
+    if (N % 256 == 0) return launch_big<FA, FB, 256, 256>(a, b, M, N, K, sa, sb, y, stream);
+    return launch_big<FA, FB, 256, 128>(a, b, M, N, K, sa, sb, y, stream);
+  }
   if (mode == FP8DP_PER_TENSOR) {
     if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);
     else launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a, b, M, N, K, sa, sb, y, stream);

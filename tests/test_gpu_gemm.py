@@ -229,3 +229,21 @@ def test_non_multiple_of_eight_tile_grid(accum):
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.25, 0.125, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 4.0, 8.0)
     _check(y, ref, absref, "15 tiles")
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 384, 256), (2304, 768, 640), (4096, 4096, 256),
+                                   (256, 768, 128), (512, 640, 384)])
+def test_large_tile_paths(M, N, K):
+    # per-tensor FP8 shapes that take the 256 x 192, 256 x 256 and 256 x 128
+    # workgroup tiles (tile counts below, at and above the grid renumbering's
+    # multiple of 8)
+    rng = np.random.default_rng(M + N + K)
+    t = O.fp8_decode_table(O.E4M3)
+    near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
+    a8 = rng.choice(near, size=(M, K)).astype(np.uint8)
+    w8 = rng.choice(near, size=(N, K)).astype(np.uint8)
+    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, FP8)
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 64)), [M - 1]]))
+    ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
+    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows)
+    _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
