@@ -12,10 +12,12 @@ workload (H [16384 x 3072] BF16, 8 sequences x 2048 tokens):
 Each step reads its own pre-generated input H_t (16 drifting steps, cycled),
 so the working set does not stay in the last-level cache.
 
-Prints ONE JSON line.  `value` is the fused quantizer's throughput in GB/s of
-algorithmic traffic (5 bytes per element: read 2, write 2 + 1) divided by the
-kernel's mean duration measured with HIP events on the launch stream; the
-GEMM's TFLOP/s and the step time are reported beside it.
+Prints ONE JSON line.  `ms_per_step` is the time of --steps whole steps
+between two events.  `value` is the fused quantizer's throughput: algorithmic
+bytes (5 per element: read 2, write 2 + 1) over its average launch duration,
+timed with HIP events on the launch stream around --steps back-to-back
+launches that rotate through the step's inputs and outputs; the GEMM's
+TFLOP/s, timed the same way, is reported beside it.
 """
 from __future__ import annotations
 
@@ -43,6 +45,9 @@ def parse():
     p.add_argument("--workload", default="gpt2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-naive", action="store_true")
+    p.add_argument("--only", choices=("quantize", "gemm", "copy"), default=None,
+                   help="launch only this kernel of the step, --steps times, on the same "
+                        "inputs (for hardware counter runs), then exit")
     return p.parse_args()
 
 
@@ -82,7 +87,7 @@ def main():
     wsc = torch.empty(2, dtype=torch.float32, device=dev)
     sq.quantize_weight(wt, sq.E4M3, sq.PER_TENSOR, w8, wsc)
 
-    n_out = 2
+    n_out = 8                     # 8 x 144 MiB of outputs: more than the 256 MB last-level cache
     A16 = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(n_out)]
     A8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(n_out)]
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -93,52 +98,72 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(i, rec=None):
-        a16, a8 = A16[i % n_out], A8[i % n_out]
-        if rec:
-            rec[0].record(stream)
-        sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, a16, a8)
-        if rec:
-            rec[1].record(stream)
-        sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR, st_a.field_ptr("scale_inv"),
-                           wsc, Y)
-        if rec:
-            rec[2].record(stream)
+    if args.only is not None:
+        kernel_only(sq, torch, args, H, A16, A8, w8, wsc, Y, st_a, n_in, n_out, dev)
+        return
+
+    def quant(i):
+        sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a,
+                          A16[i % n_out], A8[i % n_out])
+
+    def gemm(i):
+        sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                           st_a.field_ptr("scale_inv"), wsc, Y)
+
+    def step(i):
+        quant(i)
+        gemm(i)
         sq.amax_history_update(st_a)
         sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, DY8)
-        if rec:
-            rec[3].record(stream)
         sq.amax_history_update(st_g)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # ---------------------------------------------------------------- timed region
-    recs = [[ev(), ev(), ev(), ev()] for _ in range(args.steps)]
+    # ---------------------------------------------------------------- timed region: whole steps
+    # Events only at the two ends: an event recorded between two kernels adds
+    # a dispatch gap of several microseconds to the stream.
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     t_start.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, recs[i])
+        step(args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    q_ms = [r[0].elapsed_time(r[1]) for r in recs]
-    g_ms = [r[1].elapsed_time(r[2]) for r in recs]
-    dy_ms = [r[2].elapsed_time(r[3]) for r in recs]   # includes the activation state update
-    q_mean = float(np.mean(q_ms))
-    g_mean = float(np.mean(g_ms))
-    dy_mean = float(np.mean(dy_ms))
+    st_read = st_a.read()
+
+    # ---------------------------------------------------------------- per-kernel launch duration
+    # Each kernel of the step launched --steps times back to back, with the
+    # step's own rotation of inputs and outputs, between two events on the
+    # launch stream: the mean is the average launch duration, the figure a
+    # kernel trace reports for the same launches.
+    def burst(fn):
+        fn(args.warmup)
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    q_mean = burst(quant)
+    g_mean = burst(gemm)
+    dy_mean = burst(lambda i: sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2,
+                                                sq.PER_TENSOR, st_g, None, DY8))
+    up_mean = burst(lambda i: sq.amax_history_update(st_a))
 
     elems = M * K
     q_bytes = elems * w.quant_bytes_per_elem()
     q_gbs = q_bytes / (q_mean * 1e-3) / 1e9
     flops = w.gemm_flops()
     g_tflops = flops / (g_mean * 1e-3) / 1e12
-    st_read = st_a.read()
+    dy_bytes = M * N * 3.0
 
     out = {
         "metric": METRIC,
@@ -168,7 +193,10 @@ def main():
             "fp8_gemm_scaled": {"ms": round(g_mean, 5), "TFLOP/s": round(g_tflops, 1),
                                 "frac_of_fp8_peak": round(g_tflops / FP8_PEAK_TFLOPS, 4),
                                 "flops_per_launch": flops},
-            "update+e5m2_cast+update": {"ms": round(dy_mean, 5)},
+            "quantize_fused_dy_e5m2": {"ms": round(dy_mean, 5),
+                                       "GB/s": round(dy_bytes / (dy_mean * 1e-3) / 1e9, 1),
+                                       "bytes_per_launch": dy_bytes},
+            "amax_history_update": {"ms": round(up_mean, 5)},
         },
         "gemm_roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
                           "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -186,6 +214,35 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def kernel_only(sq, torch, args, H, A16, A8, w8, wsc, Y, st_a, n_in, n_out, dev):
+    """One kernel of the step, repeated with the step's own rotation of inputs
+    and outputs; a profiler's per-dispatch counters then describe exactly the
+    launches the timed steps make."""
+    for i in range(args.warmup + args.steps):
+        if args.only == "quantize":
+            sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a,
+                              A16[i % n_out], A8[i % n_out])
+        elif args.only == "gemm":
+            sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                               st_a.field_ptr("scale_inv"), wsc, Y)
+        else:
+            copy_buffers(torch, dev)
+            sq.fp8dp_bench_copy(*_COPY[i % 2])
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "launches": args.warmup + args.steps}), flush=True)
+
+
+_COPY = []
+
+
+def copy_buffers(torch, dev, nbytes=1 << 28):
+    """Two (src, dst) pairs of 256 MiB for the copy reference kernel."""
+    if not _COPY:
+        a, b, c = (torch.zeros(nbytes, dtype=torch.uint8, device=dev) for _ in range(3))
+        _COPY.extend([(a, b), (b, c)])
+    return _COPY
 
 
 def naive(sq, torch, H, a16, a8, n_in, args, dev, q_bytes, elems, fused_ms):

@@ -29,6 +29,8 @@
 namespace fp8dp {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
+constexpr int kBlocksPerCU = 32;   // grid of the element-wise kernels
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -37,6 +39,16 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Streaming stores: the outputs are not read again by this kernel, so they
+// should not displace the inputs from the caches.
+__device__ __forceinline__ void store_nt(uint4* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(u32x4_t{a, b, c, d}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
 }
 
 // Largest 16-bit magnitude among the 8 BF16 values of a vector.
@@ -147,16 +159,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(
   const float s = CAST ? *scale_ptr : 1.0f;
   uint32_t amax16 = 0, sat = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
-    const uint4 x = load_nt(h + i);
+  auto one = [&](const uint4& x, int64_t i) {
     uint32_t b[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = act_pair<ACT, HW>(b[j]);
-    if constexpr (WBF16) bout[i] = make_uint4(b[0], b[1], b[2], b[3]);
+    if constexpr (WBF16) store_nt(bout + i, b[0], b[1], b[2], b[3]);
     const uint32_t mx = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
     if constexpr (AMAX) amax16 = mx > amax16 ? mx : amax16;
-    if constexpr (CAST) qout[i] = cast8<FMT, HW>(b, mx, s, sat);
+    if constexpr (CAST) store_nt(qout + i, cast8<FMT, HW>(b, mx, s, sat));
+  };
+  // kUnroll grid-strided vectors per iteration, all loads issued first: more
+  // bytes in flight per thread to cover HBM latency
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
+    uint4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = load_nt(h + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) one(x[u], i + u * stride);
   }
+  for (; i < n8; i += stride) one(load_nt(h + i), i);
   if (tail && blockIdx.x == 0 && threadIdx.x == 0) {
     const uint16_t* ht = reinterpret_cast<const uint16_t*>(h + n8);
     for (int t = 0; t < tail; ++t) {
@@ -197,21 +219,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
     float* __restrict__ gsi, int64_t n8, fp8dp_acc_slot* __restrict__ slots) {
   uint32_t amax16 = 0, sat = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
-    const uint4 x = load_nt(h + i);
+  auto one = [&](const uint4& x, int64_t i) {
     uint32_t b[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = act_pair<ACT, HW>(b[j]);
-    if constexpr (WBF16) bout[i] = make_uint4(b[0], b[1], b[2], b[3]);
+    if constexpr (WBF16) store_nt(bout + i, b[0], b[1], b[2], b[3]);
     const uint32_t mx = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
     const uint32_t gmax = row16_max(mx);
     amax16 = gmax > amax16 ? gmax : amax16;
     if constexpr (WFP8) {
       const float sg = scale_rule(__uint_as_float(gmax << 16), 1.0f, Fmt<FMT>::maxv);
       if ((threadIdx.x & 15) == 0) gsi[i >> 4] = recip_rn(sg);
-      qout[i] = cast8<FMT, HW>(b, mx, sg, sat);
+      store_nt(qout + i, cast8<FMT, HW>(b, mx, sg, sat));
     }
+  };
+  // two grid-strided vectors per iteration (the stride is a multiple of 16,
+  // so each DPP row still holds one whole group)
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < n8; i += 2 * stride) {
+    const uint4 x0 = load_nt(h + i), x1 = load_nt(h + i + stride);
+    one(x0, i);
+    one(x1, i + stride);
   }
+  if (i < n8) one(load_nt(h + i), i);
   if constexpr (ACC) block_fold(amax16, sat, slots);
 }
 
@@ -424,8 +454,16 @@ __global__ void k_scale_rule(const float* __restrict__ amax, int64_t n, float ma
 __global__ __launch_bounds__(kThreads) void k_copy(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride)
-    dst[i] = load_nt(src + i);
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < n16; i += 2 * stride) {
+    const uint4 a = load_nt(src + i), b = load_nt(src + i + stride);
+    store_nt(dst + i, a.x, a.y, a.z, a.w);
+    store_nt(dst + i + stride, b.x, b.y, b.z, b.w);
+  }
+  if (i < n16) {
+    const uint4 a = load_nt(src + i);
+    store_nt(dst + i, a.x, a.y, a.z, a.w);
+  }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -434,7 +472,7 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
                          const float* scale_ptr, fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, 8);
+  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, kBlocksPerCU);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
@@ -464,7 +502,7 @@ template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC>
 static int launch_group(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout, float* gsi,
                         fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  const unsigned grid = grid_for(n8, kThreads, 8);
+  const unsigned grid = grid_for(n8, kThreads, kBlocksPerCU);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
@@ -676,7 +714,7 @@ extern "C" int fp8dp_bench_copy(const void* src, void* dst, int64_t bytes, hipSt
     return FP8DP_EINVAL;
   }
   const int64_t n16 = bytes / 16;
-  hipLaunchKernelGGL(k_copy, dim3(grid_for(n16, kThreads, 8)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(k_copy, dim3(grid_for(n16, kThreads, kBlocksPerCU)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n16);
   return check_launch("fp8dp_bench_copy");
 }
