@@ -246,36 +246,65 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 }
 
 // ------------------------------------------------------------------ large tiles
-// Per-tensor FP8 path for large problems.  A workgroup of WM x WN waves owns a
-// BM x BN tile (256 x 192, 256 x 256 or 256 x 128 with 4 x 2 waves: 64 x 96,
-// 64 x 128 or 64 x 64 per wave, as 32 x 32 MFMA tiles), two waves per SIMD so
-// one wave's LDS reads overlap the other's MFMAs.  K advances 128 bytes per
-// stage through two LDS stages: the copies of stage t+1 are issued before the
-// MFMAs of stage t.  Global memory is copied straight into LDS with
+// Per-tensor FP8 path for large problems.  A 512-thread workgroup (8 waves,
+// two per SIMD) owns a 256 x BN tile of y (BN = 192 or 128); wave w owns rows
+// 64 (w / 2) .. +63 and columns (BN / 2)(w % 2) .. as 2 x TN tiles of the
+// 32 x 32 x 64 MFMA.  K advances 128 bytes per stage through a two-slot LDS
+// ring.  Global memory is copied straight into LDS with
 // global_load_lds_dwordx4 (no register staging): one instruction moves 64
 // lanes x 16 bytes = 8 rows of 128 bytes, lane i landing at byte 16 i; lane i
-// therefore fetches global chunk (i % 8) ^ (i / 8) of row i / 8, which is the
-// same XOR swizzle as the small-tile kernel (chunk c of row r at c ^ (r & 7)).
+// therefore fetches global chunk (i % 8) ^ (i / 8) of row i / 8, the same XOR
+// swizzle as the small-tile kernel (chunk c of row r at c ^ (r & 7)).
+//
+// The loop is software-pipelined by half stages, with the fragments double
+// buffered: the first half of stage t reads the fragments of its second
+// 64-wide k substep while the MFMAs of the first substep run; then every wave
+// waits for its own copies of stage t+1, and one barrier per stage publishes
+// them and shows that every wave has finished reading stage t; the second half
+// refills stage t's slot with the copies of stage t+2, reads the first
+// substep of stage t+1 and runs the MFMAs of stage t's second substep.  The
+// copies of a stage therefore have a whole stage of MFMAs to land, and no
+// LDS read waits in front of the MFMA pipe.
 // The epilogue pairs adjacent output columns between neighbour lanes (one DPP
 // swap) and stores BF16 pairs straight to Y.
-// Measured alternatives (GPT-2 shape): 64-byte stages with a 4-5 deep ring,
-// and fragment reads interleaved between MFMAs, were both slower on gfx950.
+// Measured alternatives (GPT-2 shape, same tile): no half-stage pipelining
+// (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
+// deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
+// the two waves of each SIMD with a barrier per phase were all slower.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int FA, int FB, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const uint8_t* __restrict__ A,
-                                                              const uint8_t* __restrict__ B,
-                                                              int M, int N, int K,
-                                                              const float* __restrict__ sa,
-                                                              const float* __restrict__ sb,
-                                                              uint16_t* __restrict__ Y) {
-  constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;     // 32 x 32 MFMA tiles per wave
-  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiling");
-  constexpr int STAGE = (BM + BN) * kBK;                  // bytes of one LDS stage
-  constexpr int A_LOADS = BM / 8 / NW, B_LOADS = BN / 8 / NW;   // 1-KiB copies per wave
-  static_assert(A_LOADS * 8 * NW == BM && B_LOADS * 8 * NW == BN, "copy split");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt(N) and no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that neither the compiler's scheduler nor its memory
+// model may move anything across, and that leaves the memory counters alone
+// (__syncthreads() would also drain every copy in flight).
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FA, int FB, int TN>
+__global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
+                                                     const uint8_t* __restrict__ B, int M, int N,
+                                                     int K, const float* __restrict__ sa,
+                                                     const float* __restrict__ sb,
+                                                     uint16_t* __restrict__ Y) {
+  constexpr int BM = 256, BN = 64 * TN, TM = 2;
+  constexpr int ASZ = BM * kBK, SLOT = (BM + BN) * kBK;   // bytes of A / of one ring slot
+  constexpr int LA = BM / 64, LB = BN / 64;                // copies per wave per stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
@@ -284,30 +313,47 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const uint8_t* __r
   const int n0 = (tile % tiles_n) * BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = (wave / WN) * (BM / WM);
-  const int wc = (wave % WN) * (BN / WN);
+  const int wr = (wave >> 1) * 64;
+  const int wc = (wave & 1) * (BN / 2);
   const int KT = K / kBK;
 
-  // this lane's source within each 8-row copy: row lane / 8, chunk (lane % 8) ^ (lane / 8)
+  // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow;
   const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + lchunk * 16;
   const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + lchunk * 16;
-  const size_t rstep = (size_t)(8 * NW) * K;              // the waves cover 8 NW rows per round
-
+  const size_t rstep = (size_t)64 * K;
   auto issue = [&](int kt) {
+    uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
     const size_t k0 = (size_t)kt * kBK;
-    uint8_t* base = lds + (kt & 1) * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(gA + i * rstep + k0,
-                                       (lds_void_t*)(base + (i * 8 * NW + wave * 8) * kBK), 16,
-                                       0, 0);
+    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(
-          gB + i * rstep + k0, (lds_void_t*)(base + BM * kBK + (i * 8 * NW + wave * 8) * kBK),
-          16, 0, 0);
+    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
+  };
+
+  // this lane's fragment rows: A rows wr + 32 t + lane % 32, B rows wc + 32 t + lane % 32;
+  // k bytes 32 (lane / 32) .. +31 of the 64-byte substep h
+  const int frow = lane & 31;
+  const int fhalf = (lane >> 5) * 2;
+  auto load_frags = [&](int kt, int h, v8i_t* fa, v8i_t* fb) {
+    const uint8_t* sA = lds + (kt & 1) * SLOT;
+    const uint8_t* sB = sA + ASZ;
+    const int c0 = h * 4 + fhalf;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int r = wr + t * 32 + frow;
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 1));
+      fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int r = wc + t * 32 + frow;
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 1));
+      fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
 
   v16f_t acc[TM][TN];
@@ -317,47 +363,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const uint8_t* __r
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], FA,
+                                                                   FB, 0, 0, 0, 0);
+  };
 
-  const int frow = lane & 31;
-  const int fhalf = (lane >> 5) * 2;
+  // prologue: stages 0 and 1 in flight, stage 0 landed and published
   issue(0);
+  if (KT > 1) {
+    issue(1);
+    wait_vmcnt<LA + LB>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  stage_barrier();
+  v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  load_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < KT; ++kt) {
-    // This wave's copies of stage kt have landed; the barrier makes every
-    // wave's copies visible, and shows every wave is done with stage kt-1,
-    // whose slot the copies of stage kt+1 refill.  (A full __syncthreads()
-    // would be equivalent here: nothing else is in flight.)
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    if (kt + 1 < KT) issue(kt + 1);
-    const uint8_t* sA = lds + (kt & 1) * STAGE;
-    const uint8_t* sB = sA + BM * kBK;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c0 = ks * 4 + fhalf;
-      v8i_t fa[TM], fb[TN];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int r = wr + t * 32 + frow;
-        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
-        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 1));
-        fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int r = wc + t * 32 + frow;
-        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
-        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 1));
-        fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], FA,
-                                                                     FB, 0, 0, 0, 0);
-    }
+    // first half: read substep 1 of stage kt, multiply substep 0
+    load_frags(kt, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
+    wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
+    stage_barrier();
+    // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
+    if (kt + 2 < KT) issue(kt + 2);
+    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0);
+    mfmas(fa1, fb1);
   }
 
   // epilogue: scale, round to BF16 and store pairs of adjacent columns.  In a
@@ -386,11 +423,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const uint8_t* __r
       }
 }
 
-template <int FA, int FB, int BM, int BN>
+template <int FA, int FB, int TN>
 static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                       const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, BM, BN, 4, 2>), dim3((unsigned)((M / BM) * (N / BN))),
-                     dim3(64 * 8), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
+                     dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
   return check_launch("fp8_gemm_scaled");
 }
 
@@ -408,10 +445,9 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
                        uint16_t* y, hipStream_t stream) {
   const bool exact = accum == FP8DP_ACCUM_EXACT;
   if (mode == FP8DP_PER_TENSOR && !exact && M % 256 == 0) {
-    // the largest tile with at most one workgroup per compute unit at a time
-    if (N % 192 == 0) return launch_big<FA, FB, 256, 192>(a, b, M, N, K, sa, sb, y, stream);
-    if (N % 256 == 0) return launch_big<FA, FB, 256, 256>(a, b, M, N, K, sa, sb, y, stream);
-    return launch_big<FA, FB, 256, 128>(a, b, M, N, K, sa, sb, y, stream);
+    // the larger tile when it divides N (one workgroup per compute unit at a time)
+    if (N % 192 == 0) return launch_big<FA, FB, 3>(a, b, M, N, K, sa, sb, y, stream);
+    return launch_big<FA, FB, 2>(a, b, M, N, K, sa, sb, y, stream);
   }
   if (mode == FP8DP_PER_TENSOR) {
     if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);

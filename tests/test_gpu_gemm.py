@@ -232,11 +232,13 @@ def test_non_multiple_of_eight_tile_grid(accum):
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 256), (2304, 768, 640), (4096, 4096, 256),
-                                   (256, 768, 128), (512, 640, 384)])
+                                   (256, 768, 128), (512, 640, 384), (768, 384, 256),
+                                   (512, 384, 1280), (1024, 512, 1152)])
 def test_large_tile_paths(M, N, K):
-    # per-tensor FP8 shapes that take the 256 x 192, 256 x 256 and 256 x 128
-    # workgroup tiles (tile counts below, at and above the grid renumbering's
-    # multiple of 8)
+    # per-tensor FP8 shapes that take the 256 x 192 and 256 x 128 workgroup
+    # tiles: tile counts below, at and above the grid renumbering's multiple
+    # of 8, and 1, 2, 3 and 9-10 stages of 128 k (the pipeline's prologue,
+    # steady state and tail)
     rng = np.random.default_rng(M + N + K)
     t = O.fp8_decode_table(O.E4M3)
     near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
