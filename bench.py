@@ -186,7 +186,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("quantize_fused_gpt2")},
+                     "traffic": measured_traffic("quantize_fused_gpt2", "quantize.hip")},
         "kernels": {
             "quantize_fused": {"ms": round(q_mean, 5), "GB/s": round(q_gbs, 1),
                                "bytes_per_launch": q_bytes},
@@ -200,7 +200,8 @@ def main():
         },
         "gemm_roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
                           "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(g_tflops / FP8_PEAK_TFLOPS, 4)},
+                          "frac": round(g_tflops / FP8_PEAK_TFLOPS, 4),
+                          "traffic": measured_traffic("fp8_gemm_scaled_gpt2", "gemm.hip")},
         "last_step": {"scale": st_read["scale"], "amax": st_read["amax_last"],
                       "saturated": st_read["sat_last"]},
         "wall_s_timed": round(wall, 3),
@@ -311,7 +312,7 @@ def copy_ceiling(sq, torch, dev):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def measured_traffic(name):
+def measured_traffic(name, source):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
@@ -319,7 +320,7 @@ def measured_traffic(name):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "scaled_quantization_amd", "csrc", "quantize.hip"), "rb").read()
+        src = open(os.path.join(ROOT, "scaled_quantization_amd", "csrc", source), "rb").read()
         if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
             return None
         return rec.get("bytes_per_launch")

@@ -15,10 +15,10 @@
 // its four waves owns 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x64_f8f6f4
 // (the format of each operand is selected by the instruction's cbsz / blgp
 // fields: 0 = E4M3, 1 = E5M2).  K advances 128 bytes at a time; A and B tiles
-// (128 rows x 128 bytes each) are staged in LDS, double-buffered, with the
-// 16-byte chunk c of row r stored at chunk c ^ (r & 7) so the 16-byte LDS
-// reads of eight consecutive rows hit distinct banks.  Global loads for the
-// next K step are issued before the MFMAs of the current one.
+// (128 rows x 128 bytes each) are staged in LDS, double-buffered, with an XOR
+// swizzle of the 16-byte chunks (swz() below) so the 16-byte LDS reads of 16
+// consecutive rows hit distinct banks.  Global loads for the next K step are
+// issued before the MFMAs of the current one.
 #include <hip/hip_runtime.h>
 
 #include "codec.hpp"
@@ -60,7 +60,15 @@ __device__ __forceinline__ void widen_fp8(const v8i_t& x, v8h_t out[4]) {
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGemmThreads = 256;
 
-__device__ __forceinline__ int swz(int r, int chunk) { return r * kBK + ((chunk ^ (r & 7)) << 4); }
+// LDS layout of a tile with 128-byte rows: 16-byte chunk c of row r sits at
+// chunk c ^ ((r / 2) % 8).  gfx950's LDS serves 16 lanes of a 16-byte read
+// per cycle from 64 banks (256 bytes, two rows); a fragment read has those 16
+// lanes on 16 consecutive rows at one logical chunk, and (r % 2, (r / 2) % 8)
+// takes all 16 values over them, so the 16 chunks hit 16 distinct bank groups.
+// (The 32-bank pattern c ^ (r % 8) gives rows r and r + 8 the same banks.)
+__device__ __forceinline__ int swz(int r, int chunk) {
+  return r * kBK + ((chunk ^ ((r >> 1) & 7)) << 4);
+}
 
 // blockIdx -> output tile.  Workgroups are handed to the 8 XCDs round-robin
 // (block b runs on XCD b % 8); renumbering so that each XCD receives a
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // ring.  Global memory is copied straight into LDS with
 // global_load_lds_dwordx4 (no register staging): one instruction moves 64
 // lanes x 16 bytes = 8 rows of 128 bytes, lane i landing at byte 16 i; lane i
-// therefore fetches global chunk (i % 8) ^ (i / 8) of row i / 8, the same XOR
-// swizzle as the small-tile kernel (chunk c of row r at c ^ (r & 7)).
+// therefore fetches the global chunk of row i / 8 that swz() places at chunk
+// i % 8 (the same layout as the small-tile kernel).
 //
 // The loop is software-pipelined by half stages, with the fragments double
 // buffered: the first half of stage t reads the fragments of its second
@@ -317,9 +325,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   const int wc = (wave & 1) * (BN / 2);
   const int KT = K / kBK;
 
-  // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7
+  // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7; lane l
+  // lands at chunk l % 8 of row l / 8 there, so it fetches the logical chunk
+  // that swz() places at that position: (l % 8) ^ ((row / 2) % 8), where
+  // (row / 2) % 8 = (4 wave + (l / 8) / 2) % 8 for every i
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7);
   const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + lchunk * 16;
   const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + lchunk * 16;
   const size_t rstep = (size_t)64 * K;
