@@ -255,9 +255,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 
 // ------------------------------------------------------------------ large tiles
 // Per-tensor FP8 path for large problems.  A 512-thread workgroup (8 waves,
-// two per SIMD) owns a 256 x BN tile of y (BN = 192 or 128); wave w owns rows
-// 64 (w / 2) .. +63 and columns (BN / 2)(w % 2) .. as 2 x TN tiles of the
-// 32 x 32 x 64 MFMA.  K advances 128 bytes per stage through a two-slot LDS
+// two per SIMD) owns a 256 x BN tile of y (BN = 64 TN = 128, 192 or 256); wave
+// w owns rows 64 (w / 2) .. +63 and columns (BN / 2)(w % 2) .. as 2 x TN tiles
+// of the 32 x 32 x 64 MFMA (TN = 4 uses 252 of the 256 registers a wave may
+// have at two waves per SIMD).  K advances 128 bytes per stage through a two-slot LDS
 // ring.  Global memory is copied straight into LDS with
 // global_load_lds_dwordx4 (no register staging): one instruction moves 64
 // lanes x 16 bytes = 8 rows of 128 bytes, lane i landing at byte 16 i; lane i
@@ -275,6 +276,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // LDS read waits in front of the MFMA pipe.
 // The epilogue pairs adjacent output columns between neighbour lanes (one DPP
 // swap) and stores BF16 pairs straight to Y.
+// Per-128-group scales stay on the small-tile kernel: promoting a partial sum
+// per stage in this kernel (256 x 128 tiles) was slower than it, because the
+// promotion's vector work lands on both waves of a SIMD at the same time.
 // Measured alternatives (GPT-2 shape, same tile): no half-stage pipelining
 // (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
 // deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
@@ -284,6 +288,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
 }
+
 
 // s_waitcnt with vmcnt(N) and no wait on the other counters.
 template <int N>
@@ -456,8 +461,9 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
                        uint16_t* y, hipStream_t stream) {
   const bool exact = accum == FP8DP_ACCUM_EXACT;
   if (mode == FP8DP_PER_TENSOR && !exact && M % 256 == 0) {
-    // the larger tile when it divides N (one workgroup per compute unit at a time)
+    // the widest tile that divides N (one workgroup per compute unit at a time)
     if (N % 192 == 0) return launch_big<FA, FB, 3>(a, b, M, N, K, sa, sb, y, stream);
+    if (N % 256 == 0) return launch_big<FA, FB, 4>(a, b, M, N, K, sa, sb, y, stream);
     return launch_big<FA, FB, 2>(a, b, M, N, K, sa, sb, y, stream);
   }
   if (mode == FP8DP_PER_TENSOR) {

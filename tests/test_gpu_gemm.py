@@ -233,12 +233,13 @@ def test_non_multiple_of_eight_tile_grid(accum):
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 256), (2304, 768, 640), (4096, 4096, 256),
                                    (256, 768, 128), (512, 640, 384), (768, 384, 256),
-                                   (512, 384, 1280), (1024, 512, 1152)])
+                                   (512, 384, 1280), (1024, 512, 1152), (512, 1024, 384),
+                                   (2048, 2048, 640), (256, 256, 128)])
 def test_large_tile_paths(M, N, K):
-    # per-tensor FP8 shapes that take the 256 x 192 and 256 x 128 workgroup
-    # tiles: tile counts below, at and above the grid renumbering's multiple
-    # of 8, and 1, 2, 3 and 9-10 stages of 128 k (the pipeline's prologue,
-    # steady state and tail)
+    # per-tensor FP8 shapes that take the 256 x 192, 256 x 256 and 256 x 128
+    # workgroup tiles: tile counts below, at and above the grid renumbering's
+    # multiple of 8, and 1, 2, 3 and 9-10 stages of 128 k (the pipeline's
+    # prologue, steady state and tail)
     rng = np.random.default_rng(M + N + K)
     t = O.fp8_decode_table(O.E4M3)
     near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
@@ -249,3 +250,27 @@ def test_large_tile_paths(M, N, K):
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
     allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows)
     _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [(256, 128, 128, 0, 0), (512, 384, 256, 0, 0),
+                                         (768, 640, 1280, 0, 1), (2304, 1024, 384, 1, 0),
+                                         (1024, 256, 640, 1, 1)])
+def test_group_scaled_shapes(M, N, K, fa, fb):
+    # per-group FP8: per-stage partial sums promoted by sa[m, g] sb[n / 128, g]
+    # over 1, 2, 3, 5 and 10 stages, tile counts on and off the renumbering's
+    # multiple of 8, every format pair, scales that are not powers of two
+    rng = np.random.default_rng(M * 7 + N + K)
+    ta = O.fp8_decode_table(fa)
+    tb = O.fp8_decode_table(fb)
+    near_a = np.flatnonzero(np.isfinite(ta) & (np.abs(ta) >= 0.25) & (np.abs(ta) <= 16))
+    near_b = np.flatnonzero(np.isfinite(tb) & (np.abs(tb) >= 0.25) & (np.abs(tb) <= 16))
+    a8 = rng.choice(near_a, size=(M, K)).astype(np.uint8)
+    w8 = rng.choice(near_b, size=(N, K)).astype(np.uint8)
+    sa = rng.uniform(0.05, 40.0, (M, K // 128)).astype(np.float32)
+    sb = rng.uniform(0.05, 40.0, (N // 128, K // 128)).astype(np.float32)
+    y = _gemm(a8, fa, w8, fb, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 48)), [M - 1]]))
+    ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
+    allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows)
+    _check(y[rows], ref, absref, f"group {M}x{N}x{K} fa={fa} fb={fb}", allow,
+           max_plain_violation_frac=1e-3)
