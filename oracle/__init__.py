@@ -106,6 +106,9 @@ def lib() -> ctypes.CDLL:
     L.oracle_gemm_f64.argtypes = [_u8p, ctypes.c_int, _u8p, ctypes.c_int, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _f32p, _f32p,
                                   _i64p, ctypes.c_int64, _f64p, _f64p]
+    L.oracle_gemm_bf16_f64.restype = None
+    L.oracle_gemm_bf16_f64.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, _i64p, ctypes.c_int64, _f64p, _f64p]
     L.oracle_fp8_encode_batch.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, _u8p]
     L.oracle_fp8_saturates_batch.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, _u8p]
     L.oracle_bf16_rne_batch.argtypes = [_f32p, ctypes.c_int64, _u16p]
@@ -275,6 +278,23 @@ class State:
 
 
 # --------------------------------------------------------------------------- GEMM
+def gemm_bf16_f64(x: np.ndarray, w: np.ndarray, rows: Optional[Sequence[int]] = None):
+    """Float64 reference of Y = X W^T over BF16 inputs (bit patterns, uint16):
+    x [M, K], w [N, K].  Returns (ref, absref), each float64 [len(rows) or M, N]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    cnt = M if r is None else r.size
+    ref = np.empty((cnt, N), dtype=np.float64)
+    absref = np.empty((cnt, N), dtype=np.float64)
+    lib().oracle_gemm_bf16_f64(_ptr(x, _u16p), _ptr(w, _u16p), M, N, K, _ptr(r, _i64p),
+                               0 if r is None else r.size, _ptr(ref, _f64p), _ptr(absref, _f64p))
+    return ref, absref
+
+
 def gemm_f64(a: np.ndarray, fa: int, b: np.ndarray, fb: int, mode: int, sa, sb,
              rows: Optional[Sequence[int]] = None):
     """Float64 reference of the scaled FP8 GEMM.

@@ -421,6 +421,34 @@ void oracle_gemm_f64(const uint8_t* a, int fa, const uint8_t* b, int fb, int64_t
   }
 }
 
+/* BF16 x BF16 GEMM reference for an up-projection whose epilogue carries the
+   quantizer ("Paradigma Details FP8 and Optimizer Tricks Behind NanoGPT
+   Records", FP8 paragraph: the fused kernel works on the preceding
+   computation's results while they are still in registers, so the
+   pre-activation H never goes through memory).  ref[r, n] = sum over k of
+   x[m, k] * w[n, k] with m = rows[r] (or r), summed in float64 in k order;
+   every product of two BF16 values is exact in float64 (8 + 8 significant
+   bits).  absref[r, n] = the same sum of |x w|. */
+void oracle_gemm_bf16_f64(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                          const int64_t* rows, int64_t nrows, double* ref, double* absref) {
+  int64_t count = rows ? nrows : M;
+  for (int64_t r = 0; r < count; ++r) {
+    int64_t m = rows ? rows[r] : r;
+    const uint16_t* xr = x + m * K;
+    for (int64_t n = 0; n < N; ++n) {
+      const uint16_t* wr = w + n * K;
+      double s = 0.0, sabs = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = (double)oracle_bf16_to_f32(xr[k]) * (double)oracle_bf16_to_f32(wr[k]);
+        s += p;
+        sabs += fabs(p);
+      }
+      ref[r * N + n] = s;
+      if (absref) absref[r * N + n] = sabs;
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Batch helpers (the per-element functions above applied to arrays).        */
 /* ------------------------------------------------------------------------ */

@@ -123,3 +123,58 @@ def test_gemm_matches_float64_matmul_of_dequantized_inputs():
     t = R.torch_decode_table(O.E4M3)
     mm = (torch.from_numpy(t[a]) @ torch.from_numpy(t[b]).T).numpy() / (11.0 * 0.25)
     assert np.allclose(ref, mm, rtol=0, atol=1e-12 * absref.max())
+
+
+# ---------------------------------------------------------------------------
+# BF16 x BF16 reference of the up-projection whose epilogue carries the
+# quantizer ("Paradigma Details FP8 and Optimizer Tricks Behind NanoGPT
+# Records", FP8 paragraph).
+
+def _bf16_bits(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_values(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_gemm_bf16_vs_exact_rationals():
+    rng = np.random.default_rng(21)
+    x = _bf16_bits(rng, (5, 96), 3.0)
+    w = _bf16_bits(rng, (7, 96), 0.1)
+    ref, absref = O.gemm_bf16_f64(x, w)
+    xv, wv = _bf16_values(x), _bf16_values(w)
+    for m in range(5):
+        for n in range(7):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xv[m], wv[n]))
+            exact_abs = sum(abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(xv[m], wv[n]))
+            assert abs(Fraction(ref[m, n]) - exact) <= Fraction(2.0 ** -50) * exact_abs
+            assert abs(Fraction(absref[m, n]) - exact_abs) <= Fraction(2.0 ** -50) * exact_abs
+
+
+def test_gemm_bf16_identity_weight_and_transpose_symmetry():
+    rng = np.random.default_rng(22)
+    x = _bf16_bits(rng, (16, 64), 5.0)
+    one = np.uint16(0x3F80)
+    eye = np.zeros((64, 64), np.uint16)
+    np.fill_diagonal(eye, one)
+    ref, _ = O.gemm_bf16_f64(x, eye)
+    assert np.array_equal(ref, _bf16_values(x))
+    # (X W^T)^T = W X^T: swapping the operands transposes the result
+    w = _bf16_bits(rng, (24, 64))
+    a, _ = O.gemm_bf16_f64(x, w)
+    b, _ = O.gemm_bf16_f64(w, x)
+    assert np.allclose(a, b.T, rtol=0, atol=1e-12 * np.abs(a).max())
+
+
+def test_gemm_bf16_matches_float64_matmul_and_row_sampling():
+    rng = np.random.default_rng(23)
+    x = _bf16_bits(rng, (64, 768))
+    w = _bf16_bits(rng, (96, 768), 768 ** -0.5)
+    ref, absref = O.gemm_bf16_f64(x, w)
+    mm = torch.from_numpy(_bf16_values(x)) @ torch.from_numpy(_bf16_values(w)).T
+    assert np.all(np.abs(ref - mm.numpy()) <= 1e-13 * absref)
+    rows = [0, 17, 63]
+    r2, a2 = O.gemm_bf16_f64(x, w, rows=rows)
+    assert np.array_equal(r2, ref[rows]) and np.array_equal(a2, absref[rows])

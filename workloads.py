@@ -26,8 +26,13 @@ layout of a linear layer's weight):
   large     H [65536 x 16384] ~ N(0,1); W [4096 x 16384] ~ 0.02 N(0,1);
             dY [65536 x 4096] with log-normal magnitudes (sigma 3), random signs.
 
+Up-projection inputs (for the quantizer fused into the up-projection's
+epilogue): X [M x N] ~ N(0,1) (N is the model width) from seed + 4000, and
+W1 [K x N] ~ N(0, 1/N) from seed + 5000, so that X W1^T has the scale of H.
+
 Seeds: H from the workload seed, W from seed + 1000, dY from seed + 2000,
-drift / positions / signs from seed + 3000.
+drift / positions / signs from seed + 3000, X from seed + 4000, W1 from
+seed + 5000.
 """
 from __future__ import annotations
 
@@ -140,6 +145,15 @@ class Workload:
 
     def weight(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
         return normal(self.seed + 1000, self.N, self.K, std=0.02, row0=row0, nrows=nrows)
+
+    def up_x(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
+        """Input X [M x N] of the up-projection (N = model width)."""
+        return normal(self.seed + 4000, self.M, self.N, row0=row0, nrows=nrows)
+
+    def up_weight(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
+        """Up-projection weight W1 [K x N], std 1/sqrt(N)."""
+        return normal(self.seed + 5000, self.K, self.N, std=float(self.N) ** -0.5, row0=row0,
+                      nrows=nrows)
 
     def dy(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
         return signed_lognormal(self.seed + 2000, self.M, self.N, 3.0, row0=row0, nrows=nrows)
