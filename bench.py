@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 METRIC = "fused FP8 quantize GB/s (% HBM peak); FP8 down-proj GEMM TFLOPS (% peak)"
 
 
@@ -211,6 +212,7 @@ def main():
         out["naive_three_pass"] = naive(sq, torch, H, A16[0], A8[0], n_in, args, dev, q_bytes,
                                         elems, q_mean)
     out["gemm_exact_accumulation"] = gemm_exact(sq, torch, A8[0], w8, st_a, wsc, Y, args, flops)
+    out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -272,6 +274,59 @@ def naive(sq, torch, H, a16, a8, n_in, args, dev, q_bytes, elems, fused_ms):
     return {"ms": round(ms, 5), "GB/s_of_its_own_traffic": round(naive_bytes / (ms * 1e-3) / 1e9, 1),
             "bytes_per_pass": naive_bytes,
             "fused_speedup": round(ms / fused_ms, 3)}
+
+
+def fused_up(sq, torch, np, w, A16, A8, dev, args):
+    """The quantizer fused into the up-projection's epilogue: X [M x N] x
+    W1 [K x N]^T -> H [M x K] never stored; BF16 copy + E4M3 codes written.
+    Timed against the same GEMM writing H followed by quantize_fused on H."""
+    M, K, N = w.M, w.K, w.N
+    x = torch.from_numpy(w.up_x().view(np.int16)).to(dev).view(torch.bfloat16)
+    w1 = torch.from_numpy(w.up_weight().view(np.int16)).to(dev).view(torch.bfloat16)
+    h = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    st = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
+    stream = torch.cuda.current_stream()
+    n_out = len(A16)
+    # one step first, so the delayed scale is the one this data produces
+    sq.gemm_bf16_quantize_fused(x, w1, sq.ACT_RELU2, sq.E4M3, st, None, None, A8[0])
+    sq.amax_history_update(st)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    fused = timed(lambda i: sq.gemm_bf16_quantize_fused(x, w1, sq.ACT_RELU2, sq.E4M3, st, None,
+                                                        A16[i % n_out], A8[i % n_out]))
+    gemm = timed(lambda i: sq.gemm_bf16_quantize_fused(x, w1, h_out=h))
+
+    def unfused(i):
+        sq.gemm_bf16_quantize_fused(x, w1, h_out=h)
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st, A16[i % n_out], A8[i % n_out])
+
+    two = timed(unfused)
+    lib_ms = None
+    try:
+        lib_ms = timed(lambda i: torch.matmul(x, w1.t()))
+    except Exception:
+        pass
+    flops = 2.0 * M * N * K
+    tf = flops / (fused * 1e-3) / 1e12
+    return {"shape": f"X[{M}x{N}] x W1[{K}x{N}]^T -> relu2 -> bf16 copy + e4m3",
+            "ms": round(fused, 5), "TFLOP/s": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "bytes_written": M * K * 3,
+            "gemm_writing_H_ms": round(gemm, 5),
+            "gemm_then_quantize_ms": round(two, 5),
+            "fused_speedup": round(two / fused, 3),
+            "hipblaslt_bf16_gemm_ms": None if lib_ms is None else round(lib_ms, 5)}
 
 
 def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):

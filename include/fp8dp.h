@@ -192,6 +192,31 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
 int quantize_weight(const uint16_t* w, int64_t N, int64_t K, fp8dp_format fmt,
                     fp8dp_scale_mode mode, uint8_t* w8, float* scale_out, hipStream_t stream);
 
+/* Up-projection BF16 GEMM with the quantizer in its epilogue ("Paradigma
+ * Details FP8 and Optimizer Tricks Behind NanoGPT Records", FP8 paragraph:
+ * the fused kernel handles the preceding computation's results while they
+ * are still in registers, so the intermediate is neither written out nor
+ * read back).
+ *   x [M x K] BF16 (the MLP input), w [N x K] BF16 (the up-projection weight
+ *   in linear-layer layout); H = bf16_rne(x w^T) with FP32 accumulation
+ *   (the BF16 matrix instructions; products are exact in FP32).
+ *   fp8_out != NULL: the epilogue applies quantize_fused(H, act, fmt,
+ *     PER_TENSOR, st, bf16_out, fp8_out) element for element: b =
+ *     bf16_rne(act(H)) to bf16_out (may be NULL), fp8_out [M x N] codes cast
+ *     with st->scale, running amax of |b| and the saturation count folded
+ *     into st's accumulator slots (amax_history_update consumes them).
+ *     h_out [M x N] BF16 receives H when non-NULL.
+ *   fp8_out == NULL: the plain GEMM, H to h_out (required); bf16_out and st
+ *     must be NULL.
+ * All pointers are device pointers owned by the caller; nothing is allocated.
+ * Errors: EINVAL for NULL x or w, M not a positive multiple of 256, N of 128
+ * or K of 64, misaligned pointers (16 bytes), a missing state with fp8_out,
+ * or an unknown act / fmt. */
+int gemm_bf16_quantize_fused(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                             int64_t K, fp8dp_act act, fp8dp_format fmt, fp8dp_tensor_state* st,
+                             uint16_t* h_out, uint16_t* bf16_out, uint8_t* fp8_out,
+                             hipStream_t stream);
+
 /* (host) Message for the last failing call on this thread ("" if none). */
 const char* fp8dp_last_error(void);
 

@@ -8,7 +8,7 @@ It raises if the library has not been built; there is no CPU fallback.
 
 Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, fp8_gemm_scaled,
-    quantize_weight, and the comparison / diagnostic calls fp8dp_bench_*,
+    quantize_weight, gemm_bf16_quantize_fused, and the comparison / diagnostic calls fp8dp_bench_*,
     fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit, fp8dp_set_codec.
 """
 from __future__ import annotations
@@ -45,6 +45,8 @@ _SIGS = {
     "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                          _vp], ctypes.c_int),
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
+                                  _vp], ctypes.c_int),
     "fp8dp_last_error": ([], ctypes.c_char_p),
     "fp8dp_bench_act_bf16": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
     "fp8dp_bench_amax": ([_vp, _i64, _vp, _vp], ctypes.c_int),
@@ -199,6 +201,19 @@ def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scal
     N, K = w.shape
     _check(lib().quantize_weight(_p(w), N, K, fmt, mode, _p(w8), _p(scale_out), _stream(stream)),
            "quantize_weight")
+
+
+def gemm_bf16_quantize_fused(x: torch.Tensor, w: torch.Tensor, act: int = ACT_RELU2,
+                             fmt: int = E4M3, st=None, h_out: Ptr = None, bf16_out: Ptr = None,
+                             fp8_out: Ptr = None, stream=None) -> None:
+    """x [M, K] BF16, w [N, K] BF16 device tensors; outputs [M, N] (see the C header)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise Fp8dpError("gemm_bf16_quantize_fused: shape mismatch")
+    _check(lib().gemm_bf16_quantize_fused(_p(x), _p(w), M, N, K, act, fmt, _state_ptr(st),
+                                          _p(h_out), _p(bf16_out), _p(fp8_out), _stream(stream)),
+           "gemm_bf16_quantize_fused")
 
 
 def fp8dp_bench_act_bf16(h: torch.Tensor, act: int, out: torch.Tensor, stream=None) -> None:

@@ -1,0 +1,278 @@
+// fused_up.hip -- BF16 GEMM of the MLP up-projection with the quantizer in its
+// epilogue.
+//
+// "Paradigma Details FP8 and Optimizer Tricks Behind NanoGPT Records", FP8
+// paragraph: instead of writing the intermediate tensor out and reading it
+// back to scan its maximum and to convert it, one kernel produces the BF16
+// copy the backward pass needs, the FP8 copy and the running maxima while the
+// preceding computation's results are still in registers.  Here the preceding
+// computation is the up-projection H = X W1^T, so H itself never goes to
+// memory: each output tile leaves the MFMA accumulators as
+//   h = bf16_rne(acc)            (the value H would have had in memory)
+//   b = bf16_rne(act(h))         -> BF16 copy
+//   v = fp32(b * s); q = sat_rne_fp8(v)  -> FP8 copy, s the delayed scale
+//   amax = max |b|, count of saturating v  -> the state's accumulator slots
+// which is, element for element, quantize_fused applied to bf16(X W1^T).
+//
+// Kernel (gfx950): the large-tile pipeline of the FP8 GEMM (gemm_core.hpp)
+// with BF16 operands: a 128-byte LDS row holds 64 BF16 values of K, and each
+// 64-value half stage is two k steps of v_mfma_f32_32x32x16_bf16, which take
+// the same MFMA cycles per stage as the FP8 instruction.  512 threads (8
+// waves, two per SIMD) own a 256 x BN tile (BN = 128, 192 or 256); wave w
+// owns 64 x BN/2 as 2 x TN MFMA tiles.
+#include <hip/hip_runtime.h>
+
+#include "codec.hpp"
+#include "common.hpp"
+#include "gemm_core.hpp"
+#include "quant_core.hpp"
+
+namespace fp8dp {
+
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+
+// Stores the 8 packed 16-bit pairs of one 32 x 32 tile's lane.  Pair p holds
+// rows R_p and R_p + 1 of the lane's column c (lane % 32); one DPP swap with
+// the neighbour lane (quad_perm 1,0,3,2) turns them into (R_p, c..c+1) on
+// the even lane and (R_p + 1, c-1..c) on the odd lane, stored as one 32-bit
+// word at the even column.  R_p = 8 (p / 2) + 4 (lane / 32) + 2 (p % 2).
+// (Issuing the MFMA with swapped operands, so that each lane holds runs of
+// four consecutive columns of one row, needs no exchange but was measured
+// slower: each store instruction then touches 32 rows.)
+__device__ __forceinline__ void store_pairs16(const uint32_t v[8], uint16_t* out, int row0,
+                                              int col0, int ld, int lane) {
+  const bool odd = lane & 1;
+  const int col = col0 + ((lane & 31) & ~1);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t give = odd ? (v[p] & 0xFFFFu) : (v[p] >> 16);
+    const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
+    const uint32_t packed = odd ? (got | (v[p] & 0xFFFF0000u)) : ((v[p] & 0xFFFFu) | (got << 16));
+    const int row = row0 + 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (odd ? 1 : 0);
+    *reinterpret_cast<uint32_t*>(out + (size_t)row * ld + col) = packed;
+  }
+}
+
+// The same for the 8-bit codes: code pair p is bytes 2p (row R_p) and 2p + 1
+// (row R_p + 1) of the 16 codes in q[0..3].
+__device__ __forceinline__ void store_pairs8(const uint32_t q[4], uint8_t* out, int row0,
+                                             int col0, int ld, int lane) {
+  const bool odd = lane & 1;
+  const int col = col0 + ((lane & 31) & ~1);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t c16 = (q[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+    const uint32_t give = odd ? (c16 & 0xFFu) : (c16 >> 8);
+    const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
+    const uint32_t packed = odd ? (got | (c16 & 0xFF00u)) : ((c16 & 0xFFu) | (got << 8));
+    const int row = row0 + 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (odd ? 1 : 0);
+    *reinterpret_cast<uint16_t*>(out + (size_t)row * ld + col) = (uint16_t)packed;
+  }
+}
+
+// QUANT = false: plain BF16 GEMM, H = bf16(X W^T) to h_out.
+// QUANT = true: the quantizing epilogue; h_out and b_out may be null.
+template <int TN, int ACT, int FMT, bool QUANT>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int M, int N, int K,
+    const float* __restrict__ scale_ptr, fp8dp_acc_slot* __restrict__ slots,
+    uint16_t* __restrict__ h_out, uint16_t* __restrict__ b_out, uint8_t* __restrict__ q_out) {
+  constexpr int BM = 256, BN = 64 * TN, TM = 2;
+  constexpr int ASZ = BM * kBK, SLOT = (BM + BN) * kBK;
+  constexpr int LA = BM / 64, LB = BN / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+
+  const int tiles_n = N / BN;
+  const int ntiles = (M / BM) * tiles_n;
+  const int tile = tile_of_block(blockIdx.x, ntiles);
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = (wave >> 1) * 64;
+  const int wc = (wave & 1) * (BN / 2);
+  const size_t rowbytes = (size_t)K * 2;
+  const int KT = (int)(rowbytes / kBK);
+
+  // copies: as in the FP8 kernel, over rows of K * 2 bytes
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7);
+  const uint8_t* gA = reinterpret_cast<const uint8_t*>(X) + (size_t)(m0 + wave * 8 + lrow) * rowbytes + lchunk * 16;
+  const uint8_t* gB = reinterpret_cast<const uint8_t*>(W) + (size_t)(n0 + wave * 8 + lrow) * rowbytes + lchunk * 16;
+  const size_t rstep = (size_t)64 * rowbytes;
+  auto issue = [&](int kt) {
+    uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
+    const size_t k0 = (size_t)kt * kBK;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
+  };
+
+  // fragments of half stage h: k steps q = 2h, 2h + 1 of 16 values; the lane
+  // reads chunk 2q + lane / 32 (8 BF16 values) of its row.  A and B use the
+  // same k assignment, which is all a dot product needs.
+  const int frow = lane & 31;
+  const int fsel = lane >> 5;
+  auto load_frags = [&](int kt, int h, v8bf_t fa[][2], v8bf_t fb[][2]) {
+    const uint8_t* sA = lds + (kt & 1) * SLOT;
+    const uint8_t* sB = sA + ASZ;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int c = 2 * (2 * h + qq) + fsel;
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        fa[t][qq] = __builtin_bit_cast(
+            v8bf_t, *reinterpret_cast<const u32x4_t*>(sA + swz(wr + t * 32 + frow, c)));
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        fb[t][qq] = __builtin_bit_cast(
+            v8bf_t, *reinterpret_cast<const u32x4_t*>(sB + swz(wc + t * 32 + frow, c)));
+    }
+  };
+
+  v16f_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto mfmas = [&](v8bf_t fa[][2], v8bf_t fb[][2]) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][qq], fb[j][qq], acc[i][j], 0, 0, 0);
+  };
+
+  issue(0);
+  if (KT > 1) {
+    issue(1);
+    wait_vmcnt<LA + LB>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  stage_barrier();
+  v8bf_t fa0[TM][2], fb0[TN][2], fa1[TM][2], fb1[TN][2];
+  load_frags(0, 0, fa0, fb0);
+  for (int kt = 0; kt < KT; ++kt) {
+    load_frags(kt, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + 2 < KT) issue(kt + 2);
+    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0);
+    mfmas(fa1, fb1);
+  }
+
+  // epilogue
+  const float s = QUANT ? *scale_ptr : 1.0f;
+  uint32_t amax16 = 0, sat = 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row0 = m0 + wr + i * 32;
+      const int col0 = n0 + wc + j * 32;
+      uint32_t hb[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) hb[p] = pack2_bf16_hw(acc[i][j][2 * p], acc[i][j][2 * p + 1]);
+      if (!QUANT || h_out != nullptr) store_pairs16(hb, h_out, row0, col0, N, lane);
+      if constexpr (QUANT) {
+        uint32_t b[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) b[p] = act_pair<ACT, true>(hb[p]);
+        if (b_out != nullptr) store_pairs16(b, b_out, row0, col0, N, lane);
+        const uint32_t mx0 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
+        const uint32_t mx1 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b + 4);
+        const uint32_t mx = mx0 > mx1 ? mx0 : mx1;
+        amax16 = mx > amax16 ? mx : amax16;
+        const uint2 q0 = cast8<FMT, true>(b, mx0, s, sat);
+        const uint2 q1 = cast8<FMT, true>(b + 4, mx1, s, sat);
+        const uint32_t q[4] = {q0.x, q0.y, q1.x, q1.y};
+        store_pairs8(q, q_out, row0, col0, N, lane);
+      }
+    }
+  if constexpr (QUANT) block_fold<512>(amax16, sat, slots);
+}
+
+template <int TN, int ACT, int FMT, bool QUANT>
+static int launch_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                       fp8dp_tensor_state* st, uint16_t* h_out, uint16_t* b_out, uint8_t* q_out,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_bf16<TN, ACT, FMT, QUANT>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, x, w,
+                     (int)M, (int)N, (int)K, QUANT ? &st->scale : nullptr,
+                     QUANT ? st->acc : nullptr, h_out, b_out, q_out);
+  return check_launch("gemm_bf16_quantize_fused");
+}
+
+template <int ACT, int FMT, bool QUANT>
+static int launch_bf16_tile(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                            fp8dp_tensor_state* st, uint16_t* h_out, uint16_t* b_out,
+                            uint8_t* q_out, hipStream_t stream) {
+  if (N % 192 == 0) return launch_bf16<3, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
+  if (N % 256 == 0) return launch_bf16<4, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
+  return launch_bf16<2, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
+}
+
+}  // namespace fp8dp
+
+using namespace fp8dp;
+
+extern "C" int gemm_bf16_quantize_fused(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                        int64_t K, fp8dp_act act, fp8dp_format fmt,
+                                        fp8dp_tensor_state* st, uint16_t* h_out,
+                                        uint16_t* bf16_out, uint8_t* fp8_out,
+                                        hipStream_t stream) {
+  if (x == nullptr || w == nullptr) {
+    set_error("gemm_bf16_quantize_fused: x and w must be non-NULL");
+    return FP8DP_EINVAL;
+  }
+  if (M < 256 || N < 128 || K < 64 || M % 256 || N % 128 || K % 64) {
+    set_error("gemm_bf16_quantize_fused: M must be a positive multiple of 256, N of 128 and K of "
+              "64 (got %lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
+    return FP8DP_EINVAL;
+  }
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 29 ||
+      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
+    set_error("gemm_bf16_quantize_fused: shape too large");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(x) || !aligned16(w) || !aligned16(h_out) || !aligned16(bf16_out) ||
+      !aligned16(fp8_out)) {
+    set_error("gemm_bf16_quantize_fused: tensors must be 16-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  if (fp8_out == nullptr) {
+    if (h_out == nullptr || bf16_out != nullptr || st != nullptr) {
+      set_error("gemm_bf16_quantize_fused: without fp8_out it is the plain GEMM: h_out required, "
+                "bf16_out and st must be NULL");
+      return FP8DP_EINVAL;
+    }
+    return launch_bf16_tile<FP8DP_ACT_IDENTITY, 0, false>(x, w, M, N, K, nullptr, h_out, nullptr,
+                                                           nullptr, stream);
+  }
+  if (st == nullptr || reinterpret_cast<uintptr_t>(st) & 15u) {
+    set_error("gemm_bf16_quantize_fused: fp8_out needs a 16-byte aligned scaling state");
+    return FP8DP_EINVAL;
+  }
+  if ((act != FP8DP_ACT_IDENTITY && act != FP8DP_ACT_RELU2) ||
+      (fmt != FP8DP_E4M3 && fmt != FP8DP_E5M2)) {
+    set_error("gemm_bf16_quantize_fused: unknown activation or format");
+    return FP8DP_EINVAL;
+  }
+  if (act == FP8DP_ACT_RELU2) {
+    if (fmt == FP8DP_E4M3)
+      return launch_bf16_tile<FP8DP_ACT_RELU2, 0, true>(x, w, M, N, K, st, h_out, bf16_out, fp8_out, stream);
+    return launch_bf16_tile<FP8DP_ACT_RELU2, 1, true>(x, w, M, N, K, st, h_out, bf16_out, fp8_out, stream);
+  }
+  if (fmt == FP8DP_E4M3)
+    return launch_bf16_tile<FP8DP_ACT_IDENTITY, 0, true>(x, w, M, N, K, st, h_out, bf16_out, fp8_out, stream);
+  return launch_bf16_tile<FP8DP_ACT_IDENTITY, 1, true>(x, w, M, N, K, st, h_out, bf16_out, fp8_out, stream);
+}

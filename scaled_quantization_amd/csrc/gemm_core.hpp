@@ -1,0 +1,61 @@
+// gemm_core.hpp -- pieces shared by the matrix kernels (gfx950): MFMA
+// operand types, the LDS tile layout, the workgroup -> tile order, direct
+// global -> LDS copies and the barrier / wait primitives of the pipelined
+// large-tile loop.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8dp {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 128;   // bytes of K per LDS stage (one 128-byte row per operand row)
+
+// LDS layout of a tile with 128-byte rows: 16-byte chunk c of row r sits at
+// chunk c ^ ((r / 2) % 8).  gfx950's LDS serves 16 lanes of a 16-byte read
+// per cycle from 64 banks (256 bytes, two rows); a fragment read has those 16
+// lanes on 16 consecutive rows at one logical chunk, and (r % 2, (r / 2) % 8)
+// takes all 16 values over them, so the 16 chunks hit 16 distinct bank groups.
+// (The 32-bank pattern c ^ (r % 8) gives rows r and r + 8 the same banks.)
+__device__ __forceinline__ int swz(int r, int chunk) {
+  return r * kBK + ((chunk ^ ((r >> 1) & 7)) << 4);
+}
+
+// blockIdx -> output tile.  Workgroups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8); renumbering so that each XCD receives a
+// contiguous run of tiles keeps tiles that share A rows in one XCD's L2.
+__device__ __forceinline__ int tile_of_block(int b, int ntiles) {
+  const int per = ntiles / 8;
+  if (per * 8 != ntiles) return b;
+  return (b % 8) * per + b / 8;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+}
+
+
+// s_waitcnt with vmcnt(N) and no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that neither the compiler's scheduler nor its memory
+// model may move anything across, and that leaves the memory counters alone
+// (__syncthreads() would also drain every copy in flight).
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+}  // namespace fp8dp

@@ -25,6 +25,7 @@
 
 #include "codec.hpp"
 #include "common.hpp"
+#include "quant_core.hpp"
 
 namespace fp8dp {
 
@@ -32,7 +33,6 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
 constexpr int kBlocksPerCU = 32;   // grid of the element-wise kernels
 
-typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load marked non-temporal (streamed data that is not read again).
@@ -49,102 +49,6 @@ __device__ __forceinline__ void store_nt(uint4* p, uint32_t a, uint32_t b, uint3
 __device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
-}
-
-// Largest 16-bit magnitude among the 8 BF16 values of a vector.
-template <bool SIGNED>
-__device__ __forceinline__ uint32_t vec_absmax16(const uint32_t b[4]) {
-  ushort2_t m = {0, 0};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = SIGNED ? (b[j] & 0x7FFF7FFFu) : b[j];
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w));
-  }
-  return m.x > m.y ? m.x : m.y;
-}
-
-// BF16 activation of one packed pair (low half first).
-template <int ACT, bool HW>
-__device__ __forceinline__ uint32_t act_pair(uint32_t w) {
-  if constexpr (ACT == FP8DP_ACT_IDENTITY) {
-    return w;
-  } else {
-    const float lo = relu2(__uint_as_float(w << 16));
-    const float hi = relu2(__uint_as_float(w & 0xFFFF0000u));
-    return HW ? pack2_bf16_hw(lo, hi) : pack2_bf16_int(lo, hi);
-  }
-}
-
-// Casts the 8 BF16 values of a vector with multiplier s; returns the 8 codes
-// packed little-endian and adds saturating elements to `sat`.  `mx` is the
-// vector's largest BF16 magnitude.
-template <int FMT, bool HW>
-__device__ __forceinline__ uint2 cast8(const uint32_t b[4], uint32_t mx, float s, uint32_t& sat) {
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = __fmul_rn(__uint_as_float(b[j] << 16), s);
-    v[2 * j + 1] = __fmul_rn(__uint_as_float(b[j] & 0xFFFF0000u), s);
-  }
-  const uint32_t vmax = __float_as_uint(__fmul_rn(__uint_as_float(mx << 16), s));
-  const bool risky = (FMT == 0) ? (vmax > kE4M3SatAbove) : (vmax >= kE5M2SatFrom);
-  uint2 q;
-  if (!HW || risky) {
-    q.x = pack4_int<FMT>(v[0], v[1], v[2], v[3]);
-    q.y = pack4_int<FMT>(v[4], v[5], v[6], v[7]);
-    if (risky) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sat += saturates<FMT>(v[j]);
-    }
-  } else {
-    q.x = pack4_hw<FMT>(v[0], v[1], v[2], v[3]);
-    q.y = pack4_hw<FMT>(v[4], v[5], v[6], v[7]);
-  }
-  return q;
-}
-
-// One element (ragged tails): returns its BF16 copy, code and counts.
-template <int FMT, int ACT>
-__device__ __forceinline__ void quant_one(uint16_t h, float s, uint16_t& b, uint8_t& q,
-                                          uint32_t& amax16, uint32_t& sat) {
-  uint32_t bb = h;
-  if constexpr (ACT == FP8DP_ACT_RELU2) bb = bf16_rne_int(relu2(__uint_as_float((uint32_t)h << 16)));
-  b = (uint16_t)bb;
-  const uint32_t mag = bb & 0x7FFFu;
-  amax16 = mag > amax16 ? mag : amax16;
-  const float v = __fmul_rn(__uint_as_float(bb << 16), s);
-  q = (uint8_t)enc_int<FMT>(v);
-  sat += saturates<FMT>(v);
-}
-
-// Block-wide reduction of (amax16, sat) and one atomic pair into a slot.
-__device__ __forceinline__ void block_fold(uint32_t amax16, uint32_t sat, fp8dp_acc_slot* slots) {
-  __shared__ uint32_t s_max[kThreads / 64];
-  __shared__ uint32_t s_sat[kThreads / 64];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t om = __shfl_xor(amax16, off);
-    amax16 = om > amax16 ? om : amax16;
-    sat += __shfl_xor(sat, off);
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_max[w] = amax16;
-    s_sat[w] = sat;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = 0;
-    uint64_t c = 0;
-#pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) {
-      m = s_max[i] > m ? s_max[i] : m;
-      c += s_sat[i];
-    }
-    fp8dp_acc_slot* slot = slots + (blockIdx.x % FP8DP_ACC_SLOTS);
-    if (m) atomicMax(&slot->amax, m << 16);
-    if (c) atomicAdd((unsigned long long*)&slot->sat, (unsigned long long)c);
-  }
 }
 
 // ------------------------------------------------------------------ per tensor
@@ -191,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(
       if constexpr (AMAX) amax16 = a16 > amax16 ? a16 : amax16;
     }
   }
-  if (slots != nullptr && (AMAX || CAST)) block_fold(AMAX ? amax16 : 0u, CAST ? sat : 0u, slots);
+  if (slots != nullptr && (AMAX || CAST)) block_fold<kThreads>(AMAX ? amax16 : 0u, CAST ? sat : 0u, slots);
 }
 
 // ------------------------------------------------------------------ per group
@@ -242,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
     one(x1, i + stride);
   }
   if (i < n8) one(load_nt(h + i), i);
-  if constexpr (ACC) block_fold(amax16, sat, slots);
+  if constexpr (ACC) block_fold<kThreads>(amax16, sat, slots);
 }
 
 // ------------------------------------------------------------------ state

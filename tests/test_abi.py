@@ -31,7 +31,7 @@ def L():
 def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
-              "quantize_weight", "fp8dp_last_error"):
+              "quantize_weight", "gemm_bf16_quantize_fused", "fp8dp_last_error"):
         assert n in names
 
 
@@ -78,6 +78,21 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1
     rc = L.fp8dp_bench_copy(16, 16, 24, None)
     assert rc == -1
+    # gemm_bf16_quantize_fused(x, w, M, N, K, act, fmt, st, h_out, bf16_out, fp8_out, stream)
+    rc = L.gemm_bf16_quantize_fused(None, 16, 256, 128, 64, 1, 0, None, 16, None, None, None)
+    assert rc == -1 and b"non-NULL" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 16, 128, 128, 64, 1, 0, None, 16, None, None, None)
+    assert rc == -1 and b"256" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 16, 256, 128, 96, 1, 0, None, 16, None, None, None)
+    assert rc == -1 and b"64" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 16, 256, 128, 64, 1, 0, None, None, None, None, None)
+    assert rc == -1 and b"h_out" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 16, 256, 128, 64, 1, 0, None, None, None, 16, None)
+    assert rc == -1 and b"state" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 16, 256, 128, 64, 5, 0, 16, None, None, 16, None)
+    assert rc == -1 and b"activation" in L.fp8dp_last_error()
+    rc = L.gemm_bf16_quantize_fused(16, 24, 256, 128, 64, 1, 0, 16, None, None, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
 
 
 def test_switches_return_previous_value(L):
