@@ -18,8 +18,9 @@
 // with BF16 operands: a 128-byte LDS row holds 64 BF16 values of K, and each
 // 64-value half stage is two k steps of v_mfma_f32_32x32x16_bf16, which take
 // the same MFMA cycles per stage as the FP8 instruction.  512 threads (8
-// waves, two per SIMD) own a 256 x BN tile (BN = 128, 192 or 256); wave w
-// owns 64 x BN/2 as 2 x TN MFMA tiles.
+// waves, two per SIMD) own a 256 x BN tile (BN = 128, 192, or 256 for the
+// plain GEMM); wave w owns 64 x BN/2 as 2 x TN MFMA tiles.  The grid is
+// persistent: a workgroup runs its tiles back to back in one pipeline.
 #include <hip/hip_runtime.h>
 
 #include "codec.hpp"
@@ -31,43 +32,41 @@ namespace fp8dp {
 
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 
-// Stores the 8 packed 16-bit pairs of one 32 x 32 tile's lane.  Pair p holds
-// rows R_p and R_p + 1 of the lane's column c (lane % 32); one DPP swap with
-// the neighbour lane (quad_perm 1,0,3,2) turns them into (R_p, c..c+1) on
-// the even lane and (R_p + 1, c-1..c) on the odd lane, stored as one 32-bit
-// word at the even column.  R_p = 8 (p / 2) + 4 (lane / 32) + 2 (p % 2).
-// (Issuing the MFMA with swapped operands, so that each lane holds runs of
-// four consecutive columns of one row, needs no exchange but was measured
-// slower: each store instruction then touches 32 rows.)
-__device__ __forceinline__ void store_pairs16(const uint32_t v[8], uint16_t* out, int row0,
-                                              int col0, int ld, int lane) {
-  const bool odd = lane & 1;
-  const int col = col0 + ((lane & 31) & ~1);
+// Output path.  The MFMA is issued with the weight fragment first, so a
+// 32 x 32 accumulator tile holds Y^T: lane l has row l % 32 of the tile and
+// register r column 8 (r / 4) + 4 (l / 32) + r % 4 -- runs of four
+// consecutive columns.  Each wave stages one 32 x 32 tile at a time in a
+// private LDS area (one 8-byte write per run of BF16 values, one 4-byte write
+// per run of codes) and writes it out by rows, 16 bytes per lane.  Row pitches
+// of 72 and 40 bytes put the 32 rows of a column run on distinct banks.
+// (Storing the runs straight from registers touches 32 rows per store
+// instruction, and pairing columns across lanes with DPP costs ~27 vector
+// instructions per two elements; both were measured slower.)
+constexpr int kPitch16 = 72, kPitch8 = 40;
+constexpr int kStage16 = 32 * kPitch16, kStage8 = 32 * kPitch8;
+
+// Writes the staged 32 x 32 BF16 tile to out (row-major, leading dimension
+// ld) at (row0, col0): 64 bytes per row, 4 lanes per row, 16 rows per pass.
+__device__ __forceinline__ void flush16(const uint8_t* st, uint16_t* out, int row0, int col0,
+                                        int ld, int lane) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t give = odd ? (v[p] & 0xFFFFu) : (v[p] >> 16);
-    const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
-    const uint32_t packed = odd ? (got | (v[p] & 0xFFFF0000u)) : ((v[p] & 0xFFFFu) | (got << 16));
-    const int row = row0 + 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (odd ? 1 : 0);
-    *reinterpret_cast<uint32_t*>(out + (size_t)row * ld + col) = packed;
+  for (int k = 0; k < 2; ++k) {
+    const int r = (lane >> 2) + 16 * k, c = lane & 3;
+    const uint2 lo = *reinterpret_cast<const uint2*>(st + r * kPitch16 + c * 16);
+    const uint2 hi = *reinterpret_cast<const uint2*>(st + r * kPitch16 + c * 16 + 8);
+    *reinterpret_cast<uint4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) =
+        make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
-// The same for the 8-bit codes: code pair p is bytes 2p (row R_p) and 2p + 1
-// (row R_p + 1) of the 16 codes in q[0..3].
-__device__ __forceinline__ void store_pairs8(const uint32_t q[4], uint8_t* out, int row0,
-                                             int col0, int ld, int lane) {
-  const bool odd = lane & 1;
-  const int col = col0 + ((lane & 31) & ~1);
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t c16 = (q[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-    const uint32_t give = odd ? (c16 & 0xFFu) : (c16 >> 8);
-    const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
-    const uint32_t packed = odd ? (got | (c16 & 0xFF00u)) : ((c16 & 0xFFu) | (got << 8));
-    const int row = row0 + 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (odd ? 1 : 0);
-    *reinterpret_cast<uint16_t*>(out + (size_t)row * ld + col) = (uint16_t)packed;
-  }
+// The same for the staged 32 x 32 tile of codes: 32 bytes per row, 2 lanes per row.
+__device__ __forceinline__ void flush8(const uint8_t* st, uint8_t* out, int row0, int col0,
+                                       int ld, int lane) {
+  const int r = lane >> 1, c = lane & 1;
+  const uint2 lo = *reinterpret_cast<const uint2*>(st + r * kPitch8 + c * 16);
+  const uint2 hi = *reinterpret_cast<const uint2*>(st + r * kPitch8 + c * 16 + 8);
+  *reinterpret_cast<uint4*>(out + (size_t)(row0 + r) * ld + col0 + c * 16) =
+      make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // QUANT = false: plain BF16 GEMM, H = bf16(X W^T) to h_out.
@@ -80,33 +79,37 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, SLOT = (BM + BN) * kBK;
   constexpr int LA = BM / 64, LB = BN / 64;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT + 8 * (kStage16 + kStage8)];
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
-  const int tile = tile_of_block(blockIdx.x, ntiles);
-  const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
+  const int G = gridDim.x;
+  const int passes = tiles_of_block(blockIdx.x, G, ntiles);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = (wave >> 1) * 64;
   const int wc = (wave & 1) * (BN / 2);
   const size_t rowbytes = (size_t)K * 2;
   const int KT = (int)(rowbytes / kBK);
+  const int GS = passes * KT;   // stages this workgroup runs, tile after tile
 
-  // copies: as in the FP8 kernel, over rows of K * 2 bytes
+  // copies: as in the FP8 kernel, over rows of K * 2 bytes; stage g is
+  // k-stage g % KT of the tile of pass g / KT
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7);
-  const uint8_t* gA = reinterpret_cast<const uint8_t*>(X) + (size_t)(m0 + wave * 8 + lrow) * rowbytes + lchunk * 16;
-  const uint8_t* gB = reinterpret_cast<const uint8_t*>(W) + (size_t)(n0 + wave * 8 + lrow) * rowbytes + lchunk * 16;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(X) + (size_t)(wave * 8 + lrow) * rowbytes + lchunk * 16;
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(W) + (size_t)(wave * 8 + lrow) * rowbytes + lchunk * 16;
   const size_t rstep = (size_t)64 * rowbytes;
-  auto issue = [&](int kt) {
-    uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
-    const size_t k0 = (size_t)kt * kBK;
+  auto issue = [&](int g) {
+    const int tile = tile_of_pass(blockIdx.x, g / KT, G, ntiles);
+    const size_t k0 = (size_t)(g % KT) * kBK;
+    const uint8_t* gA = xb + (size_t)((tile / tiles_n) * BM) * rowbytes + k0;
+    const uint8_t* gB = wb + (size_t)((tile % tiles_n) * BN) * rowbytes + k0;
+    uint8_t* base = lds + (g & 1) * SLOT + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
+    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep, base + i * 8192);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
+    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep, base + ASZ + i * 8192);
   };
 
   // fragments of half stage h: k steps q = 2h, 2h + 1 of 16 values; the lane
@@ -114,8 +117,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(
   // same k assignment, which is all a dot product needs.
   const int frow = lane & 31;
   const int fsel = lane >> 5;
-  auto load_frags = [&](int kt, int h, v8bf_t fa[][2], v8bf_t fb[][2]) {
-    const uint8_t* sA = lds + (kt & 1) * SLOT;
+  auto load_frags = [&](int g, int h, v8bf_t fa[][2], v8bf_t fb[][2]) {
+    const uint8_t* sA = lds + (g & 1) * SLOT;
     const uint8_t* sB = sA + ASZ;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
@@ -132,12 +135,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(
   };
 
   v16f_t acc[TM][TN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  };
   auto mfmas = [&](v8bf_t fa[][2], v8bf_t fb[][2]) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
@@ -145,59 +150,94 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][qq], fb[j][qq], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j][qq], fa[i][qq], acc[i][j], 0, 0, 0);
   };
 
-  issue(0);
-  if (KT > 1) {
-    issue(1);
-    wait_vmcnt<LA + LB>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  stage_barrier();
-  v8bf_t fa0[TM][2], fb0[TN][2], fa1[TM][2], fb1[TN][2];
-  load_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < KT; ++kt) {
-    load_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    wait_vmcnt<0>();
-    stage_barrier();
-    if (kt + 2 < KT) issue(kt + 2);
-    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0);
-    mfmas(fa1, fb1);
-  }
-
-  // epilogue
   const float s = QUANT ? *scale_ptr : 1.0f;
   uint32_t amax16 = 0, sat = 0;
+  // epilogue of one tile, through this wave's staging area
+  uint8_t* st16 = lds + 2 * SLOT + wave * (kStage16 + kStage8);
+  uint8_t* st8 = st16 + kStage16;
+  const int srow = lane & 31, scol = 4 * (lane >> 5);
+  auto epilogue = [&](int tile) {
+    const int m0 = (tile / tiles_n) * BM;
+    const int n0 = (tile % tiles_n) * BN;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row0 = m0 + wr + i * 32;
-      const int col0 = n0 + wc + j * 32;
-      uint32_t hb[8];
+      for (int j = 0; j < TN; ++j) {
+        const int row0 = m0 + wr + i * 32;
+        const int col0 = n0 + wc + j * 32;
+        uint32_t hb[8];   // run g = pairs 2g, 2g + 1: columns 8 g + scol .. +3
 #pragma unroll
-      for (int p = 0; p < 8; ++p) hb[p] = pack2_bf16_hw(acc[i][j][2 * p], acc[i][j][2 * p + 1]);
-      if (!QUANT || h_out != nullptr) store_pairs16(hb, h_out, row0, col0, N, lane);
-      if constexpr (QUANT) {
-        uint32_t b[8];
+        for (int p = 0; p < 8; ++p) hb[p] = pack2_bf16_hw(acc[i][j][2 * p], acc[i][j][2 * p + 1]);
+        if (!QUANT || h_out != nullptr) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) b[p] = act_pair<ACT, true>(hb[p]);
-        if (b_out != nullptr) store_pairs16(b, b_out, row0, col0, N, lane);
-        const uint32_t mx0 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
-        const uint32_t mx1 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b + 4);
-        const uint32_t mx = mx0 > mx1 ? mx0 : mx1;
-        amax16 = mx > amax16 ? mx : amax16;
-        const uint2 q0 = cast8<FMT, true>(b, mx0, s, sat);
-        const uint2 q1 = cast8<FMT, true>(b + 4, mx1, s, sat);
-        const uint32_t q[4] = {q0.x, q0.y, q1.x, q1.y};
-        store_pairs8(q, q_out, row0, col0, N, lane);
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint2*>(st16 + srow * kPitch16 + (8 * g + scol) * 2) =
+                make_uint2(hb[2 * g], hb[2 * g + 1]);
+          flush16(st16, h_out, row0, col0, N, lane);
+        }
+        if constexpr (QUANT) {
+          uint32_t b[8];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) b[p] = act_pair<ACT, true>(hb[p]);
+          if (b_out != nullptr) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<uint2*>(st16 + srow * kPitch16 + (8 * g + scol) * 2) =
+                  make_uint2(b[2 * g], b[2 * g + 1]);
+            flush16(st16, b_out, row0, col0, N, lane);
+          }
+          const uint32_t mx0 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
+          const uint32_t mx1 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b + 4);
+          const uint32_t mx = mx0 > mx1 ? mx0 : mx1;
+          amax16 = mx > amax16 ? mx : amax16;
+          const uint2 q0 = cast8<FMT, true>(b, mx0, s, sat);       // runs 0, 1
+          const uint2 q1 = cast8<FMT, true>(b + 4, mx1, s, sat);   // runs 2, 3
+          const uint32_t q[4] = {q0.x, q0.y, q1.x, q1.y};
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint32_t*>(st8 + srow * kPitch8 + 8 * g + scol) = q[g];
+          flush8(st8, q_out, row0, col0, N, lane);
+        }
+      }
+  };
+
+  // One pipeline over all of this workgroup's stages: the copies of the next
+  // tile's first stages are in flight while a tile finishes and its epilogue
+  // runs.  (The copy-completion waits also wait for the epilogue's stores:
+  // the vector memory counter covers both.)
+  zero_acc();
+  if (GS > 0) {
+    issue(0);
+    if (GS > 1) {
+      issue(1);
+      wait_vmcnt<LA + LB>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    stage_barrier();
+    v8bf_t fa0[TM][2], fb0[TN][2], fa1[TM][2], fb1[TN][2];
+    load_frags(0, 0, fa0, fb0);
+    int kt = 0;
+    for (int g = 0; g < GS; ++g) {
+      load_frags(g, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      wait_vmcnt<0>();
+      stage_barrier();
+      if (g + 2 < GS) issue(g + 2);
+      if (g + 1 < GS) load_frags(g + 1, 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      if (++kt == KT) {
+        epilogue(tile_of_pass(blockIdx.x, g / KT, G, ntiles));
+        zero_acc();
+        kt = 0;
       }
     }
+  }
   if constexpr (QUANT) block_fold<512>(amax16, sat, slots);
 }
 
@@ -205,8 +245,14 @@ template <int TN, int ACT, int FMT, bool QUANT>
 static int launch_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
                        fp8dp_tensor_state* st, uint16_t* h_out, uint16_t* b_out, uint8_t* q_out,
                        hipStream_t stream) {
+  // persistent: at most one workgroup per compute unit (the LDS ring takes
+  // more than half of a CU's 160 KiB), a multiple of 8 for the XCD order
+  const int64_t ntiles = (M / 256) * (N / (64 * TN));
+  int64_t grid = ntiles;
+  const int64_t cus = num_cus() & ~7;
+  if (cus >= 8 && grid > cus) grid = cus;
   hipLaunchKernelGGL((k_gemm_bf16<TN, ACT, FMT, QUANT>),
-                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, x, w,
+                     dim3((unsigned)grid), dim3(512), 0, stream, x, w,
                      (int)M, (int)N, (int)K, QUANT ? &st->scale : nullptr,
                      QUANT ? st->acc : nullptr, h_out, b_out, q_out);
   return check_launch("gemm_bf16_quantize_fused");
@@ -216,8 +262,11 @@ template <int ACT, int FMT, bool QUANT>
 static int launch_bf16_tile(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
                             fp8dp_tensor_state* st, uint16_t* h_out, uint16_t* b_out,
                             uint8_t* q_out, hipStream_t stream) {
+  // (the quantizing epilogue does not fit the 256-wide tile's registers)
   if (N % 192 == 0) return launch_bf16<3, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
-  if (N % 256 == 0) return launch_bf16<4, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
+  if constexpr (!QUANT) {
+    if (N % 256 == 0) return launch_bf16<4, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
+  }
   return launch_bf16<2, ACT, FMT, QUANT>(x, w, M, N, K, st, h_out, b_out, q_out, stream);
 }
 

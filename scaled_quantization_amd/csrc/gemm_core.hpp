@@ -33,6 +33,23 @@ __device__ __forceinline__ int tile_of_block(int b, int ntiles) {
   return (b % 8) * per + b / 8;
 }
 
+// Persistent grids: G workgroups walk ntiles tiles.  With ntiles and G both
+// multiples of 8, workgroup b (on XCD b % 8) takes tiles b / 8, b / 8 + G / 8,
+// ... of that XCD's contiguous run of ntiles / 8 tiles (pass 0 is exactly
+// tile_of_block); otherwise tiles b, b + G, ...  tiles_of_block() is the
+// number of passes of workgroup b; tile_of_pass() the tile of pass p.
+__device__ __forceinline__ int tiles_of_block(int b, int G, int ntiles) {
+  if (ntiles % 8 == 0 && G % 8 == 0) {
+    const int per = ntiles / 8, gx = G / 8, l = b / 8;
+    return l < per ? (per - l + gx - 1) / gx : 0;
+  }
+  return b < ntiles ? (ntiles - b + G - 1) / G : 0;
+}
+__device__ __forceinline__ int tile_of_pass(int b, int p, int G, int ntiles) {
+  if (ntiles % 8 == 0 && G % 8 == 0) return (b % 8) * (ntiles / 8) + b / 8 + p * (G / 8);
+  return b + p * G;
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
