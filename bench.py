@@ -213,6 +213,7 @@ def main():
                                         elems, q_mean)
     out["gemm_exact_accumulation"] = gemm_exact(sq, torch, A8[0], w8, st_a, wsc, Y, args, flops)
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
+    out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -327,6 +328,52 @@ def fused_up(sq, torch, np, w, A16, A8, dev, args):
             "gemm_then_quantize_ms": round(two, 5),
             "fused_speedup": round(two / fused, 3),
             "hipblaslt_bf16_gemm_ms": None if lib_ms is None else round(lib_ms, 5)}
+
+
+def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
+    """The FP8 recipe's two backward GEMMs of the down-projection on the step's
+    codes: dA = dY W (E5M2 x E4M3, needs W8^T) and dW = dY^T A (split-K,
+    needs dY8^T and A8^T), with the transposes they need."""
+    M, K, N = w.M, w.K, w.N
+    stream = torch.cuda.current_stream()
+    w8t = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    dyt = torch.empty((N, M), dtype=torch.uint8, device=dev)
+    at = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(16 * N * K, dtype=torch.float32, device=dev)
+    si_g, si_a = st_g.field_ptr("scale_inv_used"), st_a.field_ptr("scale_inv_used")
+
+    def timed(fn, reps=None):
+        reps = reps or args.steps
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_w = timed(lambda: sq.fp8_transpose(w8, w8t))
+    t_dy = timed(lambda: sq.fp8_transpose(dy8, dyt))
+    t_a = timed(lambda: sq.fp8_transpose(A8[0], at))
+    t_dgrad = timed(lambda: sq.fp8_gemm_scaled(dy8, sq.E5M2, w8t, sq.E4M3, sq.PER_TENSOR, si_g,
+                                               wsc, dx))
+    flops = 2.0 * M * N * K
+    res = {"transpose_ms": {"W8 [768x3072]": round(t_w, 5), "dY8 [16384x768]": round(t_dy, 5),
+                            "A8 [16384x3072]": round(t_a, 5)},
+           "dgrad": {"shape": f"dY8[{M}x{N}] e5m2 x W8^T[{K}x{N}] e4m3 -> [{M}x{K}]",
+                     "ms": round(t_dgrad, 5), "TFLOP/s": round(flops / (t_dgrad * 1e-3) / 1e12, 1)},
+           "wgrad": {"shape": f"dY8^T[{N}x{M}] e5m2 x A8^T[{K}x{M}] e4m3 -> [{N}x{K}]"}}
+    for splits in (1, 4, 8, 16):
+        t = timed(lambda: sq.fp8_gemm_scaled_splitk(dyt, sq.E5M2, at, sq.E4M3, splits, si_g, si_a,
+                                                    ws, dw))
+        res["wgrad"][f"splits_{splits}"] = {"ms": round(t, 5),
+                                            "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1)}
+    return res
 
 
 def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):

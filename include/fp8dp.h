@@ -181,6 +181,34 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
                     const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
                     hipStream_t stream);
 
+/* The same GEMM (per-tensor scales, FP8 matrix instructions) with K split
+ * over `splits` workgroups per output tile, for outputs too small to fill the
+ * GPU on their own -- the weight-gradient GEMM of the FP8 recipe ("FP8
+ * Training & Inference", FP8 Training Recipe) has a [N x K] output and a
+ * contraction over all tokens.  Split s sums k in [s K/splits, (s+1)
+ * K/splits) into workspace[s][m][n] (FP32, unscaled); a second kernel adds
+ * the splits in order s = 0, 1, ... and writes
+ *   y = bf16_rne((sum_s workspace[s]) * a_scale_inv[0] * b_scale_inv[0]),
+ * so the result is deterministic; with splits = 1 it equals fp8_gemm_scaled
+ * (ACCUM_MFMA_FP8) bit for bit.
+ * workspace: caller-owned device memory of splits * M * N floats, 16-byte
+ * aligned; its contents are overwritten.
+ * Errors: EINVAL for NULL pointers, splits outside 1..64, M not a positive
+ * multiple of 256, N of 128, K of 128 * splits, misaligned pointers or a bad
+ * format. */
+int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
+                           int64_t M, int64_t N, int64_t K, int32_t splits,
+                           const float* a_scale_inv, const float* b_scale_inv, float* workspace,
+                           uint16_t* y, hipStream_t stream);
+
+/* dst [cols x rows] = src [rows x cols] transposed, bytes (FP8 codes): the
+ * operand layouts of the backward GEMMs (dgrad needs W^T, wgrad dY^T and
+ * X^T).  The codes and their scale are unchanged.
+ * Errors: EINVAL for NULL or misaligned (16 bytes) pointers, src == dst, or
+ * rows / cols not positive multiples of 64. */
+int fp8_transpose(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                  hipStream_t stream);
+
 /* Weight cast with current scaling ("FP8 training ...", Step 4: the 8-bit
  * copies are cast from the master weights at every step; Trade-offs: 128 x
  * 128 weight blocks).  w [N x K] BF16 -> w8 [N x K] codes.

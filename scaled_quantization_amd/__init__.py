@@ -8,7 +8,8 @@ It raises if the library has not been built; there is no CPU fallback.
 
 Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, fp8_gemm_scaled,
-    quantize_weight, gemm_bf16_quantize_fused, and the comparison / diagnostic calls fp8dp_bench_*,
+    quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
+    fp8_transpose, and the comparison / diagnostic calls fp8dp_bench_*,
     fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit, fp8dp_set_codec.
 """
 from __future__ import annotations
@@ -45,6 +46,9 @@ _SIGS = {
     "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                          _vp], ctypes.c_int),
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                                _vp], ctypes.c_int),
+    "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                   _vp], ctypes.c_int),
     "fp8dp_last_error": ([], ctypes.c_char_p),
@@ -194,6 +198,30 @@ def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: in
         raise Fp8dpError("fp8_gemm_scaled: shape mismatch")
     _check(lib().fp8_gemm_scaled(_p(a), fa, _p(b), fb, M, N, K, mode, accum, _p(a_scale_inv),
                                  _p(b_scale_inv), _p(y), _stream(stream)), "fp8_gemm_scaled")
+
+
+def fp8_gemm_scaled_splitk(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, splits: int,
+                           a_scale_inv: Ptr, b_scale_inv: Ptr, workspace: torch.Tensor,
+                           y: torch.Tensor, stream=None) -> None:
+    """Per-tensor FP8 GEMM with K split `splits` ways; workspace: float32 device
+    tensor of at least splits * M * N elements."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(y.shape) != (M, N):
+        raise Fp8dpError("fp8_gemm_scaled_splitk: shape mismatch")
+    if workspace.dtype != torch.float32 or workspace.numel() < splits * M * N:
+        raise Fp8dpError("fp8_gemm_scaled_splitk: workspace needs splits * M * N float32")
+    _check(lib().fp8_gemm_scaled_splitk(_p(a), fa, _p(b), fb, M, N, K, splits, _p(a_scale_inv),
+                                        _p(b_scale_inv), _p(workspace), _p(y), _stream(stream)),
+           "fp8_gemm_scaled_splitk")
+
+
+def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """dst [cols, rows] = src [rows, cols]^T (uint8 codes)."""
+    rows, cols = src.shape
+    if tuple(dst.shape) != (cols, rows):
+        raise Fp8dpError("fp8_transpose: shape mismatch")
+    _check(lib().fp8_transpose(_p(src), rows, cols, _p(dst), _stream(stream)), "fp8_transpose")
 
 
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,

@@ -262,12 +262,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
 // deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
 // the two waves of each SIMD with a barrier per phase were all slower.
-template <int FA, int FB, int TN>
+// SPLIT: workgroup u of (M/256)(N/BN) x splits runs split s = u' / ntiles of
+// tile u' % ntiles (u' = the XCD-ordered index), over K bytes
+// [s K/splits, (s+1) K/splits), and writes its FP32 sums, unscaled, to
+// ws[s][m][n]; k_splitk_reduce then adds the splits in order.
+template <int FA, int FB, int TN, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
                                                      const float* __restrict__ sb,
-                                                     uint16_t* __restrict__ Y) {
+                                                     uint16_t* __restrict__ Y,
+                                                     float* __restrict__ ws, int splits) {
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, SLOT = (BM + BN) * kBK;   // bytes of A / of one ring slot
   constexpr int LA = BM / 64, LB = BN / 64;                // copies per wave per stage
@@ -275,14 +280,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
-  const int tile = tile_of_block(blockIdx.x, ntiles);
+  int tile, split = 0;
+  if constexpr (SPLIT) {
+    const int u = tile_of_block(blockIdx.x, ntiles * splits);
+    split = u / ntiles;
+    tile = u % ntiles;
+  } else {
+    tile = tile_of_block(blockIdx.x, ntiles);
+  }
   const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = (wave >> 1) * 64;
   const int wc = (wave & 1) * (BN / 2);
-  const int KT = K / kBK;
+  const int KT = K / kBK / (SPLIT ? splits : 1);
+  const size_t kbase = (size_t)split * KT * kBK;
 
   // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7; lane l
   // lands at chunk l % 8 of row l / 8 there, so it fetches the logical chunk
@@ -290,8 +303,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   // (row / 2) % 8 = (4 wave + (l / 8) / 2) % 8 for every i
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7);
-  const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + lchunk * 16;
-  const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + lchunk * 16;
+  const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
+  const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
   const size_t rstep = (size_t)64 * K;
   auto issue = [&](int kt) {
     uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
@@ -367,6 +380,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     mfmas(fa1, fb1);
   }
 
+  if constexpr (SPLIT) {
+    // FP32 partial sums: lanes 0-31 of a store cover 32 consecutive columns
+    float* out = ws + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          out[(size_t)row * N + n0 + wc + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+    return;
+  }
+
   // epilogue: scale, round to BF16 and store pairs of adjacent columns.  In a
   // 32 x 32 MFMA tile the lane holds column lane % 32 and register r holds row
   // 8 (r / 4) + 4 (lane / 32) + r % 4; swapping one value with the neighbour
@@ -396,9 +424,60 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 template <int FA, int FB, int TN>
 static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                       const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
-                     dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y);
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
+                     dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
+}
+
+// y[m, n] = bf16_rne((sum over s in order of ws[s][m][n]) * sa[0] * sb[0]):
+// 8 consecutive elements per thread per iteration, grid-stride.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits,
+                                                       int64_t mn, const float* __restrict__ sa,
+                                                       const float* __restrict__ sb,
+                                                       uint16_t* __restrict__ y) {
+  const float f = sa[0] * sb[0];
+  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < mn; i += stride) {
+    float v[8];
+    {
+      const float4 a = *reinterpret_cast<const float4*>(ws + i);
+      const float4 b = *reinterpret_cast<const float4*>(ws + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    for (int s = 1; s < splits; ++s) {
+      const float* p = ws + (size_t)s * mn + i;
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    }
+    *reinterpret_cast<uint4*>(y + i) =
+        make_uint4(pack2_bf16_hw(v[0] * f, v[1] * f), pack2_bf16_hw(v[2] * f, v[3] * f),
+                   pack2_bf16_hw(v[4] * f, v[5] * f), pack2_bf16_hw(v[6] * f, v[7] * f));
+  }
+}
+
+template <int FA, int FB, int TN>
+static int launch_split(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                        int splits, const float* sa, const float* sb, float* ws, uint16_t* y,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, true>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)) * splits)), dim3(512), 0, stream,
+                     a, b, (int)M, (int)N, (int)K, sa, sb, y, ws, splits);
+  if (check_launch("fp8_gemm_scaled_splitk")) return FP8DP_EHIP;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3(grid_for(M * N / 8, 256, 8)), dim3(256), 0, stream, ws,
+                     splits, M * N, sa, sb, y);
+  return check_launch("fp8_gemm_scaled_splitk");
+}
+
+template <int FA, int FB>
+static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                             int splits, const float* sa, const float* sb, float* ws, uint16_t* y,
+                             hipStream_t stream) {
+  if (N % 192 == 0) return launch_split<FA, FB, 3>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
+  if (N % 256 == 0) return launch_split<FA, FB, 4>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
+  return launch_split<FA, FB, 2>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
 }
 
 template <int FA, int FB, int MODE, bool EXACT>
@@ -473,4 +552,50 @@ extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t*
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
     return launch_gemm<1, 0>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
   return launch_gemm<1, 1>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
+}
+
+extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                                      fp8dp_format fb, int64_t M, int64_t N, int64_t K,
+                                      int32_t splits, const float* a_scale_inv,
+                                      const float* b_scale_inv, float* workspace, uint16_t* y,
+                                      hipStream_t stream) {
+  if (a == nullptr || b == nullptr || y == nullptr || workspace == nullptr ||
+      a_scale_inv == nullptr || b_scale_inv == nullptr) {
+    set_error("fp8_gemm_scaled_splitk: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (splits < 1 || splits > 64) {
+    set_error("fp8_gemm_scaled_splitk: splits must be in 1..64 (got %d)", (int)splits);
+    return FP8DP_EINVAL;
+  }
+  if (M < 256 || N < 128 || K < 128 * (int64_t)splits || M % 256 || N % 128 ||
+      K % (128 * (int64_t)splits)) {
+    set_error("fp8_gemm_scaled_splitk: M must be a positive multiple of 256, N of 128 and K of "
+              "128 * splits (got %lld, %lld, %lld, splits %d)", (long long)M, (long long)N,
+              (long long)K, (int)splits);
+    return FP8DP_EINVAL;
+  }
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
+      (M / 256) * (N / 128) * splits > (int64_t)0x7FFFFFFF) {
+    set_error("fp8_gemm_scaled_splitk: shape too large");
+    return FP8DP_EINVAL;
+  }
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
+    set_error("fp8_gemm_scaled_splitk: unknown format");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u)) {
+    set_error("fp8_gemm_scaled_splitk: operands and workspace must be 16-byte aligned, scales "
+              "4-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
+    return launch_split_tile<0, 0>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
+    return launch_split_tile<0, 1>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
+  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
+    return launch_split_tile<1, 0>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
+  return launch_split_tile<1, 1>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
 }

@@ -31,7 +31,8 @@ def L():
 def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
-              "quantize_weight", "gemm_bf16_quantize_fused", "fp8dp_last_error"):
+              "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
+              "fp8_transpose", "fp8dp_last_error"):
         assert n in names
 
 
@@ -93,6 +94,19 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"activation" in L.fp8dp_last_error()
     rc = L.gemm_bf16_quantize_fused(16, 24, 256, 128, 64, 1, 0, 16, None, None, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    # fp8_gemm_scaled_splitk(a, fa, b, fb, M, N, K, splits, sa, sb, ws, y, stream)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 0, 16, 16, 16, 16, None)
+    assert rc == -1 and b"splits" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 384, 2, 16, 16, 16, 16, None)
+    assert rc == -1 and b"128 * splits" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, None, 16, None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, 24, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_transpose(16, 64, 96, 32, None)
+    assert rc == -1 and b"64" in L.fp8dp_last_error()
+    rc = L.fp8_transpose(16, 64, 64, 16, None)
+    assert rc == -1 and b"same buffer" in L.fp8dp_last_error()
 
 
 def test_switches_return_previous_value(L):
