@@ -38,6 +38,12 @@ PINNED = {
     "state/history": "closed-form delayed recurrence on the tiny workload",
     "quantize_weight_blocks": "brute force composition per block (numpy + nearest-code search)",
     "gemm_f64": "exact rational arithmetic (fractions) on small cases; identity and constant cases",
+    "mx_exponent": "closed form from the BF16 exponent and fraction bits at every BF16 magnitude; "
+                   "minimality and no-overflow invariants",
+    "quantize_mx": "nearest-code search over the decode table of b / 2^k with an independently "
+                   "computed k (pure Python); block locality; zero, infinity and NaN blocks",
+    "gemm_mx_f64": "float64 matmul of the dequantized operands; exact rational arithmetic on a "
+                   "small case; error bound against the unquantized product",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -119,6 +125,13 @@ def lib() -> ctypes.CDLL:
                                                 _u8p, _f32p, _f32p]
     L.oracle_fp8_encode_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, _u8p]
     L.oracle_bf16_rne_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _u16p]
+    L.oracle_mx_exponent.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    L.oracle_mx_exponent.restype = ctypes.c_int
+    L.oracle_quantize_mx.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_int, _u16p, _u8p, _u8p]
+    L.oracle_gemm_mx_f64.argtypes = [_u8p, ctypes.c_int, _u8p, _u8p, ctypes.c_int, _u8p,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
+                                     ctypes.c_int64, _f64p, _f64p]
     if L.oracle_state_size() != ctypes.sizeof(_State):
         raise RuntimeError("oracle_state layout mismatch between oracle.c and its wrapper")
     _lib = L
@@ -246,6 +259,61 @@ def quantize_weight_tensor(w: np.ndarray, fmt: int):
     s, si = scale_from_amax(amax, 1.0, fmt)
     r = quantize(w, ACT_IDENTITY, fmt, PER_TENSOR, float(s[0]), want_bf16=False)
     return r.fp8, float(s[0]), float(si[0])
+
+
+# --------------------------------------------------------------------------- MXFP8
+MX_BLOCK = 32
+
+
+def mx_exponent(amax: float, nonfinite: bool, fmt: int) -> int:
+    """Exponent k of an MXFP8 block's decode scale 2^k (E8M0 byte k + 127)."""
+    return int(lib().oracle_mx_exponent(float(amax), int(bool(nonfinite)), fmt))
+
+
+@dataclass
+class MXResult:
+    bf16: Optional[np.ndarray]    # uint16 [rows, cols] activation copy or None
+    fp8: Optional[np.ndarray]     # uint8 [rows, cols] codes or None
+    scale: np.ndarray             # uint8 [rows, cols/32] E8M0 bytes (decode scale 2^(e - 127))
+
+
+def quantize_mx(h: np.ndarray, act: int, fmt: int, want_bf16: bool = True,
+                want_fp8: bool = True) -> MXResult:
+    """MXFP8 cast of a row-major uint16 (BF16 bits) [rows, cols] array, cols % 32 == 0."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    if h.ndim == 1:
+        h = h.reshape(1, -1)
+    rows, cols = h.shape
+    if cols % MX_BLOCK:
+        raise ValueError("MXFP8 needs cols % 32 == 0")
+    bf = np.empty_like(h) if want_bf16 else None
+    q = np.empty(h.shape, dtype=np.uint8) if want_fp8 else None
+    e = np.empty((rows, cols // MX_BLOCK), dtype=np.uint8)
+    lib().oracle_quantize_mx(_ptr(h, _u16p), rows, cols, act, fmt, _ptr(bf, _u16p),
+                             _ptr(q, _u8p), _ptr(e, _u8p))
+    return MXResult(bf, q, e)
+
+
+def gemm_mx_f64(a: np.ndarray, fa: int, ea: np.ndarray, b: np.ndarray, fb: int, eb: np.ndarray,
+                rows: Optional[Sequence[int]] = None):
+    """Float64 reference of the MXFP8 GEMM y = a b^T with E8M0 block scales ea [M, K/32],
+    eb [N, K/32].  Returns (ref, absref), each float64 [len(rows) or M, N]."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    ea = np.ascontiguousarray(ea, dtype=np.uint8)
+    eb = np.ascontiguousarray(eb, dtype=np.uint8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2 and K % MX_BLOCK == 0
+    assert ea.size == M * (K // MX_BLOCK) and eb.size == N * (K // MX_BLOCK)
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    cnt = M if r is None else r.size
+    ref = np.empty((cnt, N), dtype=np.float64)
+    absref = np.empty((cnt, N), dtype=np.float64)
+    lib().oracle_gemm_mx_f64(_ptr(a, _u8p), fa, _ptr(ea, _u8p), _ptr(b, _u8p), fb, _ptr(eb, _u8p),
+                             M, N, K, _ptr(r, _i64p), 0 if r is None else r.size,
+                             _ptr(ref, _f64p), _ptr(absref, _f64p))
+    return ref, absref
 
 
 class State:

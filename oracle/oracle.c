@@ -450,6 +450,99 @@ void oracle_gemm_bf16_f64(const uint16_t* x, const uint16_t* w, int64_t M, int64
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP8 ([FP8T] "Trade-offs and edge cases": the microscaling recipe gives */
+/* each block of 32 adjacent values its own scale, and every scale is a     */
+/* power of two).                                                            */
+/* ------------------------------------------------------------------------ */
+#define ORC_MX_BLOCK 32
+
+/* Exponent k of a block's decode scale 2^k.  The pages fix only "power of
+   two"; the reading taken is the Step 2 rule (scale = format max / amax)
+   held to powers of two without letting the block's largest magnitude
+   overflow: k is the smallest integer in the E8M0 range [-127, 127] with
+   amax <= max * 2^k (a zero block gets -127).  When no k qualifies (an
+   infinity or a NaN in the block) k = 127.  The comparison is exact in
+   float64. */
+int oracle_mx_exponent(double amax, int nonfinite, int fmt) {
+  orc_format f = orc_fmt(fmt);
+  if (nonfinite) return 127;
+  for (int k = -127; k <= 127; ++k)
+    if (amax <= ldexp(f.maxval, k)) return k;
+  return 127;
+}
+
+/* One MXFP8 cast of a row-major [rows x cols] BF16 tensor, cols % 32 == 0.
+   Block j of a row is elements 32 j .. 32 j + 31 of that row.  For every
+   element: b = act(h) rounded to BF16 (the copy, as in oracle_quantize);
+   for every block: k from the largest |b| (oracle_mx_exponent), stored as
+   the E8M0 byte k + 127 in scale_e8m0[row * cols/32 + j]; each code is the
+   saturating RNE cast of b * 2^-k.  The product is formed exactly in
+   float64 and then narrowed to binary32, which is exact unless it lies
+   below the binary32 normal range, where every FP8 code is a signed zero
+   anyway.  bf16_out, fp8_out and scale_e8m0 may each be NULL. */
+void oracle_quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, int act, int fmt,
+                        uint16_t* bf16_out, uint8_t* fp8_out, uint8_t* scale_e8m0) {
+  int64_t nblocks = rows * (cols / ORC_MX_BLOCK);
+  for (int64_t g = 0; g < nblocks; ++g) {
+    uint16_t b[ORC_MX_BLOCK];
+    double amax = 0.0;
+    int nonfinite = 0;
+    for (int j = 0; j < ORC_MX_BLOCK; ++j) {
+      b[j] = act_bf16(h[g * ORC_MX_BLOCK + j], act);
+      double v = fabs((double)oracle_bf16_to_f32(b[j]));
+      if (isnan(v) || isinf(v)) nonfinite = 1;
+      else if (v > amax) amax = v;
+    }
+    int k = oracle_mx_exponent(amax, nonfinite, fmt);
+    if (scale_e8m0) scale_e8m0[g] = (uint8_t)(k + 127);
+    for (int j = 0; j < ORC_MX_BLOCK; ++j) {
+      if (bf16_out) bf16_out[g * ORC_MX_BLOCK + j] = b[j];
+      if (fp8_out) {
+        float v = (float)ldexp((double)oracle_bf16_to_f32(b[j]), -k);
+        fp8_out[g * ORC_MX_BLOCK + j] = oracle_fp8_encode(v, fmt);
+      }
+    }
+  }
+}
+
+/* Float64 reference of the MXFP8 GEMM y = a b^T, a [M x K] and b [N x K]
+   codes, each with its E8M0 block bytes ([M x K/32], [N x K/32]); every
+   32-wide block product is multiplied by both decode scales:
+     ref[r, n] = sum_j 2^(ea[m, j] - 127) 2^(eb[n, j] - 127)
+                       sum_{k in block j} dec(a[m, k]) dec(b[n, k])
+   absref the same with |products|.  rows selects output rows (NULL: all). */
+void oracle_gemm_mx_f64(const uint8_t* a, int fa, const uint8_t* ea, const uint8_t* b, int fb,
+                        const uint8_t* eb, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                        int64_t nrows, double* ref, double* absref) {
+  double da[256], db[256];
+  for (int c = 0; c < 256; ++c) {
+    da[c] = oracle_fp8_decode((uint8_t)c, fa);
+    db[c] = oracle_fp8_decode((uint8_t)c, fb);
+  }
+  int64_t count = rows ? nrows : M;
+  int64_t nb = K / ORC_MX_BLOCK;
+  for (int64_t r = 0; r < count; ++r) {
+    int64_t m = rows ? rows[r] : r;
+    for (int64_t n = 0; n < N; ++n) {
+      double total = 0.0, total_abs = 0.0;
+      for (int64_t j = 0; j < nb; ++j) {
+        double s = 0.0, sabs = 0.0;
+        for (int64_t k = j * ORC_MX_BLOCK; k < (j + 1) * ORC_MX_BLOCK; ++k) {
+          double p = da[a[m * K + k]] * db[b[n * K + k]];
+          s += p;
+          sabs += fabs(p);
+        }
+        double x = ldexp(1.0, (int)ea[m * nb + j] - 127 + (int)eb[n * nb + j] - 127);
+        total += s * x;
+        total_abs += sabs * x;
+      }
+      ref[r * N + n] = total;
+      if (absref) absref[r * N + n] = total_abs;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batch helpers (the per-element functions above applied to arrays).        */
 /* ------------------------------------------------------------------------ */
 void oracle_fp8_encode_batch(const float* x, int64_t n, int fmt, uint8_t* out) {
