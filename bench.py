@@ -214,6 +214,7 @@ def main():
     out["gemm_exact_accumulation"] = gemm_exact(sq, torch, A8[0], w8, st_a, wsc, Y, args, flops)
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
+    out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -374,6 +375,48 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
         res["wgrad"][f"splits_{splits}"] = {"ms": round(t, 5),
                                             "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1)}
     return res
+
+
+def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
+    """The microscaled variant of the step's forward half: quantize_mx of the
+    activation (relu2, BF16 copy, E4M3 codes + one E8M0 exponent per 32
+    values), quantize_mx of the weight, and the MX GEMM that applies the block
+    exponents inside the matrix instructions.  Timed like the per-tensor
+    kernels (back-to-back launches between two events)."""
+    M, K, N = w.M, w.K, w.N
+    stream = torch.cuda.current_stream()
+    n_in, n_out = len(H), len(A16)
+    E = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(n_out)]
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    we = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    q = timed(lambda i: sq.quantize_mx(H[i % n_in], sq.ACT_RELU2, sq.E4M3, A8[i % n_out],
+                                       E[i % n_out], A16[i % n_out]))
+    qw = timed(lambda i: sq.quantize_mx(wt, sq.ACT_IDENTITY, sq.E4M3, w8, we))
+    g = timed(lambda i: sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], w8, sq.E4M3, we, Y))
+    q_bytes = M * K * (2 + 2 + 1) + M * K // 32
+    flops = w.gemm_flops()
+    tf = flops / (g * 1e-3) / 1e12
+    return {"quantize_mx": {"ms": round(q, 5), "GB/s": round(q_bytes / (q * 1e-3) / 1e9, 1),
+                            "bytes_per_launch": q_bytes,
+                            "vs_per_tensor_quantize": round(q_tensor_ms / q, 3)},
+            "quantize_mx_weight_ms": round(qw, 5),
+            "fp8_gemm_mx": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
+                            "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                            "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
 
 
 def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):

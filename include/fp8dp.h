@@ -209,6 +209,38 @@ int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, 
 int fp8_transpose(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                   hipStream_t stream);
 
+/* MXFP8 cast ("FP8 training ...", Trade-offs and edge cases: the
+ * microscaling recipe gives each block of 32 adjacent values its own scale,
+ * a power of two).  h [rows x cols] BF16 (cols % 32 == 0); block j of a row
+ * is its elements 32 j .. 32 j + 31.
+ *   b = bf16_rne(act(h)) -> bf16_out (may be NULL)
+ *   per block: k = the smallest integer in [-127, 127] with
+ *     |b| <= max * 2^k for all 32 elements (zero blocks: -127; a block with
+ *     an infinity or NaN: 127), written as the E8M0 byte k + 127 to
+ *     scale_out[row * cols/32 + j] (decode scale 2^(byte - 127))
+ *   codes: fp8_out = sat_rne(b * 2^-k) (finite values never saturate).
+ * No scaling state is read or written.  Pointers are device pointers owned
+ * by the caller; nothing is allocated.
+ * Errors: EINVAL for NULL h / fp8_out / scale_out, rows < 1, cols not a
+ * positive multiple of 32, h, bf16_out or fp8_out not 16-byte aligned, or an
+ * unknown act / fmt. */
+int quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act, fp8dp_format fmt,
+                uint16_t* bf16_out, uint8_t* fp8_out, uint8_t* scale_out, hipStream_t stream);
+
+/* MXFP8 GEMM: a [M x K] codes (format fa) with E8M0 block exponents a_scale
+ * [M x K/32], b [N x K] codes (format fb) with b_scale [N x K/32] (the output
+ * of quantize_mx on each operand), y [M x N] BF16:
+ *   y = bf16_rne( sum_j 2^(a_scale[m, j] - 127) 2^(b_scale[n, j] - 127)
+ *                       sum_{k in block j} dec(a[m, k]) dec(b[n, k]) )
+ * with FP32 accumulation; the block scales are applied by the matrix
+ * instructions themselves (gfx950 microscaled MFMA), one per 32-value block.
+ * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
+ * not of 128, a, b or y not 16-byte aligned, exponent arrays not 4-byte
+ * aligned, or a bad format. */
+int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale, const uint8_t* b,
+                fp8dp_format fb, const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
+                uint16_t* y, hipStream_t stream);
+
 /* Weight cast with current scaling ("FP8 training ...", Step 4: the 8-bit
  * copies are cast from the master weights at every step; Trade-offs: 128 x
  * 128 weight blocks).  w [N x K] BF16 -> w8 [N x K] codes.

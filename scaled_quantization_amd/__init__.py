@@ -49,6 +49,8 @@ _SIGS = {
     "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
                                 _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "quantize_mx": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_mx": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                   _vp], ctypes.c_int),
     "fp8dp_last_error": ([], ctypes.c_char_p),
@@ -222,6 +224,30 @@ def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if tuple(dst.shape) != (cols, rows):
         raise Fp8dpError("fp8_transpose: shape mismatch")
     _check(lib().fp8_transpose(_p(src), rows, cols, _p(dst), _stream(stream)), "fp8_transpose")
+
+
+def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,
+                scale_out: torch.Tensor, bf16_out: Ptr = None, stream=None) -> None:
+    """MXFP8 cast: h [rows, cols] BF16 (cols % 32 == 0) -> fp8_out [rows, cols] codes and
+    scale_out [rows, cols/32] E8M0 block exponents (uint8)."""
+    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    if fp8_out.numel() != rows * cols or scale_out.numel() * 32 != rows * cols:
+        raise Fp8dpError("quantize_mx: output sizes do not match the input")
+    _check(lib().quantize_mx(_p(h), rows, cols, act, fmt, _p(bf16_out), _p(fp8_out),
+                             _p(scale_out), _stream(stream)), "quantize_mx")
+
+
+def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor, fb: int,
+                b_scale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """MXFP8 GEMM y [M, N] = a [M, K] b [N, K]^T with E8M0 block exponents
+    a_scale [M, K/32] and b_scale [N, K/32]."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(y.shape) != (M, N) or a_scale.numel() * 32 != M * K or \
+            b_scale.numel() * 32 != N * K:
+        raise Fp8dpError("fp8_gemm_mx: shape mismatch")
+    _check(lib().fp8_gemm_mx(_p(a), fa, _p(a_scale), _p(b), fb, _p(b_scale), M, N, K, _p(y),
+                             _stream(stream)), "fp8_gemm_mx")
 
 
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,

@@ -266,16 +266,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // tile u' % ntiles (u' = the XCD-ordered index), over K bytes
 // [s K/splits, (s+1) K/splits), and writes its FP32 sums, unscaled, to
 // ws[s][m][n]; k_splitk_reduce then adds the splits in order.
-template <int FA, int FB, int TN, bool SPLIT>
+// MX: microscaled operands (32-value blocks along k, E8M0 block exponents
+// ea [M x K/32], eb [N x K/32]).  A stage's 128 k bytes are 4 blocks, so each
+// tile row needs one dword of exponents per stage: waves 0-3 copy the 256 A
+// rows' dwords and waves 4-7 the B rows' into the ring slot next to the
+// tiles, with the same waits and barrier.  In the 32 x 32 x 64 instruction a
+// lane supplies the operand exponent of its fragment row for its 32 k bytes
+// (lane / 32 selects the half), which is exactly one block: the MFMA applies
+// 2^(ea - 127) 2^(eb - 127) to each block's products, and the epilogue has
+// no scale to apply.
+template <int FA, int FB, int TN, bool SPLIT, bool MX = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
                                                      const float* __restrict__ sb,
                                                      uint16_t* __restrict__ Y,
-                                                     float* __restrict__ ws, int splits) {
+                                                     float* __restrict__ ws, int splits,
+                                                     const uint8_t* __restrict__ ea = nullptr,
+                                                     const uint8_t* __restrict__ eb = nullptr) {
+  static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
-  constexpr int ASZ = BM * kBK, SLOT = (BM + BN) * kBK;   // bytes of A / of one ring slot
-  constexpr int LA = BM / 64, LB = BN / 64;                // copies per wave per stage
+  constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
+  constexpr int SLOT = TILES + (MX ? 2048 : 0);             // + 256 A and 256 B exponent dwords
+  constexpr int LA = BM / 64, LB = BN / 64;                 // tile copies per wave per stage
+  constexpr int NCOPY = LA + LB + (MX ? 1 : 0);             // copies per wave per stage
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
 
   const int tiles_n = N / BN;
@@ -306,6 +320,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
   const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
   const size_t rstep = (size_t)64 * K;
+  // exponent dwords: wave w < 4 fetches A row 64 w + lane, wave w >= 4 B row
+  // 64 (w - 4) + lane (clamped into the tile; the surplus dwords are unused)
+  const uint8_t* gE = nullptr;
+  if constexpr (MX) {
+    const int r = (wave & 3) * 64 + lane;
+    const size_t kb = (size_t)K / 32;
+    gE = wave < 4 ? ea + (size_t)(m0 + r) * kb + kbase / 32
+                  : eb + (size_t)(n0 + (r < BN ? r : BN - 1)) * kb + kbase / 32;
+  }
   auto issue = [&](int kt) {
     uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
     const size_t k0 = (size_t)kt * kBK;
@@ -313,28 +336,54 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
 #pragma unroll
     for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
+    if constexpr (MX) copy4_to_lds(gE + kt * 4, lds + (kt & 1) * SLOT + TILES + wave * 256);
   };
 
-  // this lane's fragment rows: A rows wr + 32 t + lane % 32, B rows wc + 32 t + lane % 32;
-  // k bytes 32 (lane / 32) .. +31 of the 64-byte substep h
+  // this lane's fragment rows: A rows wr + 32 t + lane % 32, B rows wc + 32 t + lane % 32.
+  // The instruction takes the 64 k of a substep as two 32-wide blocks: bytes
+  // 0-15 of lane l are k 16 (l / 32) .. +15 of the first block and bytes 16-31
+  // the same k of the second (measured with single-instruction probes), so
+  // the lane reads 16-byte chunks h*4 + l/32 and h*4 + 2 + l/32 of substep h.
+  // MX: lane l supplies the exponent of block l / 32 of its row, i.e. block
+  // 2 h + l / 32 of the stage, byte 2 h + l / 32 of the row's dword; the
+  // instruction reads the low byte of the scale operand.
   const int frow = lane & 31;
-  const int fhalf = (lane >> 5) * 2;
-  auto load_frags = [&](int kt, int h, v8i_t* fa, v8i_t* fb) {
+  const int fhalf = lane >> 5;
+  auto load_frags = [&](int kt, int h, v8i_t* fa, v8i_t* fb, uint32_t* xa, uint32_t* xb) {
     const uint8_t* sA = lds + (kt & 1) * SLOT;
     const uint8_t* sB = sA + ASZ;
     const int c0 = h * 4 + fhalf;
+    if constexpr (MX) {
+      // the exponents of this substep packed one per byte (fragment t in
+      // byte t, picked by the instruction's byte select): one register for
+      // A and one for B instead of one per fragment
+      const uint32_t* sE = reinterpret_cast<const uint32_t*>(sA + TILES);
+      const uint32_t bsel = 2 * h + fhalf;                       // byte of the row dword
+      const uint32_t pair = bsel | ((bsel + 4) << 8) | 0x0C0C0000u;   // -> bytes 0, 1; 0s above
+      xa[0] = __builtin_amdgcn_perm(sE[wr + 32 + frow], sE[wr + frow], pair);
+      const uint32_t* sEb = sE + 256 + wc + frow;
+      const uint32_t b01 = __builtin_amdgcn_perm(sEb[32], sEb[0], pair);
+      if constexpr (TN == 2) {
+        xb[0] = b01;
+      } else if constexpr (TN == 3) {
+        xb[0] = __builtin_amdgcn_perm(sEb[64], b01, 0x0C000100u | ((bsel + 4) << 16));
+      } else {
+        const uint32_t b23 = __builtin_amdgcn_perm(sEb[96], sEb[64], pair);
+        xb[0] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int r = wr + t * 32 + frow;
       const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
-      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 1));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 2));
       fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int r = wc + t * 32 + frow;
       const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
-      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 1));
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 2));
       fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
@@ -346,38 +395,59 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb) {
+  // Without MX the scale operands are the constant 0, which the compiler
+  // lowers to the unscaled instruction (checked in the generated assembly).
+  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa, const uint32_t* xb) {
+    if constexpr (MX) {
+      static_for<TM>([&](auto I) {
+        static_for<TN>([&](auto J) {
+          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[I], fb[J], acc[I][J], FA, FB, decltype(I)::value, (int)xa[0],
+              decltype(J)::value, (int)xb[0]);
+        });
+      });
+    } else {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], FA,
-                                                                   FB, 0, 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j],
+                                                                     FA, FB, 0, 0, 0, 0);
+    }
   };
 
   // prologue: stages 0 and 1 in flight, stage 0 landed and published
   issue(0);
   if (KT > 1) {
     issue(1);
-    wait_vmcnt<LA + LB>();
+    wait_vmcnt<NCOPY>();
   } else {
     wait_vmcnt<0>();
   }
   stage_barrier();
   v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  load_frags(0, 0, fa0, fb0);
+  uint32_t xa0[1], xb0[1], xa1[1], xb1[1];   // MX: packed block exponents
+  load_frags(0, 0, fa0, fb0, xa0, xb0);
   for (int kt = 0; kt < KT; ++kt) {
     // first half: read substep 1 of stage kt, multiply substep 0
-    load_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
+    load_frags(kt, 1, fa1, fb1, xa1, xb1);
+    mfmas(fa0, fb0, xa0, xb0);
+    if constexpr (MX) {
+      // keep these products in the first half: without a use here the
+      // compiler sinks them past the barrier (they only feed later ones)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
     wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
     stage_barrier();
     // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
     if (kt + 2 < KT) issue(kt + 2);
-    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0);
-    mfmas(fa1, fb1);
+    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
+    mfmas(fa1, fb1, xa1, xb1);
   }
 
   if constexpr (SPLIT) {
@@ -400,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   // 8 (r / 4) + 4 (lane / 32) + r % 4; swapping one value with the neighbour
   // lane (DPP quad_perm 1,0,3,2) gives the even lane columns (c, c+1) of row
   // r and the odd lane the same columns of row r+1.
-  const float f = sa[0] * sb[0];
+  const float f = MX ? 1.0f : sa[0] * sb[0];
   const bool odd = lane & 1;
   const int colp = (lane & 31) & ~1;
 #pragma unroll
@@ -427,6 +497,24 @@ static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
   hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
                      dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
+}
+
+template <int FA, int FB, int TN>
+static int launch_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
+                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
+                     (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea, eb);
+  return check_launch("fp8_gemm_mx");
+}
+
+template <int FA, int FB>
+static int launch_mx_tile(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
+                          const uint8_t* eb, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                          hipStream_t stream) {
+  // no 256-wide tile here: with the exponent registers it would spill
+  if (N % 192 == 0) return launch_mx<FA, FB, 3>(a, ea, b, eb, M, N, K, y, stream);
+  return launch_mx<FA, FB, 2>(a, ea, b, eb, M, N, K, y, stream);
 }
 
 // y[m, n] = bf16_rne((sum over s in order of ws[s][m][n]) * sa[0] * sb[0]):
@@ -598,4 +686,39 @@ extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const u
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
     return launch_split_tile<1, 0>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
   return launch_split_tile<1, 1>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
+}
+
+extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale,
+                           const uint8_t* b, fp8dp_format fb, const uint8_t* b_scale, int64_t M,
+                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  if (a == nullptr || b == nullptr || y == nullptr || a_scale == nullptr || b_scale == nullptr) {
+    set_error("fp8_gemm_mx: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
+    set_error("fp8_gemm_mx: M must be a positive multiple of 256, N and K of 128 (got %lld, "
+              "%lld, %lld)", (long long)M, (long long)N, (long long)K);
+    return FP8DP_EINVAL;
+  }
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
+      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
+    set_error("fp8_gemm_mx: shape too large");
+    return FP8DP_EINVAL;
+  }
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
+    set_error("fp8_gemm_mx: unknown format");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(a_scale) & 3u) || (reinterpret_cast<uintptr_t>(b_scale) & 3u)) {
+    set_error("fp8_gemm_mx: operands must be 16-byte aligned, block exponents 4-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
+    return launch_mx_tile<0, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
+    return launch_mx_tile<0, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
+  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
+    return launch_mx_tile<1, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
+  return launch_mx_tile<1, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
 }

@@ -4,6 +4,8 @@
 // large-tile loop.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <stdint.h>
 
 namespace fp8dp {
@@ -52,8 +54,24 @@ __device__ __forceinline__ int tile_of_pass(int b, int p, int G, int ntiles) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
+// indices, for instruction operands that must be constants).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+}
+
+// The 4-byte form: lane i's dword lands at l + 4 i.
+__device__ __forceinline__ void copy4_to_lds(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
 }
 
 

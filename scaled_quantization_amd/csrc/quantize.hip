@@ -149,6 +149,68 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
   if constexpr (ACC) block_fold<kThreads>(amax16, sat, slots);
 }
 
+// ------------------------------------------------------------------ MXFP8
+// "FP8 training: what it is and how it works", Trade-offs and edge cases: the
+// microscaling recipe scales each block of 32 adjacent values by its own
+// power of two.  Block exponent k (decode scale 2^k, stored as the E8M0 byte
+// k + 127): the smallest k in [-127, 127] with |b| <= max * 2^k for every
+// element of the block.  From the block's largest BF16 magnitude pattern m
+// (sign cleared; NaN patterns order above infinity): for a normal m = 1.f 2^e
+// and max = 1.75 * 2^emax, k = e - emax, plus one when the fraction exceeds
+// 0.75 (7-bit field above 0x60); zero and subnormal BF16 values lie below
+// max * 2^-127 (k = -127); infinity and NaN admit no k (k = 127).
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(uint32_t m) {
+  constexpr int emax = FMT == 0 ? 8 : 15;
+  const int ef = (int)(m >> 7);
+  if (ef >= 0xFF) return 127;
+  if (ef == 0) return -127;
+  const int k = ef - 127 - emax + ((m & 0x7Fu) > 0x60u ? 1 : 0);
+  return k < -127 ? -127 : k;
+}
+
+// 2^-k in binary32 (k = 127 gives the subnormal 2^-127).
+__device__ __forceinline__ float mx_multiplier(int k) {
+  return __uint_as_float(k == 127 ? 0x00400000u : (uint32_t)(127 - k) << 23);
+}
+
+// Each block of 32 is 4 vectors of 8, held by the 4 lanes of a DPP quad (the
+// grid stride is a multiple of 4 and n8 % 4 == 0, so a quad is active or
+// inactive as a whole); two quad swaps give every lane the block maximum, and
+// the quad's first lane writes the exponent byte.
+template <int FMT, int ACT, bool WBF16, bool HW>
+__global__ __launch_bounds__(kThreads) void k_quant_mx(const uint4* __restrict__ h,
+                                                       uint4* __restrict__ bout,
+                                                       uint2* __restrict__ qout,
+                                                       uint8_t* __restrict__ e8, int64_t n8) {
+  uint32_t sat = 0;   // nothing finite saturates under this rule; the count is unused
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto one = [&](const uint4& x, int64_t i) {
+    uint32_t b[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = act_pair<ACT, HW>(b[j]);
+    if constexpr (WBF16) store_nt(bout + i, b[0], b[1], b[2], b[3]);
+    const uint32_t mx = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b);
+    uint32_t bm = mx;
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bm, 0xB1, 0xF, 0xF, false);
+    bm = o > bm ? o : bm;
+    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bm, 0x4E, 0xF, 0xF, false);
+    bm = o > bm ? o : bm;
+    const int k = mx_exponent<FMT>(bm);
+    if ((threadIdx.x & 3) == 0) e8[i >> 2] = (uint8_t)(k + 127);
+    store_nt(qout + i, cast8<FMT, HW>(b, mx, mx_multiplier(k), sat));
+  };
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
+    uint4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = load_nt(h + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) one(x[u], i + u * stride);
+  }
+  for (; i < n8; i += stride) one(load_nt(h + i), i);
+}
+
 // ------------------------------------------------------------------ state
 __global__ void k_state_init(fp8dp_tensor_state* st, int fmt, int hist_len, float margin,
                              float initial_amax) {
@@ -439,6 +501,29 @@ static int dispatch_group(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t*
   return FP8DP_EINVAL;
 }
 
+template <int FMT, int ACT, bool WBF16>
+static int launch_mx_quant(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout,
+                           uint8_t* e8, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  const unsigned grid = grid_for(n8, kThreads, kBlocksPerCU);
+  if (codec() == 0)
+    hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
+                       reinterpret_cast<uint2*>(qout), e8, n8);
+  else
+    hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
+                       reinterpret_cast<uint2*>(qout), e8, n8);
+  return check_launch("quantize_mx");
+}
+
+template <int FMT, int ACT>
+static int dispatch_mx(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout, uint8_t* e8,
+                       hipStream_t stream) {
+  return bout ? launch_mx_quant<FMT, ACT, true>(h, n, bout, qout, e8, stream)
+              : launch_mx_quant<FMT, ACT, false>(h, n, bout, qout, e8, stream);
+}
+
 static bool valid_fmt(int f) { return f == FP8DP_E4M3 || f == FP8DP_E5M2; }
 static bool valid_act(int a) { return a == FP8DP_ACT_IDENTITY || a == FP8DP_ACT_RELU2; }
 
@@ -656,4 +741,32 @@ extern "C" int fp8dp_scale_rule(const float* amax, int64_t n, float margin, fp8d
   hipLaunchKernelGGL(k_scale_rule, dim3(grid), dim3(256), 0, stream, amax, n, margin,
                      fmt == FP8DP_E4M3 ? 448.0f : 57344.0f, scale, scale_inv);
   return check_launch("fp8dp_scale_rule");
+}
+
+extern "C" int quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                           fp8dp_format fmt, uint16_t* bf16_out, uint8_t* fp8_out,
+                           uint8_t* scale_out, hipStream_t stream) {
+  if (h == nullptr || fp8_out == nullptr || scale_out == nullptr) {
+    set_error("quantize_mx: NULL input, code or exponent pointer");
+    return FP8DP_EINVAL;
+  }
+  if (rows < 1 || cols < 32 || cols % 32 != 0) {
+    set_error("quantize_mx: need rows >= 1 and cols a positive multiple of 32 (got %lld, %lld)",
+              (long long)rows, (long long)cols);
+    return FP8DP_EINVAL;
+  }
+  if (!valid_fmt(fmt) || !valid_act(act)) {
+    set_error("quantize_mx: unknown format %d or activation %d", (int)fmt, (int)act);
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(h) || !aligned16(bf16_out) || !aligned16(fp8_out)) {
+    set_error("quantize_mx: input, copy and code pointers must be 16-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  const int64_t n = rows * cols;
+  if (fmt == FP8DP_E4M3)
+    return act == FP8DP_ACT_RELU2 ? dispatch_mx<0, 1>(h, n, bf16_out, fp8_out, scale_out, stream)
+                                  : dispatch_mx<0, 0>(h, n, bf16_out, fp8_out, scale_out, stream);
+  return act == FP8DP_ACT_RELU2 ? dispatch_mx<1, 1>(h, n, bf16_out, fp8_out, scale_out, stream)
+                                : dispatch_mx<1, 0>(h, n, bf16_out, fp8_out, scale_out, stream);
 }

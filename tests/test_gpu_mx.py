@@ -1,0 +1,243 @@
+"""MXFP8 cast and MXFP8 GEMM against the oracle (GPU).
+
+"FP8 training: what it is and how it works", Trade-offs and edge cases: the
+microscaling recipe gives each block of 32 adjacent values its own
+power-of-two scale.  quantize_mx is compared bit for bit with oracle
+quantize_mx (BF16 copy, codes, E8M0 block exponents); fp8_gemm_mx with the
+oracle's float64 MX GEMM to |y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| plus the
+FP8 instructions' truncation allowance, the fraction outside the plain bound
+capped.  Workloads: the seeded synthetic tensors of workloads.py (the GPT-2
+MLP activation and down-projection weight at full size), block magnitudes
+spread over many binades, and special blocks (zero, signed zero, subnormal,
+infinity, NaN).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import scaled_quantization_amd as sq
+import workloads
+from gpu_util import (DEV, THREADS, bf16_np, fp8_mfma_allowance_mx, to_dev_bf16, to_dev_u8,
+                      u8_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=[0, 1], ids=["hw", "int"])
+def codec(request):
+    prev = sq.fp8dp_set_codec(request.param)
+    yield request.param
+    sq.fp8dp_set_codec(prev)
+
+
+def _spread(rng, rows, cols, lo=-30, hi=30):
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(lo, hi, (rows, cols // 32, 1)).astype(np.float32)).repeat(
+        32, axis=2).reshape(rows, cols)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _run_mx(h_np, act, fmt, want_bf16=True):
+    rows, cols = h_np.shape
+    h = to_dev_bf16(h_np)
+    b = torch.empty_like(h) if want_bf16 else None
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    e = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    sq.quantize_mx(h, act, fmt, q, e, b)
+    return b, q, e
+
+
+def _oracle_mx(h, act, fmt, want_bf16=True):
+    """oracle quantize_mx over row ranges in parallel (rows are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = h.shape[0]
+    if rows < 64:
+        return O.quantize_mx(h, act, fmt, want_bf16)
+    step = (rows + 4 * THREADS - 1) // (4 * THREADS)
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda r0: O.quantize_mx(h[r0:r0 + step], act, fmt, want_bf16),
+                            range(0, rows, step)))
+    return O.MXResult(np.concatenate([p.bf16 for p in parts]) if want_bf16 else None,
+                      np.concatenate([p.fp8 for p in parts]),
+                      np.concatenate([p.scale for p in parts]))
+
+
+# ------------------------------------------------------------------ cast
+@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("act", [0, 1], ids=["identity", "relu2"])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (17, 4128), (257, 768)])
+def test_quantize_mx_vs_oracle(rows, cols, act, fmt, codec):
+    rng = np.random.default_rng(rows * 7 + cols + act + 2 * fmt)
+    h = _spread(rng, rows, cols)
+    b, q, e = _run_mx(h, act, fmt)
+    r = O.quantize_mx(h, act, fmt)
+    assert np.array_equal(bf16_np(b), r.bf16)
+    assert np.array_equal(u8_np(e), r.scale)
+    assert np.array_equal(u8_np(q), r.fp8)
+
+
+def test_quantize_mx_without_copy():
+    rng = np.random.default_rng(3)
+    h = _spread(rng, 64, 512)
+    _, q, e = _run_mx(h, sq.ACT_RELU2, sq.E4M3, want_bf16=False)
+    r = O.quantize_mx(h, O.ACT_RELU2, O.E4M3, want_bf16=False)
+    assert np.array_equal(u8_np(q), r.fp8) and np.array_equal(u8_np(e), r.scale)
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+def test_quantize_mx_special_blocks(fmt, codec):
+    rng = np.random.default_rng(9)
+    h = _spread(rng, 4, 256)
+    h[0, 0:32] = 0                        # zero block
+    h[0, 32:64] = 0x8000                  # negative zeros
+    h[0, 64:96] = rng.integers(1, 0x80, 32)   # BF16 subnormals only
+    h[1, 0] = 0x7F80                      # +inf with finite neighbours
+    h[1, 33] = 0xFF80                     # -inf
+    h[1, 64] = 0x7FC1                     # NaN
+    h[1, 97] = 0xFFC0                     # -NaN
+    h[2, 128:160] = 0x7F7F                # largest finite BF16 everywhere
+    h[3, 5] = 0x0001                      # smallest subnormal among normal values
+    for act in (0, 1):
+        b, q, e = _run_mx(h, act, fmt)
+        r = O.quantize_mx(h, act, fmt)
+        assert np.array_equal(bf16_np(b), r.bf16)
+        assert np.array_equal(u8_np(e), r.scale)
+        assert np.array_equal(u8_np(q), r.fp8)
+
+
+def test_quantize_mx_every_exponent_boundary():
+    """Block maxima at and around max * 2^k for every k the BF16 range reaches."""
+    rows = []
+    for fmt in (0, 1):
+        for k in range(-133, 121):
+            for frac in (0x5F, 0x60, 0x61, 0x7F, 0x00):
+                ef = k + 127 + (8 if fmt == 0 else 15)
+                if 1 <= ef <= 254:
+                    blk = np.full(32, 0x3F80, np.uint16)
+                    blk[7] = (ef << 7) | frac
+                    rows.append(blk)
+    h = np.stack(rows)
+    for fmt in (0, 1):
+        _, q, e = _run_mx(h, 0, fmt, want_bf16=False)
+        r = O.quantize_mx(h, 0, fmt, want_bf16=False)
+        assert np.array_equal(u8_np(e), r.scale)
+        assert np.array_equal(u8_np(q), r.fp8)
+
+
+def test_quantize_mx_gpt2_activation_full_size():
+    w = workloads.get("gpt2")
+    h = w.h0()
+    b, q, e = _run_mx(h, sq.ACT_RELU2, sq.E4M3)
+    r = _oracle_mx(h, O.ACT_RELU2, O.E4M3)
+    assert np.array_equal(u8_np(e), r.scale)
+    assert np.array_equal(u8_np(q), r.fp8)
+    assert np.array_equal(bf16_np(b), r.bf16)
+
+
+def test_quantize_mx_errors():
+    h = torch.zeros((4, 48), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((4, 48), dtype=torch.uint8, device=DEV)
+    e = torch.empty((4, 2), dtype=torch.uint8, device=DEV)
+    # cols not a multiple of 32
+    assert sq.lib().quantize_mx(h.data_ptr(), 4, 48, 0, 0, None, q.data_ptr(), e.data_ptr(),
+                                None) == -1
+    # missing exponent output, unknown format
+    assert sq.lib().quantize_mx(h.data_ptr(), 4, 32, 0, 0, None, q.data_ptr(), None, None) == -1
+    assert sq.lib().quantize_mx(h.data_ptr(), 4, 32, 0, 7, None, q.data_ptr(), e.data_ptr(),
+                                None) == -1
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ GEMM
+def _check(y, ref, absref, allow, what, cap=1e-3):
+    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
+    err = np.abs(np.asarray(y, np.float64) - ref)
+    bad = err > bound + allow
+    assert not bad.any(), f"{what}: {int(bad.sum())} outside bound + allowance"
+    assert (err > bound).mean() <= cap, f"{what}: {(err > bound).mean():.2e} outside the plain bound"
+
+
+def _gemm_case(rng, M, N, K, fa, fb, lo=-12, hi=12):
+    ha = _spread(rng, M, K, lo, hi)
+    hb = _spread(rng, N, K, lo, hi)
+    ra = O.quantize_mx(ha, O.ACT_IDENTITY, fa, want_bf16=False)
+    rb = O.quantize_mx(hb, O.ACT_IDENTITY, fb, want_bf16=False)
+    return ra.fp8, ra.scale, rb.fp8, rb.scale
+
+
+def _gemm_mx_dev(a8, fa, ea, b8, fb, eb):
+    M, N = a8.shape[0], b8.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_mx(to_dev_u8(a8), fa, to_dev_u8(ea), to_dev_u8(b8), fb, to_dev_u8(eb), y)
+    return y.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", [(256, 128, 128, 0, 0), (256, 384, 1024, 0, 0),
+                                         (512, 512, 512, 1, 0), (256, 640, 256, 0, 1),
+                                         (768, 768, 3072, 0, 0), (256, 256, 384, 1, 1)])
+def test_gemm_mx_vs_oracle(M, N, K, fa, fb):
+    rng = np.random.default_rng(M + 3 * N + 7 * K + fa + 2 * fb)
+    a8, ea, b8, eb = _gemm_case(rng, M, N, K, fa, fb)
+    y = _gemm_mx_dev(a8, fa, ea, b8, fb, eb)
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 24)), [M - 1]]))
+    ref, absref = O.gemm_mx_f64(a8, fa, ea, b8, fb, eb, rows)
+    allow = fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, rows)
+    _check(y[rows], ref, absref, allow, f"{M}x{N}x{K}")
+
+
+def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
+    """Exponent bytes 127 + i (A) and 127 + j (B) everywhere equal per-tensor
+    scales 2^i, 2^j: the MX GEMM then matches fp8_gemm_scaled bit for bit."""
+    rng = np.random.default_rng(5)
+    M, N, K = 512, 768, 1024
+    t = O.fp8_decode_table(0)
+    ok = np.flatnonzero(np.isfinite(t) & (np.abs(t) <= 16))
+    a8 = rng.choice(ok, size=(M, K)).astype(np.uint8)
+    b8 = rng.choice(ok, size=(N, K)).astype(np.uint8)
+    for i, j in ((0, 0), (3, -5)):
+        ea = np.full((M, K // 32), 127 + i, np.uint8)
+        eb = np.full((N, K // 32), 127 + j, np.uint8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y)
+        y2 = torch.empty_like(y)
+        sa = torch.tensor([2.0 ** i], dtype=torch.float32, device=DEV)
+        sb = torch.tensor([2.0 ** j], dtype=torch.float32, device=DEV)
+        sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(b8), 0, sq.PER_TENSOR, sa, sb, y2)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (i, j)
+
+
+def test_gemm_mx_gpt2_down_projection():
+    """The GPT-2 down-projection in MXFP8: H = relu2(H0) and W cast by
+    quantize_mx on the GPU, checked byte for byte against the oracle's cast,
+    then the GEMM on sampled rows against the oracle."""
+    w = workloads.get("gpt2")
+    h = w.h0()
+    wt = w.weight()                          # [768, 3072]
+    _, qa, ea = _run_mx(h, sq.ACT_RELU2, sq.E4M3, want_bf16=False)
+    _, qb, eb = _run_mx(wt, sq.ACT_IDENTITY, sq.E4M3, want_bf16=False)
+    rng = np.random.default_rng(17)
+    rows = np.sort(rng.choice(h.shape[0], size=24, replace=False))
+    ra = O.quantize_mx(h[rows], O.ACT_RELU2, O.E4M3, want_bf16=False)
+    rb = O.quantize_mx(wt, O.ACT_IDENTITY, O.E4M3, want_bf16=False)
+    assert np.array_equal(u8_np(qa)[rows], ra.fp8) and np.array_equal(u8_np(ea)[rows], ra.scale)
+    assert np.array_equal(u8_np(qb), rb.fp8) and np.array_equal(u8_np(eb), rb.scale)
+    M, N = h.shape[0], wt.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_mx(qa, sq.E4M3, ea, qb, sq.E4M3, eb, y)
+    ref, absref = O.gemm_mx_f64(ra.fp8, O.E4M3, ra.scale, rb.fp8, O.E4M3, rb.scale)
+    allow = fp8_mfma_allowance_mx(ra.fp8, 0, ra.scale, rb.fp8, 0, rb.scale, np.arange(24))
+    _check(y.float().cpu().numpy()[rows], ref, absref, allow, "gpt2 mx")
+
+
+def test_gemm_mx_errors():
+    a = torch.zeros((256, 128), dtype=torch.uint8, device=DEV)
+    e = torch.zeros((256, 4), dtype=torch.uint8, device=DEV)
+    y = torch.empty((256, 256), dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros((256, 128), dtype=torch.uint8, device=DEV)
+    rc = sq.lib().fp8_gemm_mx(a.data_ptr(), 0, e.data_ptr(), b.data_ptr(), 0, e.data_ptr(),
+                              128, 256, 128, y.data_ptr(), None)
+    assert rc == -1
+    rc = sq.lib().fp8_gemm_mx(a.data_ptr(), 0, e.data_ptr(), b.data_ptr(), 0, e.data_ptr() + 1,
+                              256, 256, 128, y.data_ptr(), None)
+    assert rc == -1
