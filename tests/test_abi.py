@@ -32,7 +32,7 @@ def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
-              "fp8_transpose", "fp8dp_last_error"):
+              "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "fp8dp_last_error"):
         assert n in names
 
 
@@ -122,3 +122,20 @@ def test_binding_refuses_host_tensors(L):
     with pytest.raises(sq.Fp8dpError):
         sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, None, None, None, None,
                           stream=0)
+
+
+def test_mx_argument_checks_reject_without_launching(L):
+    rc = L.quantize_mx(16, 4, 48, 0, 0, None, 16, 16, None)
+    assert rc == -1 and b"32" in L.fp8dp_last_error()
+    rc = L.quantize_mx(16, 4, 64, 0, 0, None, 16, None, None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+    rc = L.quantize_mx(16, 4, 64, 0, 9, None, 16, 16, None)
+    assert rc == -1 and b"format" in L.fp8dp_last_error()
+    rc = L.quantize_mx(24, 4, 64, 0, 0, None, 16, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_mx(16, 0, 16, 16, 0, 16, 128, 128, 128, 16, None)
+    assert rc == -1 and b"256" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_mx(16, 0, 18, 16, 0, 16, 256, 128, 128, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_mx(16, 3, 16, 16, 0, 16, 256, 128, 128, 16, None)
+    assert rc == -1 and b"format" in L.fp8dp_last_error()
