@@ -215,6 +215,8 @@ def main():
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
     out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
+    out["recompute_on_overflow"] = recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args,
+                                             total_ms / args.steps)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -417,6 +419,42 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
             "fp8_gemm_mx": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
+
+
+def recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args, step_ms):
+    """Cost of the overflow-triggered recompute: quantize_recompute and
+    fp8_gemm_scaled_if enqueued after the state update of every step.  The
+    step's own state has not overflowed (idle: every workgroup reads the
+    flag and returns); a second state initialised with a tiny amax has (the
+    re-cast and the GEMM run in full)."""
+    stream = torch.cuda.current_stream()
+    h = H[0]
+    st_hot = sq.TensorState(sq.E4M3, 1, w.margin, 1e-3, device=dev)
+    sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_hot, None, A8[1])
+    sq.amax_history_update(st_hot)
+
+    def pair(st, a8):
+        sq.quantize_recompute(h, sq.ACT_RELU2, sq.E4M3, st, a8)
+        sq.fp8_gemm_scaled_if(a8, sq.E4M3, w8, sq.E4M3, st.field_ptr("scale_inv"), wsc, Y,
+                              st.field_ptr("overflow"))
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    idle = timed(lambda: pair(st_a, A8[0]))
+    hot = timed(lambda: pair(st_hot, A8[1]))
+    flags = (st_a.read()["overflow"], st_hot.read()["overflow"])
+    return {"idle_ms": round(idle, 5), "idle_frac_of_step": round(idle / step_ms, 4),
+            "triggered_ms": round(hot, 5), "overflow_flags_idle_hot": list(flags)}
 
 
 def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):

@@ -209,6 +209,35 @@ int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, 
 int fp8_transpose(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                   hipStream_t stream);
 
+/* Recompute after an overflow ("FP8 Training & Inference", Delayed Scaling:
+ * a step whose delayed scale was too large is detected and recomputed with a
+ * corrected scale).  Enqueue after amax_history_update of the step: when that
+ * update set st->overflow, fp8_out = sat_rne(b * st->scale) for every element
+ * (b = bf16_rne(act(h)), st->scale now computed from a history that includes
+ * the step's own amax); when it did not, the kernel returns at once and
+ * fp8_out is untouched.  The decision is taken on the GPU (no host round
+ * trip).  The BF16 copy is not rewritten (it does not depend on the scale),
+ * and nothing is folded into st.  Same shapes and alignment as
+ * quantize_fused in PER_TENSOR mode.
+ * Errors: EINVAL for NULL h / st / fp8_out, rows or cols < 1, misaligned
+ * pointers, or an unknown act / fmt. */
+int quantize_recompute(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                       fp8dp_format fmt, const fp8dp_tensor_state* st, uint8_t* fp8_out,
+                       hipStream_t stream);
+
+/* fp8_gemm_scaled (PER_TENSOR, ACCUM_MFMA_FP8) that runs only when
+ * *run_flag != 0, read on the GPU -- the GEMM half of the recompute above:
+ * pass &st->overflow of the operand whose cast overflowed and
+ * &st->scale_inv (the corrected scale's inverse).  With *run_flag == 0 y is
+ * untouched.
+ * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
+ * not of 128, misaligned pointers (operands 16 bytes, scales and flag 4), or
+ * a bad format. */
+int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
+                       int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
+                       const float* b_scale_inv, uint16_t* y, const uint32_t* run_flag,
+                       hipStream_t stream);
+
 /* MXFP8 cast ("FP8 training ...", Trade-offs and edge cases: the
  * microscaling recipe gives each block of 32 adjacent values its own scale,
  * a power of two).  h [rows x cols] BF16 (cols % 32 == 0); block j of a row

@@ -49,6 +49,9 @@ _SIGS = {
     "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
                                 _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "quantize_recompute": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+                           ctypes.c_int),
     "quantize_mx": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_mx": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -121,7 +124,7 @@ def _p(t: Ptr) -> Optional[int]:
 # Field offsets of fp8dp_tensor_state (include/fp8dp.h).
 _HDR = struct.Struct("<fffIQffiiIi16f")          # 112 bytes of header fields
 _SLOT = struct.Struct("<IIQ48x")                 # 64-byte accumulator slot
-_OFF = {"scale": 0, "scale_inv": 4, "scale_inv_used": 8, "acc": 192}
+_OFF = {"scale": 0, "scale_inv": 4, "scale_inv_used": 8, "overflow": 12, "acc": 192}
 
 
 class TensorState:
@@ -224,6 +227,27 @@ def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if tuple(dst.shape) != (cols, rows):
         raise Fp8dpError("fp8_transpose: shape mismatch")
     _check(lib().fp8_transpose(_p(src), rows, cols, _p(dst), _stream(stream)), "fp8_transpose")
+
+
+def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.Tensor,
+                       stream=None) -> None:
+    """Re-cast h with st's corrected scale when st's last update flagged an overflow
+    (decided on the GPU; otherwise nothing is written)."""
+    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    _check(lib().quantize_recompute(_p(h), rows, cols, act, fmt, _state_ptr(st), _p(fp8_out),
+                                    _stream(stream)), "quantize_recompute")
+
+
+def fp8_gemm_scaled_if(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, a_scale_inv: Ptr,
+                       b_scale_inv: Ptr, y: torch.Tensor, run_flag: Ptr, stream=None) -> None:
+    """Per-tensor FP8 GEMM that runs only when the device word *run_flag is nonzero."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(y.shape) != (M, N):
+        raise Fp8dpError("fp8_gemm_scaled_if: shape mismatch")
+    _check(lib().fp8_gemm_scaled_if(_p(a), fa, _p(b), fb, M, N, K, _p(a_scale_inv),
+                                    _p(b_scale_inv), _p(y), _p(run_flag), _stream(stream)),
+           "fp8_gemm_scaled_if")
 
 
 def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,

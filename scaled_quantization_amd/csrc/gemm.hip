@@ -275,7 +275,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // (lane / 32 selects the half), which is exactly one block: the MFMA applies
 // 2^(ea - 127) 2^(eb - 127) to each block's products, and the epilogue has
 // no scale to apply.
-template <int FA, int FB, int TN, bool SPLIT, bool MX = false>
+// COND: the launch does nothing unless *run_flag != 0 (a device-side flag,
+// e.g. the overflow mark of a scaling state), read once by every workgroup.
+template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
@@ -283,8 +285,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
                                                      uint16_t* __restrict__ Y,
                                                      float* __restrict__ ws, int splits,
                                                      const uint8_t* __restrict__ ea = nullptr,
-                                                     const uint8_t* __restrict__ eb = nullptr) {
+                                                     const uint8_t* __restrict__ eb = nullptr,
+                                                     const uint32_t* __restrict__ run_flag = nullptr) {
   static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
+  if constexpr (COND) {
+    if (*run_flag == 0) return;
+  }
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
   constexpr int SLOT = TILES + (MX ? 2048 : 0);             // + 256 A and 256 B exponent dwords
@@ -497,6 +503,25 @@ static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
   hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
                      dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
+}
+
+template <int FA, int FB, int TN>
+static int launch_cond(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                       const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, true>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
+                     (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1, nullptr, nullptr, flag);
+  return check_launch("fp8_gemm_scaled_if");
+}
+
+template <int FA, int FB>
+static int launch_cond_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
+                            hipStream_t stream) {
+  if (N % 192 == 0) return launch_cond<FA, FB, 3>(a, b, M, N, K, sa, sb, y, flag, stream);
+  if (N % 256 == 0) return launch_cond<FA, FB, 4>(a, b, M, N, K, sa, sb, y, flag, stream);
+  return launch_cond<FA, FB, 2>(a, b, M, N, K, sa, sb, y, flag, stream);
 }
 
 template <int FA, int FB, int TN>
@@ -721,4 +746,44 @@ extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_s
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
     return launch_mx_tile<1, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
   return launch_mx_tile<1, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
+}
+
+extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                                  fp8dp_format fb, int64_t M, int64_t N, int64_t K,
+                                  const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
+                                  const uint32_t* run_flag, hipStream_t stream) {
+  if (a == nullptr || b == nullptr || y == nullptr || a_scale_inv == nullptr ||
+      b_scale_inv == nullptr || run_flag == nullptr) {
+    set_error("fp8_gemm_scaled_if: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
+    set_error("fp8_gemm_scaled_if: M must be a positive multiple of 256, N and K of 128 (got "
+              "%lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
+    return FP8DP_EINVAL;
+  }
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
+      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
+    set_error("fp8_gemm_scaled_if: shape too large");
+    return FP8DP_EINVAL;
+  }
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
+    set_error("fp8_gemm_scaled_if: unknown format");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(run_flag) & 3u)) {
+    set_error("fp8_gemm_scaled_if: operands must be 16-byte aligned, scales and flag 4-byte "
+              "aligned");
+    return FP8DP_EINVAL;
+  }
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
+    return launch_cond_tile<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
+    return launch_cond_tile<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
+    return launch_cond_tile<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+  return launch_cond_tile<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
 }

@@ -149,6 +149,42 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
   if constexpr (ACC) block_fold<kThreads>(amax16, sat, slots);
 }
 
+// ------------------------------------------------------------------ recompute on overflow
+// "FP8 Training & Inference", Delayed Scaling: when the delayed scale was too
+// large the step is detected and recomputed with a corrected scale.  Launched
+// after amax_history_update: if that update flagged the step (overflow != 0)
+// every element is cast again with the state's new scale (which includes the
+// step's own amax); otherwise every block returns at once.  The BF16 copy
+// does not depend on the scale and is not rewritten; nothing is folded into
+// the accumulators (the step's amax is already in the history).
+template <int FMT, int ACT, bool HW>
+__global__ __launch_bounds__(kThreads) void k_quant_recast(const uint4* __restrict__ h,
+                                                           uint2* __restrict__ qout, int64_t n8,
+                                                           int tail,
+                                                           const fp8dp_tensor_state* __restrict__ st) {
+  if (st->overflow == 0) return;
+  const float s = st->scale;
+  uint32_t sat = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
+    const uint4 x = load_nt(h + i);
+    uint32_t b[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = act_pair<ACT, HW>(b[j]);
+    store_nt(qout + i, cast8<FMT, HW>(b, vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(b), s, sat));
+  }
+  if (tail && blockIdx.x == 0 && threadIdx.x == 0) {
+    const uint16_t* ht = reinterpret_cast<const uint16_t*>(h + n8);
+    for (int t = 0; t < tail; ++t) {
+      uint16_t bb;
+      uint8_t q;
+      uint32_t a16 = 0;
+      quant_one<FMT, ACT>(ht[t], s, bb, q, a16, sat);
+      reinterpret_cast<uint8_t*>(qout + n8)[t] = q;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ MXFP8
 // "FP8 training: what it is and how it works", Trade-offs and edge cases: the
 // microscaling recipe scales each block of 32 adjacent values by its own
@@ -524,6 +560,23 @@ static int dispatch_mx(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qo
               : launch_mx_quant<FMT, ACT, false>(h, n, bout, qout, e8, stream);
 }
 
+template <int FMT, int ACT>
+static int launch_recast(const uint16_t* h, int64_t n, uint8_t* qout,
+                         const fp8dp_tensor_state* st, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  const int tail = (int)(n % 8);
+  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, kBlocksPerCU);
+  if (codec() == 0)
+    hipLaunchKernelGGL((k_quant_recast<FMT, ACT, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(h), reinterpret_cast<uint2*>(qout), n8,
+                       tail, st);
+  else
+    hipLaunchKernelGGL((k_quant_recast<FMT, ACT, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(h), reinterpret_cast<uint2*>(qout), n8,
+                       tail, st);
+  return check_launch("quantize_recompute");
+}
+
 static bool valid_fmt(int f) { return f == FP8DP_E4M3 || f == FP8DP_E5M2; }
 static bool valid_act(int a) { return a == FP8DP_ACT_IDENTITY || a == FP8DP_ACT_RELU2; }
 
@@ -769,4 +822,27 @@ extern "C" int quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_
                                   : dispatch_mx<0, 0>(h, n, bf16_out, fp8_out, scale_out, stream);
   return act == FP8DP_ACT_RELU2 ? dispatch_mx<1, 1>(h, n, bf16_out, fp8_out, scale_out, stream)
                                 : dispatch_mx<1, 0>(h, n, bf16_out, fp8_out, scale_out, stream);
+}
+
+extern "C" int quantize_recompute(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                                  fp8dp_format fmt, const fp8dp_tensor_state* st,
+                                  uint8_t* fp8_out, hipStream_t stream) {
+  if (h == nullptr || st == nullptr || fp8_out == nullptr || rows < 1 || cols < 1) {
+    set_error("quantize_recompute: need non-NULL h, st, fp8_out and rows, cols >= 1");
+    return FP8DP_EINVAL;
+  }
+  if (!valid_fmt(fmt) || !valid_act(act)) {
+    set_error("quantize_recompute: unknown format %d or activation %d", (int)fmt, (int)act);
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(h) || !aligned16(fp8_out) || !aligned16(st)) {
+    set_error("quantize_recompute: tensor and state pointers must be 16-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  const int64_t n = rows * cols;
+  if (fmt == FP8DP_E4M3)
+    return act == FP8DP_ACT_RELU2 ? launch_recast<0, 1>(h, n, fp8_out, st, stream)
+                                  : launch_recast<0, 0>(h, n, fp8_out, st, stream);
+  return act == FP8DP_ACT_RELU2 ? launch_recast<1, 1>(h, n, fp8_out, st, stream)
+                                : launch_recast<1, 0>(h, n, fp8_out, st, stream);
 }

@@ -32,7 +32,8 @@ def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
-              "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "fp8dp_last_error"):
+              "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
+              "fp8_gemm_scaled_if", "fp8dp_last_error"):
         assert n in names
 
 
@@ -139,3 +140,16 @@ def test_mx_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.fp8_gemm_mx(16, 3, 16, 16, 0, 16, 256, 128, 128, 16, None)
     assert rc == -1 and b"format" in L.fp8dp_last_error()
+
+
+def test_recompute_argument_checks_reject_without_launching(L):
+    rc = L.quantize_recompute(16, 4, 8, 0, 0, None, 16, None)
+    assert rc == -1 and b"non-NULL" in L.fp8dp_last_error()
+    rc = L.quantize_recompute(16, 4, 8, 0, 0, 24, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, None, None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 128, 128, 128, 16, 16, 16, 16, None)
+    assert rc == -1 and b"256" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 18, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
