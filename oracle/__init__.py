@@ -38,6 +38,9 @@ PINNED = {
     "state/history": "closed-form delayed recurrence on the tiny workload",
     "quantize_weight_blocks": "brute force composition per block (numpy + nearest-code search)",
     "gemm_f64": "exact rational arithmetic (fractions) on small cases; identity and constant cases",
+    "relu2_backward": "chain rule against torch autograd of relu(h)^2 in float64 within the "
+                      "formats' error bound (BF16 and FP8 caches); exact squares; signed zeros; "
+                      "E5M2 codes by nearest-code search; amax and saturation by numpy/torch",
     "mx_exponent": "closed form from the BF16 exponent and fraction bits at every BF16 magnitude; "
                    "minimality and no-overflow invariants",
     "quantize_mx": "nearest-code search over the decode table of b / 2^k with an independently "
@@ -125,6 +128,9 @@ def lib() -> ctypes.CDLL:
                                                 _u8p, _f32p, _f32p]
     L.oracle_fp8_encode_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, _u8p]
     L.oracle_bf16_rne_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _u16p]
+    L.oracle_relu2_backward.argtypes = [_u16p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_float, _u16p, _u8p,
+                                        _u32p, _u64p]
     L.oracle_mx_exponent.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int]
     L.oracle_mx_exponent.restype = ctypes.c_int
     L.oracle_quantize_mx.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -259,6 +265,34 @@ def quantize_weight_tensor(w: np.ndarray, fmt: int):
     s, si = scale_from_amax(amax, 1.0, fmt)
     r = quantize(w, ACT_IDENTITY, fmt, PER_TENSOR, float(s[0]), want_bf16=False)
     return r.fp8, float(s[0]), float(si[0])
+
+
+# --------------------------------------------------------------------------- activation backward
+CACHE_BF16 = 2
+
+
+def relu2_backward(dA: np.ndarray, cache: np.ndarray, cache_kind: int, a_scale_inv: float,
+                   fmt: int, scale: float) -> QuantResult:
+    """dH = bf16(dA * 2 sqrt(a)) from the cached activation (BF16 bits when
+    cache_kind == CACHE_BF16, else FP8 codes of format cache_kind with their
+    inverse scale), cast to `fmt` with `scale`.  Returns a QuantResult
+    (bf16 = dH copy, fp8 = codes, amax_bits, sat)."""
+    dA = np.ascontiguousarray(dA, dtype=np.uint16)
+    shape = dA.shape
+    if cache_kind == CACHE_BF16:
+        cache = np.ascontiguousarray(cache, dtype=np.uint16)
+    else:
+        cache = np.ascontiguousarray(cache, dtype=np.uint8)
+    assert cache.shape == shape
+    n = dA.size
+    bf = np.empty(shape, dtype=np.uint16)
+    q = np.empty(shape, dtype=np.uint8)
+    amax = ctypes.c_uint32(0)
+    sat = ctypes.c_uint64(0)
+    lib().oracle_relu2_backward(_ptr(dA, _u16p), cache.ctypes.data, cache_kind, a_scale_inv, n,
+                                fmt, scale, _ptr(bf, _u16p), _ptr(q, _u8p), ctypes.byref(amax),
+                                ctypes.byref(sat))
+    return QuantResult(bf, q, None, int(amax.value), int(sat.value))
 
 
 # --------------------------------------------------------------------------- MXFP8

@@ -543,6 +543,54 @@ void oracle_gemm_mx_f64(const uint8_t* a, int fa, const uint8_t* ea, const uint8
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the squared ReLU from a cached activation ([FP8T] Step 3:    */
+/* the activations kept for the backward pass may be stored in FP8 to save  */
+/* memory, except a few sensitive ones).                                    */
+/* ------------------------------------------------------------------------ */
+#define ORC_CACHE_BF16 2
+
+/* For A = relu(H)^2 the derivative is dA/dH = 2 relu(H) = 2 sqrt(A), so the
+   backward pass needs only the cached activation a (the tensor the weight
+   gradient of the next layer reads anyway), either its BF16 copy or its FP8
+   codes with the inverse scale they were cast with.  Per element, binary32
+   with round-to-nearest-even, one operation at a time:
+     a  = cache_kind == ORC_CACHE_BF16 ? bf16(cache) : dec(code) * a_scale_inv
+     r  = sqrt(a)                      (IEEE square root: NaN below zero, -0 kept)
+     g  = (2 r) * dA                   (2 r is exact)
+     b  = bf16_rne(g)                  -> bf16_out
+     code = sat_rne(b * scale)         -> fp8_out, the gradient's delayed scale
+   amax is the largest |b| (bit patterns compared as unsigned integers) and
+   sat the number of saturating elements, as in oracle_quantize. */
+void oracle_relu2_backward(const uint16_t* dA, const void* cache, int cache_kind,
+                           float a_scale_inv, int64_t n, int fmt, float scale,
+                           uint16_t* bf16_out, uint8_t* fp8_out, uint32_t* amax_bits_out,
+                           uint64_t* sat_out) {
+  uint32_t amax = 0;
+  uint64_t sat = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    float a;
+    if (cache_kind == ORC_CACHE_BF16) {
+      a = oracle_bf16_to_f32(((const uint16_t*)cache)[i]);
+    } else {
+      float d = (float)oracle_fp8_decode(((const uint8_t*)cache)[i], cache_kind);
+      a = d * a_scale_inv;
+    }
+    float r = sqrtf(a);
+    float two_r = 2.0f * r;
+    float g = two_r * oracle_bf16_to_f32(dA[i]);
+    uint16_t b = oracle_bf16_rne(g);
+    if (bf16_out) bf16_out[i] = b;
+    uint32_t mag = ((uint32_t)(b & 0x7FFF)) << 16;
+    if (mag > amax) amax = mag;
+    float v = oracle_bf16_to_f32(b) * scale;
+    if (fp8_out) fp8_out[i] = oracle_fp8_encode(v, fmt);
+    sat += (uint64_t)oracle_fp8_saturates(v, fmt);
+  }
+  if (amax_bits_out) *amax_bits_out = amax;
+  if (sat_out) *sat_out = sat;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batch helpers (the per-element functions above applied to arrays).        */
 /* ------------------------------------------------------------------------ */
 void oracle_fp8_encode_batch(const float* x, int64_t n, int fmt, uint8_t* out) {
