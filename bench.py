@@ -215,6 +215,8 @@ def main():
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
     out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
+    out["fp8_cached_activation"] = fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args,
+                                              q_mean)
     out["recompute_on_overflow"] = recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args,
                                              total_ms / args.steps)
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
@@ -419,6 +421,49 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
             "fp8_gemm_mx": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
+
+
+def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):
+    """The activation kept for the backward pass stored only as FP8: the
+    forward quantizer without the BF16 copy (3 B per element instead of 5),
+    and the squared ReLU's backward reading the E4M3 cache (dH = dA * 2 sqrt(A),
+    cast to E5M2 with the gradient state) against the same kernel reading the
+    BF16 copy."""
+    M, K = w.M, w.K
+    stream = torch.cuda.current_stream()
+    n_in, n_out = len(H), len(A16)
+    dA = torch.from_numpy(w.da().view(np.int16)).to(dev).view(torch.bfloat16)
+    dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
+    st_h = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
+    si = st_a.field_ptr("scale_inv_used")
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    fwd = timed(lambda i: sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR,
+                                            st_a, None, A8[i % n_out]))
+    bwd8 = timed(lambda i: sq.relu2_backward_quantize(dA, A8[i % n_out], sq.CACHE_E4M3, si,
+                                                      sq.E5M2, st_h, dH8[i % 2]))
+    bwd16 = timed(lambda i: sq.relu2_backward_quantize(dA, A16[i % n_out], sq.CACHE_BF16, None,
+                                                       sq.E5M2, st_h, dH8[i % 2]))
+    n = M * K
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    return {"forward_quantize_without_copy": {"ms": round(fwd, 5), "GB/s": gbs(3 * n, fwd),
+                                              "vs_with_copy": round(q_with_copy_ms / fwd, 3)},
+            "relu2_backward_e4m3_cache": {"ms": round(bwd8, 5), "GB/s": gbs(4 * n, bwd8),
+                                          "bytes_per_launch": 4 * n},
+            "relu2_backward_bf16_cache": {"ms": round(bwd16, 5), "GB/s": gbs(5 * n, bwd16),
+                                          "bytes_per_launch": 5 * n},
+            "activation_bytes_kept": {"fp8": n, "bf16": 2 * n}}
 
 
 def recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args, step_ms):

@@ -209,6 +209,35 @@ int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, 
 int fp8_transpose(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                   hipStream_t stream);
 
+/* Which form the activation kept for the backward pass takes: FP8 codes
+ * (with the inverse scale they were cast with) or the BF16 copy. */
+typedef enum { FP8DP_CACHE_E4M3 = 0, FP8DP_CACHE_E5M2 = 1, FP8DP_CACHE_BF16 = 2 } fp8dp_cache;
+
+/* Backward of the squared ReLU from the cached activation, fused with the
+ * gradient's FP8 cast ("FP8 training ...", Step 3: the activations kept for
+ * the backward pass may be stored in FP8, except a few sensitive ones).
+ * For A = relu(H)^2, dH = dA * 2 relu(H) = dA * 2 sqrt(A):
+ *   dA        [rows x cols] BF16, the gradient of A (e.g. the dgrad GEMM's output)
+ *   a_cache   [rows x cols] the cached A: FP8 codes (cache = E4M3 / E5M2) or
+ *             BF16 (cache = BF16)
+ *   a_scale_inv  device pointer to the inverse scale the codes were cast
+ *             with (FP8 caches; e.g. &st_a->scale_inv_used after the forward
+ *             step's amax_history_update), ignored for BF16
+ *   per element, binary32 nearest-even one operation at a time:
+ *     a = BF16 ? bf16(a_cache) : dec(code) * a_scale_inv; g = (2 sqrt(a)) * dA
+ *     (IEEE square root: a negative or NaN a gives NaN, whose sign is not
+ *     specified); b = bf16_rne(g) -> bf16_out (may be NULL);
+ *     fp8_out = sat_rne(b * st->scale) in format fmt (E5M2 in the FP8
+ *     recipe), max |b| and the saturation count folded into st's
+ *     accumulators (consumed by amax_history_update), as quantize_fused.
+ * Errors: EINVAL for NULL dA / a_cache / st / fp8_out, a NULL a_scale_inv with
+ * an FP8 cache, rows or cols < 1, misaligned pointers (16 bytes; the scale 4),
+ * or an unknown cache kind or format. */
+int relu2_backward_quantize(const uint16_t* dA, const void* a_cache, fp8dp_cache cache,
+                            const float* a_scale_inv, int64_t rows, int64_t cols,
+                            fp8dp_format fmt, fp8dp_tensor_state* st, uint16_t* bf16_out,
+                            uint8_t* fp8_out, hipStream_t stream);
+
 /* Recompute after an overflow ("FP8 Training & Inference", Delayed Scaling:
  * a step whose delayed scale was too large is detected and recomputed with a
  * corrected scale).  Enqueue after amax_history_update of the step: when that
@@ -333,7 +362,8 @@ int fp8dp_bench_copy(const void* src, void* dst, int64_t bytes, hipStream_t stre
 /* Device conversion routines applied to arbitrary binary32 inputs, for
  * exhaustive comparison with a reference.  target 0: E4M3 codes (uint8 out),
  * 1: E5M2 codes (uint8 out), 2: BF16 round-to-nearest-even (uint16 out).
- * 3: saturation predicate for E4M3, 4: for E5M2 (uint8 0/1 out). */
+ * 3: saturation predicate for E4M3, 4: for E5M2 (uint8 0/1 out), 5: the
+ * binary32 square root the activation backward uses (float out). */
 int fp8dp_convert_f32(const float* x, int64_t n, int32_t target, void* out, hipStream_t stream);
 
 /* Device scale rule on n amax values: scale[i] = max / (amax[i] * margin)

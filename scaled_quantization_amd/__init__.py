@@ -49,6 +49,8 @@ _SIGS = {
     "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
                                 _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
+                                ctypes.c_int),
     "quantize_recompute": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
                            ctypes.c_int),
@@ -227,6 +229,22 @@ def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if tuple(dst.shape) != (cols, rows):
         raise Fp8dpError("fp8_transpose: shape mismatch")
     _check(lib().fp8_transpose(_p(src), rows, cols, _p(dst), _stream(stream)), "fp8_transpose")
+
+
+CACHE_E4M3, CACHE_E5M2, CACHE_BF16 = 0, 1, 2
+
+
+def relu2_backward_quantize(dA: torch.Tensor, a_cache: torch.Tensor, cache: int,
+                            a_scale_inv: Ptr, fmt: int, st, fp8_out: torch.Tensor,
+                            bf16_out: Ptr = None, stream=None) -> None:
+    """dH = dA * 2 sqrt(A) from the cached activation (FP8 codes + inverse scale, or
+    BF16), cast to fmt with st's delayed scale (amax / saturation folded into st)."""
+    rows, cols = (1, dA.numel()) if dA.dim() == 1 else (dA.shape[0], dA[0].numel())
+    if a_cache.numel() != dA.numel() or fp8_out.numel() != dA.numel():
+        raise Fp8dpError("relu2_backward_quantize: size mismatch")
+    _check(lib().relu2_backward_quantize(_p(dA), _p(a_cache), cache, _p(a_scale_inv), rows, cols,
+                                         fmt, _state_ptr(st), _p(bf16_out), _p(fp8_out),
+                                         _stream(stream)), "relu2_backward_quantize")
 
 
 def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.Tensor,

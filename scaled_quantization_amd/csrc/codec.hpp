@@ -144,6 +144,28 @@ __device__ __forceinline__ uint32_t pack2_bf16_int(float lo, float hi) {
   return bf16_rne_int(lo) | (bf16_rne_int(hi) << 16);
 }
 
+// ---------------------------------------------------------------- decode
+// FP8 code -> binary32, exact (every E4M3 / E5M2 value is a binary32 value):
+// normal codes rebias the exponent (E4M3: +120, E5M2: +112) and move the
+// mantissa to the top of the fraction; subnormal codes are m * 2^-9 (E4M3)
+// or m * 2^-16 (E5M2); E4M3 S.1111.111 and E5M2 exponent 31 with m != 0 are
+// NaN, E5M2 exponent 31 with m == 0 is infinity.
+template <int FMT>
+__device__ __forceinline__ float dec_int(uint32_t c) {
+  const uint32_t sgn = (c & 0x80u) << 24;
+  if constexpr (FMT == 0) {
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    if (e == 15u && m == 7u) return __uint_as_float(sgn | 0x7FC00000u);
+    if (e == 0u) return __uint_as_float(sgn | __float_as_uint((float)m * 0x1p-9f));
+    return __uint_as_float(sgn | ((e + 120u) << 23) | (m << 20));
+  } else {
+    const uint32_t e = (c >> 2) & 0x1Fu, m = c & 3u;
+    if (e == 31u) return __uint_as_float(sgn | (m ? 0x7FC00000u : 0x7F800000u));
+    if (e == 0u) return __uint_as_float(sgn | __float_as_uint((float)m * 0x1p-16f));
+    return __uint_as_float(sgn | ((e + 112u) << 23) | (m << 21));
+  }
+}
+
 // ---------------------------------------------------------------- scale rule
 // s = max / (amax * margin) in binary32, nearest even, no contraction; falls
 // back to 1 when amax * margin is not a positive finite number or the

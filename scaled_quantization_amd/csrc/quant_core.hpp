@@ -13,6 +13,27 @@
 namespace fp8dp {
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_nt_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt_t __attribute__((ext_vector_type(2)));
+
+// 16- and 8-byte loads marked non-temporal (streamed data that is not read again).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const u32x2_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// Streaming stores: the outputs are not read again by this kernel, so they
+// should not displace the inputs from the caches.
+__device__ __forceinline__ void store_nt(uint4* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(u32x4_nt_t{a, b, c, d}, reinterpret_cast<u32x4_nt_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2_nt_t{v.x, v.y}, reinterpret_cast<u32x2_nt_t*>(p));
+}
 
 // Largest 16-bit magnitude among the 8 BF16 values of a vector.
 template <bool SIGNED>

@@ -33,23 +33,6 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
 constexpr int kBlocksPerCU = 32;   // grid of the element-wise kernels
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte load marked non-temporal (streamed data that is not read again).
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Streaming stores: the outputs are not read again by this kernel, so they
-// should not displace the inputs from the caches.
-__device__ __forceinline__ void store_nt(uint4* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  __builtin_nontemporal_store(u32x4_t{a, b, c, d}, reinterpret_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
-}
 
 // ------------------------------------------------------------------ per tensor
 // h/bout/qout are viewed as vectors of 8 elements (n8 of them); the last
@@ -431,6 +414,12 @@ __global__ __launch_bounds__(kThreads) void k_convert(const float* __restrict__ 
                        pack2_bf16_hw(v[4], v[5]), pack2_bf16_hw(v[6], v[7]));
       }
       reinterpret_cast<uint4*>(out)[i] = r;
+    } else if constexpr (TARGET == 5) {
+      float r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = __builtin_sqrtf(v[j]);
+      reinterpret_cast<float4*>(out)[2 * i] = make_float4(r[0], r[1], r[2], r[3]);
+      reinterpret_cast<float4*>(out)[2 * i + 1] = make_float4(r[4], r[5], r[6], r[7]);
     } else {
       uint2 q = make_uint2(0, 0);
 #pragma unroll
@@ -763,7 +752,7 @@ extern "C" int fp8dp_bench_copy(const void* src, void* dst, int64_t bytes, hipSt
 
 extern "C" int fp8dp_convert_f32(const float* x, int64_t n, int32_t target, void* out,
                                  hipStream_t stream) {
-  if (x == nullptr || out == nullptr || n < 8 || n % 8 || target < 0 || target > 4 ||
+  if (x == nullptr || out == nullptr || n < 8 || n % 8 || target < 0 || target > 5 ||
       !aligned16(x) || !aligned16(out)) {
     set_error("fp8dp_convert_f32: bad arguments (n must be a positive multiple of 8)");
     return FP8DP_EINVAL;
@@ -780,6 +769,7 @@ extern "C" int fp8dp_convert_f32(const float* x, int64_t n, int32_t target, void
   FP8DP_CONV(2)
   FP8DP_CONV(3)
   FP8DP_CONV(4)
+  FP8DP_CONV(5)
 #undef FP8DP_CONV
   return check_launch("fp8dp_convert_f32");
 }

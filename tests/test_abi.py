@@ -33,7 +33,7 @@ def test_header_declares_the_named_entry_points():
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
               "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
-              "fp8_gemm_scaled_if", "fp8dp_last_error"):
+              "fp8_gemm_scaled_if", "relu2_backward_quantize", "fp8dp_last_error"):
         assert n in names
 
 
@@ -153,3 +153,14 @@ def test_recompute_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"256" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 18, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+
+
+def test_relu2_backward_argument_checks_reject_without_launching(L):
+    rc = L.relu2_backward_quantize(16, 16, 0, None, 4, 8, 1, 16, None, 16, None)
+    assert rc == -1 and b"inverse scale" in L.fp8dp_last_error()
+    rc = L.relu2_backward_quantize(16, 16, 5, 16, 4, 8, 1, 16, None, 16, None)
+    assert rc == -1 and b"cache" in L.fp8dp_last_error()
+    rc = L.relu2_backward_quantize(16, 16, 2, None, 4, 8, 1, 24, None, 16, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.relu2_backward_quantize(16, 16, 2, None, 4, 8, 1, 16, None, None, None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()

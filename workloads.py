@@ -155,6 +155,11 @@ class Workload:
         return normal(self.seed + 5000, self.K, self.N, std=float(self.N) ** -0.5, row0=row0,
                       nrows=nrows)
 
+    def da(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
+        """Gradient dA [M x K] of the activation (the dgrad GEMM's output shape):
+        signed log-normal, sigma 1."""
+        return signed_lognormal(self.seed + 6000, self.M, self.K, 1.0, row0=row0, nrows=nrows)
+
     def dy(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
         return signed_lognormal(self.seed + 2000, self.M, self.N, 3.0, row0=row0, nrows=nrows)
 
