@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--workload", default="gpt2")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-naive", action="store_true")
-    p.add_argument("--only", choices=("quantize", "gemm", "copy"), default=None,
+    p.add_argument("--only", choices=("quantize", "gemm", "copy", "quantize_mx", "gemm_mx",
+                                      "relu2_bwd"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
                         "inputs (for hardware counter runs), then exit")
     return p.parse_args()
@@ -100,7 +101,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     if args.only is not None:
-        kernel_only(sq, torch, args, H, A16, A8, w8, wsc, Y, st_a, n_in, n_out, dev)
+        kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, n_out, dev)
         return
 
     def quant(i):
@@ -225,12 +226,42 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_only(sq, torch, args, H, A16, A8, w8, wsc, Y, st_a, n_in, n_out, dev):
+def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, n_out, dev):
     """One kernel of the step, repeated with the step's own rotation of inputs
     and outputs; a profiler's per-dispatch counters then describe exactly the
-    launches the timed steps make."""
+    launches the timed steps make (the MX and activation-backward legs the
+    same way as their bench legs)."""
+    M, K, N = w.M, w.K, w.N
+    # one step first, so the delayed scale is the one this data produces (as in
+    # the timed steps, which follow the warm-up)
+    sq.quantize_fused(H[0], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, None, None)
+    sq.amax_history_update(st_a)
+    if args.only in ("quantize_mx", "gemm_mx"):
+        E = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(n_out)]
+        wm8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        we = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+        sq.quantize_mx(wt, sq.ACT_IDENTITY, sq.E4M3, wm8, we)
+        for j in range(n_out):
+            sq.quantize_mx(H[j % n_in], sq.ACT_RELU2, sq.E4M3, A8[j], E[j])
+    if args.only == "relu2_bwd":
+        dA = torch.from_numpy(w.da().view(np.int16)).to(dev).view(torch.bfloat16)
+        dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
+        st_h = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
+        for j in range(n_out):
+            sq.quantize_fused(H[j % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, None, A8[j])
+        sq.relu2_backward_quantize(dA, A8[0], sq.CACHE_E4M3, st_a.field_ptr("scale_inv"),
+                                   sq.E5M2, st_h, dH8[0])
+        sq.amax_history_update(st_h)
     for i in range(args.warmup + args.steps):
-        if args.only == "quantize":
+        if args.only == "quantize_mx":
+            sq.quantize_mx(H[i % n_in], sq.ACT_RELU2, sq.E4M3, A8[i % n_out], E[i % n_out],
+                           A16[i % n_out])
+        elif args.only == "gemm_mx":
+            sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], wm8, sq.E4M3, we, Y)
+        elif args.only == "relu2_bwd":
+            sq.relu2_backward_quantize(dA, A8[i % n_out], sq.CACHE_E4M3,
+                                       st_a.field_ptr("scale_inv"), sq.E5M2, st_h, dH8[i % 2])
+        elif args.only == "quantize":
             sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a,
                               A16[i % n_out], A8[i % n_out])
         elif args.only == "gemm":
@@ -436,6 +467,9 @@ def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):
     dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
     st_h = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
     si = st_a.field_ptr("scale_inv_used")
+    # one step first, so the gradient's delayed scale is the one this data produces
+    sq.relu2_backward_quantize(dA, A8[0], sq.CACHE_E4M3, si, sq.E5M2, st_h, dH8[0])
+    sq.amax_history_update(st_h)
 
     def timed(fn):
         for i in range(args.warmup):
@@ -468,38 +502,61 @@ def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):
 
 def recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args, step_ms):
     """Cost of the overflow-triggered recompute: quantize_recompute and
-    fp8_gemm_scaled_if enqueued after the state update of every step.  The
-    step's own state has not overflowed (idle: every workgroup reads the
-    flag and returns); a second state initialised with a tiny amax has (the
-    re-cast and the GEMM run in full)."""
+    fp8_gemm_scaled_if enqueued after the state update of every step.  Idle
+    (the usual case: no overflow, every workgroup reads the flag and returns)
+    as the difference of whole-step times with and without the two calls;
+    triggered (a state initialised with a tiny amax has overflowed) as the
+    re-cast plus the GEMM run in full."""
+    import numpy as np
     stream = torch.cuda.current_stream()
-    h = H[0]
-    st_hot = sq.TensorState(sq.E4M3, 1, w.margin, 1e-3, device=dev)
-    sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_hot, None, A8[1])
-    sq.amax_history_update(st_hot)
+    n_in, n_out = len(H), len(A8)
+    DY8 = torch.empty((w.M, w.N), dtype=torch.uint8, device=dev)
+    dy = torch.from_numpy(w.dy().view(np.int16)).to(dev).view(torch.bfloat16)
+    st = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
+    st_g = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
 
-    def pair(st, a8):
-        sq.quantize_recompute(h, sq.ACT_RELU2, sq.E4M3, st, a8)
-        sq.fp8_gemm_scaled_if(a8, sq.E4M3, w8, sq.E4M3, st.field_ptr("scale_inv"), wsc, Y,
-                              st.field_ptr("overflow"))
+    def step(i, with_recompute):
+        h, a8 = H[i % n_in], A8[i % n_out]
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st, None, a8)
+        sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR, st.field_ptr("scale_inv"),
+                           wsc, Y)
+        sq.amax_history_update(st)
+        if with_recompute:
+            sq.quantize_recompute(h, sq.ACT_RELU2, sq.E4M3, st, a8)
+            sq.fp8_gemm_scaled_if(a8, sq.E4M3, w8, sq.E4M3, st.field_ptr("scale_inv"), wsc, Y,
+                                  st.field_ptr("overflow"))
+        sq.quantize_fused(dy, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, DY8)
+        sq.amax_history_update(st_g)
+        if with_recompute:
+            sq.quantize_recompute(dy, sq.ACT_IDENTITY, sq.E5M2, st_g, DY8)
 
-    def timed(fn):
-        for _ in range(3):
-            fn()
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(args.steps):
-            fn()
+        for i in range(reps):
+            fn(3 + i)
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
+        return a.elapsed_time(b) / reps
 
-    idle = timed(lambda: pair(st_a, A8[0]))
-    hot = timed(lambda: pair(st_hot, A8[1]))
-    flags = (st_a.read()["overflow"], st_hot.read()["overflow"])
-    return {"idle_ms": round(idle, 5), "idle_frac_of_step": round(idle / step_ms, 4),
-            "triggered_ms": round(hot, 5), "overflow_flags_idle_hot": list(flags)}
+    plain = timed(lambda i: step(i, False), args.steps)
+    withr = timed(lambda i: step(i, True), args.steps)
+    flag_idle = st.read()["overflow"]
+    st_hot = sq.TensorState(sq.E4M3, 1, w.margin, 1e-3, device=dev)
+    sq.quantize_fused(H[0], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_hot, None, A8[1])
+    sq.amax_history_update(st_hot)
+    hot = timed(lambda i: (sq.quantize_recompute(H[0], sq.ACT_RELU2, sq.E4M3, st_hot, A8[1]),
+                           sq.fp8_gemm_scaled_if(A8[1], sq.E4M3, w8, sq.E4M3,
+                                                 st_hot.field_ptr("scale_inv"), wsc, Y,
+                                                 st_hot.field_ptr("overflow"))), args.steps)
+    return {"step_ms": round(plain, 5), "step_with_recompute_ms": round(withr, 5),
+            "idle_cost_ms": round(withr - plain, 5),
+            "idle_cost_frac": round((withr - plain) / plain, 4),
+            "triggered_ms": round(hot, 5),
+            "overflow_flags_idle_hot": [flag_idle, st_hot.read()["overflow"]]}
 
 
 def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):

@@ -33,11 +33,22 @@ constexpr int kCacheBf16 = FP8DP_CACHE_BF16;
 
 typedef float v2f_t __attribute__((ext_vector_type(2)));
 
-// The 8 cached activation values of vector i as binary32.
-template <int CACHE, bool HW>
-__device__ __forceinline__ void load_cache(const void* cache, int64_t i, float si, float a[8]) {
+// The raw cache bytes of vector i (16 for BF16, 8 for FP8), loaded before
+// any arithmetic so that both vectors of an iteration are in flight together.
+template <int CACHE>
+__device__ __forceinline__ uint4 load_cache(const void* cache, int64_t i) {
   if constexpr (CACHE == kCacheBf16) {
-    const uint4 c = load_nt(reinterpret_cast<const uint4*>(cache) + i);
+    return load_nt(reinterpret_cast<const uint4*>(cache) + i);
+  } else {
+    const uint2 c = load_nt(reinterpret_cast<const uint2*>(cache) + i);
+    return make_uint4(c.x, c.y, 0u, 0u);
+  }
+}
+
+// Those bytes as 8 binary32 activation values.
+template <int CACHE, bool HW>
+__device__ __forceinline__ void cache_values(const uint4& c, float si, float a[8]) {
+  if constexpr (CACHE == kCacheBf16) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -45,7 +56,6 @@ __device__ __forceinline__ void load_cache(const void* cache, int64_t i, float s
       a[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
   } else {
-    const uint2 c = load_nt(reinterpret_cast<const uint2*>(cache) + i);
     const uint32_t w[2] = {c.x, c.y};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -87,9 +97,9 @@ __global__ __launch_bounds__(kThreads) void k_relu2_bwd(const uint4* __restrict_
   const float s = *s_ptr;
   uint32_t amax16 = 0, sat = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  auto one = [&](const uint4& d, int64_t i) {
+  auto one = [&](const uint4& d, const uint4& c, int64_t i) {
     float a[8];
-    load_cache<CACHE, HW>(cache, i, si, a);
+    cache_values<CACHE, HW>(c, si, a);
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
     float g[8];
     uint32_t gmax = 0;
@@ -119,10 +129,11 @@ __global__ __launch_bounds__(kThreads) void k_relu2_bwd(const uint4* __restrict_
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   for (; i + stride < n8; i += 2 * stride) {
     const uint4 d0 = load_nt(dA + i), d1 = load_nt(dA + i + stride);
-    one(d0, i);
-    one(d1, i + stride);
+    const uint4 c0 = load_cache<CACHE>(cache, i), c1 = load_cache<CACHE>(cache, i + stride);
+    one(d0, c0, i);
+    one(d1, c1, i + stride);
   }
-  if (i < n8) one(load_nt(dA + i), i);
+  if (i < n8) one(load_nt(dA + i), load_cache<CACHE>(cache, i), i);
   if (tail && blockIdx.x == 0 && threadIdx.x == 0) {
     const uint16_t* dt = reinterpret_cast<const uint16_t*>(dA + n8);
     for (int t = 0; t < tail; ++t) {

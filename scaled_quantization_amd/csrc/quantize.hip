@@ -554,7 +554,9 @@ static int launch_recast(const uint16_t* h, int64_t n, uint8_t* qout,
                          const fp8dp_tensor_state* st, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, kBlocksPerCU);
+  // a small grid: in the usual case (no overflow) every workgroup only reads
+  // the flag, and the launch's cost grows with its workgroup count
+  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, 2);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_recast<FMT, ACT, true>), dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint4*>(h), reinterpret_cast<uint2*>(qout), n8,
