@@ -97,16 +97,41 @@ __global__ __launch_bounds__(kThreads) void k_relu2_bwd(const uint4* __restrict_
   const float s = *s_ptr;
   uint32_t amax16 = 0, sat = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  // An FP8 cache has 256 possible codes and one inverse scale per launch, so
+  // 2 sqrt(dec(code) * si) is tabulated once per workgroup (thread t computes
+  // code t with exactly the per-element operations) and each element costs
+  // one LDS read and one multiply.
+  __shared__ float two_root[CACHE == kCacheBf16 ? 1 : 256];
+  if constexpr (CACHE != kCacheBf16) {
+    static_assert(kThreads == 256, "one table entry per thread");
+    float d;
+    if constexpr (!HW) {
+      d = dec_int<CACHE>(threadIdx.x);
+    } else if constexpr (CACHE == 0) {
+      d = __builtin_amdgcn_cvt_pk_f32_fp8((int)threadIdx.x, false)[0];
+    } else {
+      d = __builtin_amdgcn_cvt_pk_f32_bf8((int)threadIdx.x, false)[0];
+    }
+    two_root[threadIdx.x] = __fmul_rn(2.0f, __builtin_sqrtf(__fmul_rn(d, si)));
+    __syncthreads();
+  }
   auto one = [&](const uint4& d, const uint4& c, int64_t i) {
-    float a[8];
-    cache_values<CACHE, HW>(c, si, a);
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
     float g[8];
     uint32_t gmax = 0;
+    float a[8];
+    if constexpr (CACHE == kCacheBf16) cache_values<CACHE, HW>(c, si, a);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      g[2 * j] = dgrad_elem(a[2 * j], __uint_as_float(dw[j] << 16));
-      g[2 * j + 1] = dgrad_elem(a[2 * j + 1], __uint_as_float(dw[j] & 0xFFFF0000u));
+      if constexpr (CACHE == kCacheBf16) {
+        g[2 * j] = dgrad_elem(a[2 * j], __uint_as_float(dw[j] << 16));
+        g[2 * j + 1] = dgrad_elem(a[2 * j + 1], __uint_as_float(dw[j] & 0xFFFF0000u));
+      } else {
+        const uint32_t w = j < 2 ? c.x : c.y;
+        const uint32_t c0 = (w >> (16 * (j & 1))) & 0xFFu, c1 = (w >> (16 * (j & 1) + 8)) & 0xFFu;
+        g[2 * j] = __fmul_rn(two_root[c0], __uint_as_float(dw[j] << 16));
+        g[2 * j + 1] = __fmul_rn(two_root[c1], __uint_as_float(dw[j] & 0xFFFF0000u));
+      }
       const uint32_t m0 = __float_as_uint(g[2 * j]) & 0x7FFFFFFFu;
       const uint32_t m1 = __float_as_uint(g[2 * j + 1]) & 0x7FFFFFFFu;
       gmax = m0 > gmax ? m0 : gmax;
