@@ -409,6 +409,27 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
                                                     ws, dw))
         res["wgrad"][f"splits_{splits}"] = {"ms": round(t, 5),
                                             "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1)}
+    # dgrad with the squared ReLU's backward in its epilogue (FP8 activation
+    # cache A8, E5M2 dH with its own delayed state) against the same two steps
+    # as separate kernels
+    dh8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    st_h = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
+    sq.fp8_gemm_relu2_backward(dy8, sq.E5M2, w8t, sq.E4M3, si_g, wsc, A8[0], sq.CACHE_E4M3, si_a,
+                               sq.E5M2, st_h, dh8)
+    sq.amax_history_update(st_h)
+    t_fused = timed(lambda: sq.fp8_gemm_relu2_backward(dy8, sq.E5M2, w8t, sq.E4M3, si_g, wsc,
+                                                       A8[0], sq.CACHE_E4M3, si_a, sq.E5M2,
+                                                       st_h, dh8))
+
+    def two():
+        sq.fp8_gemm_scaled(dy8, sq.E5M2, w8t, sq.E4M3, sq.PER_TENSOR, si_g, wsc, dx)
+        sq.relu2_backward_quantize(dx, A8[0], sq.CACHE_E4M3, si_a, sq.E5M2, st_h, dh8)
+
+    t_two = timed(two)
+    res["dgrad_relu2_backward_fused"] = {
+        "shape": f"dY8[{M}x{N}] x W8^T -> dA[{M}x{K}] -> dH = dA * 2 sqrt(A) from A8 -> e5m2",
+        "ms": round(t_fused, 5), "TFLOP/s": round(flops / (t_fused * 1e-3) / 1e12, 1),
+        "unfused_ms": round(t_two, 5), "fused_speedup": round(t_two / t_fused, 3)}
     return res
 
 

@@ -238,6 +238,28 @@ int relu2_backward_quantize(const uint16_t* dA, const void* a_cache, fp8dp_cache
                             fp8dp_format fmt, fp8dp_tensor_state* st, uint16_t* bf16_out,
                             uint8_t* fp8_out, hipStream_t stream);
 
+/* The FP8 recipe's dgrad GEMM with the squared ReLU's backward in its
+ * epilogue ("FP8 training ...", Step 3: activations kept for the backward
+ * pass in FP8; "FP8 Training & Inference", FP8 Training Recipe: E5M2
+ * gradients x E4M3 weights).  Equal, bit for bit, to
+ *   fp8_gemm_scaled(a, E5M2, b, E4M3, M, N, K, PER_TENSOR, ACCUM_MFMA_FP8,
+ *                   a_scale_inv, b_scale_inv, dA)           (dA [M x N] BF16)
+ *   relu2_backward_quantize(dA, act_cache, cache, act_scale_inv, M, N, fmt,
+ *                           st, NULL, dh_out)
+ * without dA's write and read: dh_out [M x N] codes in format fmt cast with
+ * st->scale, amax and saturation count folded into st.  a [M x K] is dY8, b
+ * [N x K] the weight codes transposed (W8^T), act_cache [M x N] the FP8 codes
+ * of the activation A with act_scale_inv the inverse scale they were cast
+ * with.
+ * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
+ * not of 128, misaligned pointers (16 bytes; scales 4) or unknown formats;
+ * EUNSUPPORTED for operand formats other than E5M2 x E4M3 or a BF16 cache. */
+int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
+                            int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
+                            const float* b_scale_inv, const uint8_t* act_cache, fp8dp_cache cache,
+                            const float* act_scale_inv, fp8dp_format fmt, fp8dp_tensor_state* st,
+                            uint8_t* dh_out, hipStream_t stream);
+
 /* Recompute after an overflow ("FP8 Training & Inference", Delayed Scaling:
  * a step whose delayed scale was too large is detected and recomputed with a
  * corrected scale).  Enqueue after amax_history_update of the step: when that

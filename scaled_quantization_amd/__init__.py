@@ -51,6 +51,8 @@ _SIGS = {
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
+    "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
+                                 _vp, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_recompute": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
                            ctypes.c_int),
@@ -245,6 +247,22 @@ def relu2_backward_quantize(dA: torch.Tensor, a_cache: torch.Tensor, cache: int,
     _check(lib().relu2_backward_quantize(_p(dA), _p(a_cache), cache, _p(a_scale_inv), rows, cols,
                                          fmt, _state_ptr(st), _p(bf16_out), _p(fp8_out),
                                          _stream(stream)), "relu2_backward_quantize")
+
+
+def fp8_gemm_relu2_backward(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, a_scale_inv: Ptr,
+                            b_scale_inv: Ptr, act_cache: torch.Tensor, cache: int,
+                            act_scale_inv: Ptr, fmt: int, st, dh_out: torch.Tensor,
+                            stream=None) -> None:
+    """dgrad a [M, K] x b [N, K]^T with the squared ReLU's backward in the epilogue:
+    dh_out [M, N] gradient codes from the cached activation codes act_cache [M, N]."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(act_cache.shape) != (M, N) or tuple(dh_out.shape) != (M, N):
+        raise Fp8dpError("fp8_gemm_relu2_backward: shape mismatch")
+    _check(lib().fp8_gemm_relu2_backward(_p(a), fa, _p(b), fb, M, N, K, _p(a_scale_inv),
+                                         _p(b_scale_inv), _p(act_cache), cache, _p(act_scale_inv),
+                                         fmt, _state_ptr(st), _p(dh_out), _stream(stream)),
+           "fp8_gemm_relu2_backward")
 
 
 def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.Tensor,

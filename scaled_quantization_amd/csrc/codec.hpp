@@ -125,6 +125,18 @@ __device__ __forceinline__ uint32_t pack4_hw(float v0, float v1, float v2, float
   return (uint32_t)w;
 }
 
+// The same for two values (codes in the low 16 bits).
+template <int FMT>
+__device__ __forceinline__ uint32_t pack2_hw(float v0, float v1) {
+  constexpr float m = Fmt<FMT>::maxv;
+  v0 = __builtin_amdgcn_fmed3f(v0, -m, m);
+  v1 = __builtin_amdgcn_fmed3f(v1, -m, m);
+  int w;
+  if constexpr (FMT == 0) w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  else w = __builtin_amdgcn_cvt_pk_bf8_f32(v0, v1, 0, false);
+  return (uint32_t)w & 0xFFFFu;
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t pack4_int(float v0, float v1, float v2, float v3) {
   return enc_int<FMT>(v0) | (enc_int<FMT>(v1) << 8) | (enc_int<FMT>(v2) << 16) |

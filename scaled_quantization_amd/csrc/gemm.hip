@@ -24,6 +24,7 @@
 #include "codec.hpp"
 #include "common.hpp"
 #include "gemm_core.hpp"
+#include "quant_core.hpp"
 
 namespace fp8dp {
 
@@ -275,9 +276,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // (lane / 32 selects the half), which is exactly one block: the MFMA applies
 // 2^(ea - 127) 2^(eb - 127) to each block's products, and the epilogue has
 // no scale to apply.
+// The squared ReLU's backward applied in the epilogue (BC >= 0): the GEMM's
+// output is dA, and each element leaves as the gradient code
+//   code = sat_rne(bf16(two_root[c] * bf16(dA)) * scale),
+//   two_root[c] = 2 sqrt(dec(c) * cache_si), c = the cached activation's code,
+// i.e. exactly fp8_gemm_scaled followed by relu2_backward_quantize on its
+// output, without dA's round trip through memory.
+struct Relu2Bwd {
+  const uint8_t* cache;     // [M x N] FP8 codes of the cached activation (format BC)
+  const float* cache_si;    // the inverse scale they were cast with
+  uint8_t* out;             // [M x N] gradient codes (format BF)
+  const float* scale;       // the gradient state's scale
+  fp8dp_acc_slot* slots;    // the gradient state's accumulators
+};
+
 // COND: the launch does nothing unless *run_flag != 0 (a device-side flag,
 // e.g. the overflow mark of a scaling state), read once by every workgroup.
-template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false>
+template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false, int BC = -1,
+          int BF = 1>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
@@ -286,8 +302,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
                                                      float* __restrict__ ws, int splits,
                                                      const uint8_t* __restrict__ ea = nullptr,
                                                      const uint8_t* __restrict__ eb = nullptr,
-                                                     const uint32_t* __restrict__ run_flag = nullptr) {
+                                                     const uint32_t* __restrict__ run_flag = nullptr,
+                                                     Relu2Bwd bwd = {}) {
   static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
+  static_assert(BC < 0 || !(MX || SPLIT), "the backward epilogue follows the per-tensor GEMM");
   if constexpr (COND) {
     if (*run_flag == 0) return;
   }
@@ -422,6 +440,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     }
   };
 
+  // BC >= 0: the tile's cached codes [256 x BN], row-major, copied with the
+  // 16-byte global->LDS copies into the ring slot stage KT would have used
+  // (free once iteration KT-2's barrier has shown every wave done with stage
+  // KT-2): issued there, they have the last stage and a half to land, and the
+  // last stage's wait and barrier publish them.  Copy k of wave w moves chunks
+  // 64 (8 k + w) .. +63 (chunk q = row q / (BN/16), 16-byte column q % (BN/16)).
+  auto issue_cache = [&](uint8_t* dst) {
+    if constexpr (BC >= 0) {
+      constexpr int CPR = BN / 16, NCC = BM * CPR / 512;
+#pragma unroll
+      for (int k = 0; k < NCC; ++k) {
+        const int q = (8 * k + wave) * 64 + lane;
+        copy16_to_lds(bwd.cache + (size_t)(m0 + q / CPR) * N + n0 + (q % CPR) * 16,
+                      dst + (8 * k + wave) * 1024);
+      }
+    }
+  };
+  uint8_t* const cache_lds = lds + (KT & 1) * SLOT;
+
   // prologue: stages 0 and 1 in flight, stage 0 landed and published
   issue(0);
   if (KT > 1) {
@@ -452,6 +489,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     stage_barrier();
     // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
     if (kt + 2 < KT) issue(kt + 2);
+    if constexpr (BC >= 0) {
+      if (kt + 2 == KT) issue_cache(cache_lds);
+    }
     if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
     mfmas(fa1, fb1, xa1, xb1);
   }
@@ -468,6 +508,89 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
           const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           out[(size_t)row * N + n0 + wc + j * 32 + (lane & 31)] = acc[i][j][r];
         }
+    return;
+  }
+
+  if constexpr (BC >= 0) {
+    // with a single stage there was no iteration KT-2: copy now (every wave
+    // has passed the stage's barrier after its last fragment reads)
+    if (KT < 2) issue_cache(cache_lds);
+    // 2 sqrt(dec(c) * si) for the 256 codes (threads 0-255, the per-element
+    // operations of relu2_backward_quantize)
+    __shared__ float two_root[256];
+    if (threadIdx.x < 256) {
+      float d;
+      if constexpr (BC == 0) d = __builtin_amdgcn_cvt_pk_f32_fp8((int)threadIdx.x, false)[0];
+      else d = __builtin_amdgcn_cvt_pk_f32_bf8((int)threadIdx.x, false)[0];
+      two_root[threadIdx.x] = __fmul_rn(2.0f, __builtin_sqrtf(__fmul_rn(d, *bwd.cache_si)));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    const float f = sa[0] * sb[0];
+    const float sg = *bwd.scale;
+    const bool odd = lane & 1;
+    const int colp = (lane & 31) & ~1;
+    uint32_t amax16 = 0, sat = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        // per 32 x 32 tile, in three passes so that the LDS reads of its 8
+        // row pairs are in flight together: (1) dA pairs and their cached
+        // codes, (2) the table entries, (3) the gradient codes
+        uint32_t da[8], c2[8];
+        int lrow[8];
+        const int lcol = wc + j * 32 + colp;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // the pair of adjacent columns (col, col+1) of one row, as in the
+          // BF16 epilogue below: dA exactly as fp8_gemm_scaled stores it
+          const int r = 2 * k;
+          const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
+          const float give = odd ? v0 : v1;
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
+                                                 false));
+          da[k] = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
+          lrow[k] = wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
+          c2[k] = *reinterpret_cast<const uint16_t*>(cache_lds + lrow[k] * BN + lcol);
+        }
+        float t0[8], t1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          t0[k] = two_root[c2[k] & 0xFFu];
+          t1[k] = two_root[c2[k] >> 8];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float g0 = __fmul_rn(t0[k], __uint_as_float(da[k] << 16));
+          const float g1 = __fmul_rn(t1[k], __uint_as_float(da[k] & 0xFFFF0000u));
+          const uint32_t m0g = __float_as_uint(g0) & 0x7FFFFFFFu, m1g = __float_as_uint(g1) & 0x7FFFFFFFu;
+          uint32_t b, code;
+          if (m0g <= kF32Inf && m1g <= kF32Inf) {
+            // no NaN: the hardware conversions (the clamp saturates, the
+            // convert rounds to nearest even: the integer codec's codes), and
+            // the saturation count from the scaled values directly
+            b = pack2_bf16_hw(g0, g1);
+            const float q0 = __fmul_rn(__uint_as_float(b << 16), sg);
+            const float q1 = __fmul_rn(__uint_as_float(b & 0xFFFF0000u), sg);
+            code = pack2_hw<BF>(q0, q1);
+            sat += saturates<BF>(q0) + saturates<BF>(q1);
+          } else {
+            b = pack2_bf16_int(g0, g1);
+            const float q0 = __fmul_rn(__uint_as_float(b << 16), sg);
+            const float q1 = __fmul_rn(__uint_as_float(b & 0xFFFF0000u), sg);
+            code = enc_int<BF>(q0) | (enc_int<BF>(q1) << 8);
+            sat += saturates<BF>(q0) + saturates<BF>(q1);
+          }
+          const uint32_t b0 = b & 0x7FFFu, b1 = (b >> 16) & 0x7FFFu;
+          const uint32_t mx = b0 > b1 ? b0 : b1;
+          amax16 = mx > amax16 ? mx : amax16;
+          *reinterpret_cast<uint16_t*>(bwd.out + (size_t)(m0 + lrow[k]) * N + n0 + lcol) =
+              (uint16_t)code;
+        }
+      }
+    block_fold<512>(amax16, sat, bwd.slots);
     return;
   }
 
@@ -522,6 +645,25 @@ static int launch_cond_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64
   if (N % 192 == 0) return launch_cond<FA, FB, 3>(a, b, M, N, K, sa, sb, y, flag, stream);
   if (N % 256 == 0) return launch_cond<FA, FB, 4>(a, b, M, N, K, sa, sb, y, flag, stream);
   return launch_cond<FA, FB, 2>(a, b, M, N, K, sa, sb, y, flag, stream);
+}
+
+template <int BC, int BF, int TN>
+static int launch_bwd_epi(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                          const float* sa, const float* sb, uint16_t* y_unused, Relu2Bwd bwd,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<1, 0, TN, false, false, false, BC, BF>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
+                     (int)M, (int)N, (int)K, sa, sb, y_unused, nullptr, 1, nullptr, nullptr,
+                     nullptr, bwd);
+  return check_launch("fp8_gemm_relu2_backward");
+}
+
+template <int BC, int BF>
+static int launch_bwd_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                           const float* sa, const float* sb, Relu2Bwd bwd, hipStream_t stream) {
+  if (N % 192 == 0) return launch_bwd_epi<BC, BF, 3>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
+  if (N % 256 == 0) return launch_bwd_epi<BC, BF, 4>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
+  return launch_bwd_epi<BC, BF, 2>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
 }
 
 template <int FA, int FB, int TN>
@@ -786,4 +928,53 @@ extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
     return launch_cond_tile<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
   return launch_cond_tile<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+}
+
+extern "C" int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                                       fp8dp_format fb, int64_t M, int64_t N, int64_t K,
+                                       const float* a_scale_inv, const float* b_scale_inv,
+                                       const uint8_t* act_cache, fp8dp_cache cache,
+                                       const float* act_scale_inv, fp8dp_format fmt,
+                                       fp8dp_tensor_state* st, uint8_t* dh_out,
+                                       hipStream_t stream) {
+  if (a == nullptr || b == nullptr || a_scale_inv == nullptr || b_scale_inv == nullptr ||
+      act_cache == nullptr || act_scale_inv == nullptr || st == nullptr || dh_out == nullptr) {
+    set_error("fp8_gemm_relu2_backward: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
+    set_error("fp8_gemm_relu2_backward: M must be a positive multiple of 256, N and K of 128 "
+              "(got %lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
+    return FP8DP_EINVAL;
+  }
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
+      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
+    set_error("fp8_gemm_relu2_backward: shape too large");
+    return FP8DP_EINVAL;
+  }
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
+      (fmt != FP8DP_E4M3 && fmt != FP8DP_E5M2) ||
+      (cache != FP8DP_CACHE_E4M3 && cache != FP8DP_CACHE_E5M2 && cache != FP8DP_CACHE_BF16)) {
+    set_error("fp8_gemm_relu2_backward: unknown format or cache kind");
+    return FP8DP_EINVAL;
+  }
+  if (fa != FP8DP_E5M2 || fb != FP8DP_E4M3 || cache == FP8DP_CACHE_BF16) {
+    set_error("fp8_gemm_relu2_backward: provided for E5M2 gradients x E4M3 weights with an FP8 "
+              "activation cache (the FP8 recipe's dgrad)");
+    return FP8DP_EUNSUPPORTED;
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned16(act_cache) || !aligned16(dh_out) ||
+      !aligned16(st) || (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(act_scale_inv) & 3u)) {
+    set_error("fp8_gemm_relu2_backward: operands, cache, output and state must be 16-byte "
+              "aligned, scales 4-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  const Relu2Bwd bwd{act_cache, act_scale_inv, dh_out, &st->scale, st->acc};
+  if (cache == FP8DP_CACHE_E4M3)
+    return fmt == FP8DP_E5M2 ? launch_bwd_tile<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream)
+                             : launch_bwd_tile<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream);
+  return fmt == FP8DP_E5M2 ? launch_bwd_tile<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream)
+                           : launch_bwd_tile<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream);
 }
