@@ -33,7 +33,8 @@ def test_header_declares_the_named_entry_points():
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
               "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
-              "fp8_gemm_scaled_if", "relu2_backward_quantize", "fp8dp_last_error"):
+              "fp8_gemm_scaled_if", "relu2_backward_quantize", "fp8_gemm_relu2_backward",
+              "fp8dp_last_error"):
         assert n in names
 
 
@@ -164,3 +165,22 @@ def test_relu2_backward_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.relu2_backward_quantize(16, 16, 2, None, 4, 8, 1, 16, None, None, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+
+
+def test_fused_dgrad_argument_checks_reject_without_launching(L):
+    # fp8_gemm_relu2_backward(a, fa, b, fb, M, N, K, sa, sb, cache, kind, sc, fmt, st, out, stream)
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, None, 0, 16, 1, 16, 16,
+                                   None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 128, 128, 128, 16, 16, 16, 0, 16, 1, 16, 16,
+                                   None)
+    assert rc == -1 and b"256" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_relu2_backward(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 0, 16, 1, 16, 16,
+                                   None)
+    assert rc == -2
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, 16, 2, 16, 1, 16, 16,
+                                   None)
+    assert rc == -2
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, 24, 0, 16, 1, 16, 16,
+                                   None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
