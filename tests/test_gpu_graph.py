@@ -1,0 +1,82 @@
+"""The benchmark step captured in a HIP graph (GPU).
+
+Every entry point enqueues kernels on the caller's stream, never allocates
+and never synchronizes, so a whole step -- quantize_fused on H, the FP8 GEMM,
+amax_history_update, the E5M2 cast of dY, its update, and the overflow
+recompute of both casts -- can be captured once and replayed.  Each replay
+is one more step of delayed scaling: the test replays the graph several
+times, with eager work and host synchronizations in between, and checks
+every replay bit for bit against the same steps run eagerly on a second set
+of buffers and states (codes, BF16 copies, GEMM output, both states).
+"""
+import numpy as np
+import pytest
+import torch
+
+import scaled_quantization_amd as sq
+import workloads
+from gpu_util import DEV, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(bufs, recompute=True):
+    h, a16, a8, w8, wsc, y, dy, dy8, st_a, st_g = bufs
+    sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, a16, a8)
+    sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR, st_a.field_ptr("scale_inv"), wsc, y)
+    sq.amax_history_update(st_a)
+    if recompute:
+        sq.quantize_recompute(h, sq.ACT_RELU2, sq.E4M3, st_a, a8)
+        sq.fp8_gemm_scaled_if(a8, sq.E4M3, w8, sq.E4M3, st_a.field_ptr("scale_inv"), wsc, y,
+                              st_a.field_ptr("overflow"))
+    sq.quantize_fused(dy, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, dy8)
+    sq.amax_history_update(st_g)
+    if recompute:
+        sq.quantize_recompute(dy, sq.ACT_IDENTITY, sq.E5M2, st_g, dy8)
+
+
+def _buffers(w, h, dy, wt):
+    M, K, N = w.M, w.K, w.N
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    wsc = torch.empty(2, dtype=torch.float32, device=DEV)
+    sq.quantize_weight(wt, sq.E4M3, sq.PER_TENSOR, w8, wsc)
+    return [h, torch.empty((M, K), dtype=torch.bfloat16, device=DEV),
+            torch.empty((M, K), dtype=torch.uint8, device=DEV), w8, wsc,
+            torch.empty((M, N), dtype=torch.bfloat16, device=DEV), dy,
+            torch.empty((M, N), dtype=torch.uint8, device=DEV),
+            sq.TensorState(sq.E4M3, 1, w.margin, w.initial_amax),
+            sq.TensorState(sq.E5M2, 1, w.margin, w.initial_amax)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2"])
+def test_step_graph_replays_equal_eager_steps(name):
+    w = workloads.get(name)
+    h = to_dev_bf16(w.h0())
+    dy = to_dev_bf16(w.dy())
+    wt = to_dev_bf16(w.weight())
+    g_bufs = _buffers(w, h, dy, wt)
+    e_bufs = _buffers(w, h, dy, wt)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up outside the capture (library load)
+        _step(g_bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    _step(e_bufs)                          # the eager twin runs the same warm-up step
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _step(g_bufs)
+    # capture enqueues nothing: the captured step has not run yet
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        _step(e_bufs)
+        torch.cuda.synchronize()
+        for k in (1, 2, 5, 7):             # a16, a8, y, dy8
+            assert torch.equal(g_bufs[k].view(torch.uint8), e_bufs[k].view(torch.uint8)), (rep, k)
+        for k in (8, 9):                   # every field of both states (not the padding)
+            assert g_bufs[k].read() == e_bufs[k].read(), (rep, k)
+        # eager work between replays
+        torch.cuda.synchronize()
+    assert g_bufs[8].read()["steps"] == 5
