@@ -28,7 +28,10 @@ namespace fp8dp {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kBlocksPerCU = 32;
+// grid caps in workgroups per CU by read/write mix, as for the quantizer:
+// 96 with the BF16 dH copy (writes >= reads), 32 without (3-4 B read, 1 B written)
+constexpr int kBlocksPerCU = 96;
+constexpr int kBlocksPerCURead = 32;
 constexpr int kCacheBf16 = FP8DP_CACHE_BF16;
 
 typedef float v2f_t __attribute__((ext_vector_type(2)));
@@ -186,7 +189,7 @@ int launch_bwd(const uint16_t* dA, const void* cache, const float* a_si, uint16_
                uint8_t* qout, int64_t n, fp8dp_tensor_state* st, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, kBlocksPerCU);
+  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
   if (codec() == 0)
     hipLaunchKernelGGL((k_relu2_bwd<CACHE, FMT, WBF16, true>), dim3(grid), dim3(kThreads), 0,
                        stream, reinterpret_cast<const uint4*>(dA), cache, a_si,

@@ -31,7 +31,14 @@ namespace fp8dp {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
-constexpr int kBlocksPerCU = 32;   // grid of the element-wise kernels
+// Grid caps of the element-wise kernels, in workgroups per CU, by their
+// read/write mix (measured at the GPT-2 shapes): kernels that write at least
+// as many bytes as they read stream faster with more workgroups queued (the
+// quantizer with its BF16 copy, 2 B read / 3 B written: +6% at 96 against
+// 32; the copy +11%), read-heavy ones with fewer (the cast without the copy,
+// 2 B / 1 B: -14% at 96).
+constexpr int kBlocksPerCU = 96;      // writes >= reads
+constexpr int kBlocksPerCURead = 32;  // reads > writes
 
 
 // ------------------------------------------------------------------ per tensor
@@ -463,7 +470,7 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
                          const float* scale_ptr, fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, kBlocksPerCU);
+  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
@@ -493,7 +500,7 @@ template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC>
 static int launch_group(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout, float* gsi,
                         fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  const unsigned grid = grid_for(n8, kThreads, kBlocksPerCU);
+  const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
@@ -530,7 +537,7 @@ template <int FMT, int ACT, bool WBF16>
 static int launch_mx_quant(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout,
                            uint8_t* e8, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  const unsigned grid = grid_for(n8, kThreads, kBlocksPerCU);
+  const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
   if (codec() == 0)
     hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true>), dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
