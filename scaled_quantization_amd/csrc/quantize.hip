@@ -262,10 +262,21 @@ __global__ void k_state_init(fp8dp_tensor_state* st, int fmt, int hist_len, floa
   }
 }
 
+// One wave: lane l reduces accumulator slot l and holds history entry l.
+// Every load is issued before any use (one memory round trip instead of a
+// chain of dependent ones); the ring after this step's write -- entry pos
+// replaced by the step's amax -- is reduced in registers.
 __global__ void k_history_update(fp8dp_tensor_state* st) {
-  const int l = threadIdx.x;  // 64 threads, one per accumulator slot
+  const int l = threadIdx.x;  // 64 threads
   uint32_t m = st->acc[l].amax;
   uint64_t c = st->acc[l].sat;
+  const float h = l < FP8DP_MAX_HIST ? st->history[l] : 0.0f;
+  const int len = st->hist_len;
+  const int pos = st->hist_pos;
+  const float margin = st->margin;
+  const int fmt = st->fmt;
+  const float sinv = st->scale_inv;
+  const uint32_t steps = st->steps;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const uint32_t om = __shfl_xor(m, off);
@@ -274,28 +285,26 @@ __global__ void k_history_update(fp8dp_tensor_state* st) {
     const uint32_t chi = __shfl_xor((uint32_t)(c >> 32), off);
     c += ((uint64_t)chi << 32) | clo;
   }
+  const float amax_t = __uint_as_float(m);
+  uint32_t hm = l < len ? (__float_as_uint(l == pos ? amax_t : h) & 0x7FFFFFFFu) : 0u;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(hm, off);
+    hm = o > hm ? o : hm;
+  }
   st->acc[l].amax = 0;
   st->acc[l].sat = 0;
   if (l == 0) {
-    const float amax_t = __uint_as_float(m);
-    const int len = st->hist_len;
-    int pos = st->hist_pos;
     st->history[pos] = amax_t;
-    pos += 1;
-    st->hist_pos = (pos == len) ? 0 : pos;
-    uint32_t hm = 0;
-    for (int i = 0; i < len; ++i) {
-      const uint32_t hb = __float_as_uint(st->history[i]) & 0x7FFFFFFFu;
-      hm = hb > hm ? hb : hm;
-    }
-    st->scale_inv_used = st->scale_inv;
-    const float s = scale_rule(__uint_as_float(hm), st->margin, st->fmt == 0 ? 448.0f : 57344.0f);
+    st->hist_pos = (pos + 1 == len) ? 0 : pos + 1;
+    st->scale_inv_used = sinv;
+    const float s = scale_rule(__uint_as_float(hm), margin, fmt == 0 ? 448.0f : 57344.0f);
     st->scale = s;
     st->scale_inv = recip_rn(s);
     st->sat_last = c;
     st->overflow = c > 0 ? 1u : 0u;
     st->amax_last = amax_t;
-    st->steps += 1;
+    st->steps = steps + 1;
   }
 }
 

@@ -151,6 +151,31 @@ def test_gpt2_two_delayed_steps_full_size():
         _compare_state(st, ost)
 
 
+@pytest.mark.parametrize("hist_len", [2, 4, 16])
+def test_history_window_sequence(hist_len):
+    """Delayed scaling with a window of hist_len steps ("FP8 training: what it
+    is and how it works", Trade-offs: a stored amax history): 40 steps whose
+    amax rises, falls and jumps, state compared field by field with the
+    oracle after every update."""
+    rng = np.random.default_rng(hist_len)
+    levels = np.concatenate([np.geomspace(0.5, 300.0, 12), np.geomspace(300.0, 0.01, 12),
+                             [5.0, 5000.0, 5.0, 0.0, 7.0], rng.uniform(0.1, 50.0, 11)])
+    st = sq.TensorState(sq.E4M3, hist_len, 1.25, 1.0)
+    ost = O.State(O.E4M3, hist_len, 1.25, 1.0)
+    q = torch.empty((4, 64), dtype=torch.uint8, device=DEV)
+    for t, lv in enumerate(levels):
+        x = (rng.standard_normal((4, 64)) * lv).astype(np.float32)
+        h = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        sq.quantize_fused(to_dev_bf16(h), sq.ACT_IDENTITY, sq.E4M3, sq.PER_TENSOR, st, None, q)
+        r = O.quantize(h, O.ACT_IDENTITY, O.E4M3, O.PER_TENSOR, ost.scale, want_bf16=False)
+        assert np.array_equal(u8_np(q), r.fp8), t
+        sq.amax_history_update(st)
+        ost.accumulate(r.amax_bits, r.sat)
+        ost.update()
+        _compare_state(st, ost)
+        assert st.read()["amax_last"] == np.float32(r.amax), t
+
+
 def test_outlier_stress_65_steps():
     w = workloads.get("outlier")
     st = sq.TensorState(sq.E4M3, 1, w.margin, w.initial_amax)
