@@ -28,9 +28,10 @@ namespace fp8dp {
 
 namespace {
 constexpr int kThreads = 256;
-// grid caps in workgroups per CU by read/write mix, as for the quantizer:
-// 96 with the BF16 dH copy (writes >= reads), 32 without (3-4 B read, 1 B written)
-constexpr int kBlocksPerCU = 96;
+// grid by read/write mix, as for the quantizer: one vector per thread with
+// the BF16 dH copy (writes >= reads), 32 workgroups per CU looping without it
+// (3-4 B read, 1 B written)
+constexpr int kBlocksPerCU = 1 << 20;
 constexpr int kBlocksPerCURead = 32;
 constexpr int kCacheBf16 = FP8DP_CACHE_BF16;
 

@@ -39,6 +39,7 @@ inline int check_launch(const char* what) {
 inline unsigned grid_for(int64_t work_items, int block_threads, int blocks_per_cu) {
   int64_t need = (work_items + block_threads - 1) / block_threads;
   int64_t cap = (int64_t)num_cus() * blocks_per_cu;
+  if (cap > ((int64_t)1 << 30)) cap = (int64_t)1 << 30;   // grid-stride loops cover the rest
   int32_t lim = grid_limit();
   if (lim > 0 && cap > lim) cap = lim;
   if (need > cap) need = cap;

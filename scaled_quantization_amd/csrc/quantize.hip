@@ -31,14 +31,15 @@ namespace fp8dp {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
-// Grid caps of the element-wise kernels, in workgroups per CU, by their
-// read/write mix (measured at the GPT-2 shapes): kernels that write at least
-// as many bytes as they read stream faster with more workgroups queued (the
-// quantizer with its BF16 copy, 2 B read / 3 B written: +6% at 96 against
-// 32; the copy +11%), read-heavy ones with fewer (the cast without the copy,
-// 2 B / 1 B: -14% at 96).
-constexpr int kBlocksPerCU = 96;      // writes >= reads
-constexpr int kBlocksPerCURead = 32;  // reads > writes
+// Grid of the element-wise kernels, by their read/write mix (measured):
+// kernels that write at least as many bytes as they read stream fastest with
+// one 8-element vector per thread and no grid-stride loop (the quantizer with
+// its BF16 copy, 2 B read / 3 B written: 6.4 TB/s at 0.5 and 2 GiB against
+// 4.9 with 32 workgroups per CU looping); read-heavy ones with 32 workgroups
+// per CU looping (the cast without the copy, 2 B / 1 B: 14% slower with one
+// vector per thread).
+constexpr int kBlocksPerCU = 1 << 20;  // writes >= reads: no cap below one vector per thread
+constexpr int kBlocksPerCURead = 32;   // reads > writes
 
 
 // ------------------------------------------------------------------ per tensor
