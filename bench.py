@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-naive", action="store_true")
     p.add_argument("--only", choices=("quantize", "gemm", "copy", "quantize_mx", "gemm_mx",
-                                      "relu2_bwd"), default=None,
+                                      "relu2_bwd", "gemm_pg"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
                         "inputs (for hardware counter runs), then exit")
     return p.parse_args()
@@ -229,6 +229,7 @@ def main():
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
     out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
+    out["per_group_128"] = per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["fp8_cached_activation"] = fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args,
                                               q_mean)
     out["graph_step"] = graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8, st_a, st_g, args,
@@ -258,6 +259,14 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
         sq.quantize_mx(wt, sq.ACT_IDENTITY, sq.E4M3, wm8, we)
         for j in range(n_out):
             sq.quantize_mx(H[j % n_in], sq.ACT_RELU2, sq.E4M3, A8[j], E[j])
+    if args.only == "gemm_pg":
+        GS = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(n_out)]
+        wg8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        wgs = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+        sq.quantize_weight(wt, sq.E4M3, sq.PER_GROUP128, wg8, wgs)
+        for j in range(n_out):
+            sq.quantize_fused(H[j % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, None, None,
+                              A8[j], GS[j])
     if args.only == "relu2_bwd":
         dA = torch.from_numpy(w.da().view(np.int16)).to(dev).view(torch.bfloat16)
         dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
@@ -271,6 +280,9 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
         if args.only == "quantize_mx":
             sq.quantize_mx(H[i % n_in], sq.ACT_RELU2, sq.E4M3, A8[i % n_out], E[i % n_out],
                            A16[i % n_out])
+        elif args.only == "gemm_pg":
+            sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, wg8, sq.E4M3, sq.PER_GROUP128,
+                               GS[i % n_out], wgs, Y)
         elif args.only == "gemm_mx":
             sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], wm8, sq.E4M3, we, Y)
         elif args.only == "relu2_bwd":
@@ -488,6 +500,50 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
             "fp8_gemm_mx": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
+
+
+def per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
+    """The per-128 mode of the same forward half: quantize_fused with current
+    per-group scales (relu2, BF16 copy, E4M3 codes + one FP32 inverse scale
+    per 1 x 128 group), the weight cast with 128 x 128 block scales, and the
+    GEMM that promotes every 128-wide partial sum by sa[m, g] sb[n / 128, g].
+    Timed like the per-tensor kernels (back-to-back launches between two
+    events)."""
+    M, K, N = w.M, w.K, w.N
+    stream = torch.cuda.current_stream()
+    n_in, n_out = len(H), len(A16)
+    GS = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(n_out)]
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    sq.quantize_weight(wt, sq.E4M3, sq.PER_GROUP128, w8, ws)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    q = timed(lambda i: sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128,
+                                          None, A16[i % n_out], A8[i % n_out], GS[i % n_out]))
+    g = timed(lambda i: sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_GROUP128,
+                                           GS[i % n_out], ws, Y))
+    q_bytes = M * K * (2 + 2 + 1) + M * (K // 128) * 4
+    flops = w.gemm_flops()
+    tf = flops / (g * 1e-3) / 1e12
+    return {"quantize_fused_per_group": {"ms": round(q, 5),
+                                         "GB/s": round(q_bytes / (q * 1e-3) / 1e9, 1),
+                                         "bytes_per_launch": q_bytes,
+                                         "vs_per_tensor_quantize": round(q_tensor_ms / q, 3)},
+            "fp8_gemm_scaled_per_group": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
+                                          "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                                          "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
 
 
 def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):

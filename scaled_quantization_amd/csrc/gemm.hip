@@ -256,9 +256,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // LDS read waits in front of the MFMA pipe.
 // The epilogue pairs adjacent output columns between neighbour lanes (one DPP
 // swap) and stores BF16 pairs straight to Y.
-// Per-128-group scales stay on the small-tile kernel: promoting a partial sum
-// per stage in this kernel (256 x 128 tiles) was slower than it, because the
-// promotion's vector work lands on both waves of a SIMD at the same time.
+// PG (per-128-group scales, 256 x 128 tiles): one stage is one 128-wide
+// group of k, so each stage's two substeps accumulate a partial sum that is
+// then promoted, acc += part * (sa[m, g] * sb[n / 128, g]) -- the small-tile
+// kernel's arithmetic.  The tiles are computed transposed (B fragment first),
+// which leaves one scale product per lane and fragment row instead of one per
+// element: with the A rows in the registers the promotion cost a product per
+// element and was slower than the small-tile kernel.
 // Measured alternatives (GPT-2 shape, same tile): no half-stage pipelining
 // (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
 // deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
@@ -276,6 +280,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // (lane / 32 selects the half), which is exactly one block: the MFMA applies
 // 2^(ea - 127) 2^(eb - 127) to each block's products, and the epilogue has
 // no scale to apply.
+// XG = 4 (K a multiple of 512, exponent arrays 16-byte aligned): a lane's
+// 4-byte exponent copy touches a row of its own, so per stage it costs as
+// many cache-line requests as all the tile copies of its wave together;
+// instead one 16-byte copy per row carries 4 stages' exponents, issued with
+// the tiles of every fourth stage into a two-slot exponent ring (slot g % 2
+// for stages 4g .. 4g+3).  Group g is issued with stage 4g, two stages before
+// its first read, and its slot was last read by stage 4g - 5.
 // The squared ReLU's backward applied in the epilogue (BC >= 0): the GEMM's
 // output is dA, and each element leaves as the gradient code
 //   code = sat_rne(bf16(two_root[c] * bf16(dA)) * scale),
@@ -293,7 +304,7 @@ struct Relu2Bwd {
 // COND: the launch does nothing unless *run_flag != 0 (a device-side flag,
 // e.g. the overflow mark of a scaling state), read once by every workgroup.
 template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false, int BC = -1,
-          int BF = 1>
+          int BF = 1, int XG = 1, bool PG = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
@@ -311,10 +322,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   }
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
-  constexpr int SLOT = TILES + (MX ? 2048 : 0);             // + 256 A and 256 B exponent dwords
+  static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
+  static_assert(!PG || (TN == 2 && XG == 4 && !MX && !SPLIT && BC < 0),
+                "per-group scales: 256 x 128 tiles, scales through the ring");
+  constexpr bool XR = (MX || PG) && XG == 4;                // exponents / scales in their own ring
+  constexpr int SLOT = TILES + (MX && !XR ? 2048 : 0);      // + 256 A and 256 B exponent dwords
+  constexpr int XSZ = XR ? 8192 : 0;                        // 512 rows x 16 bytes (4 stages)
   constexpr int LA = BM / 64, LB = BN / 64;                 // tile copies per wave per stage
-  constexpr int NCOPY = LA + LB + (MX ? 1 : 0);             // copies per wave per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+  constexpr int NCOPY = LA + LB + (MX && !XR ? 1 : 0);      // copies of a stage with no exponents
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT + 2 * XSZ];
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
@@ -346,12 +362,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   const size_t rstep = (size_t)64 * K;
   // exponent dwords: wave w < 4 fetches A row 64 w + lane, wave w >= 4 B row
   // 64 (w - 4) + lane (clamped into the tile; the surplus dwords are unused)
+  // PG: the same copies move the FP32 group scales, whose rows (K / 128
+  // floats) are as long as the exponent rows: A row 64 w + lane, and for
+  // waves 4-7 the tile's one row of B block scales
   const uint8_t* gE = nullptr;
-  if constexpr (MX) {
+  if constexpr (MX || PG) {
     const int r = (wave & 3) * 64 + lane;
     const size_t kb = (size_t)K / 32;
-    gE = wave < 4 ? ea + (size_t)(m0 + r) * kb + kbase / 32
-                  : eb + (size_t)(n0 + (r < BN ? r : BN - 1)) * kb + kbase / 32;
+    if constexpr (PG)
+      gE = wave < 4 ? reinterpret_cast<const uint8_t*>(sa) + (size_t)(m0 + r) * kb
+                    : reinterpret_cast<const uint8_t*>(sb) + (size_t)(n0 / 128) * kb;
+    else
+      gE = wave < 4 ? ea + (size_t)(m0 + r) * kb + kbase / 32
+                    : eb + (size_t)(n0 + (r < BN ? r : BN - 1)) * kb + kbase / 32;
   }
   auto issue = [&](int kt) {
     uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
@@ -360,7 +383,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
 #pragma unroll
     for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
-    if constexpr (MX) copy4_to_lds(gE + kt * 4, lds + (kt & 1) * SLOT + TILES + wave * 256);
+    if constexpr (XR) {
+      if ((kt & 3) == 0)
+        copy16_to_lds(gE + kt * 4, lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ + wave * 1024);
+    } else if constexpr (MX) {
+      copy4_to_lds(gE + kt * 4, lds + (kt & 1) * SLOT + TILES + wave * 256);
+    }
   };
 
   // this lane's fragment rows: A rows wr + 32 t + lane % 32, B rows wc + 32 t + lane % 32.
@@ -377,23 +405,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     const uint8_t* sA = lds + (kt & 1) * SLOT;
     const uint8_t* sB = sA + ASZ;
     const int c0 = h * 4 + fhalf;
-    if constexpr (MX) {
-      // the exponents of this substep packed one per byte (fragment t in
-      // byte t, picked by the instruction's byte select): one register for
-      // A and one for B instead of one per fragment
-      const uint32_t* sE = reinterpret_cast<const uint32_t*>(sA + TILES);
-      const uint32_t bsel = 2 * h + fhalf;                       // byte of the row dword
-      const uint32_t pair = bsel | ((bsel + 4) << 8) | 0x0C0C0000u;   // -> bytes 0, 1; 0s above
-      xa[0] = __builtin_amdgcn_perm(sE[wr + 32 + frow], sE[wr + frow], pair);
-      const uint32_t* sEb = sE + 256 + wc + frow;
-      const uint32_t b01 = __builtin_amdgcn_perm(sEb[32], sEb[0], pair);
-      if constexpr (TN == 2) {
-        xb[0] = b01;
-      } else if constexpr (TN == 3) {
-        xb[0] = __builtin_amdgcn_perm(sEb[64], b01, 0x0C000100u | ((bsel + 4) << 16));
+    if constexpr (MX || PG) {
+      // the row dwords of this lane's fragments (packed just before the
+      // MFMAs that use them, so that no wait on these reads sits in front of
+      // the MFMAs in between)
+      if constexpr (XR) {
+        // row r's 16 bytes at 16 r (B rows from 256 on); stage kt's dword is the (kt % 4)-th
+        const uint32_t* sE =
+            reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) xa[t] = sE[4 * (wr + 32 * t + frow)];
+        if constexpr (PG) {
+          xb[0] = sE[4 * 256];             // the tile's B block scale
+        } else {
+#pragma unroll
+          for (int t = 0; t < TN; ++t) xb[t] = sE[4 * (256 + wc + 32 * t + frow)];
+        }
       } else {
-        const uint32_t b23 = __builtin_amdgcn_perm(sEb[96], sEb[64], pair);
-        xb[0] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+        const uint32_t* sE = reinterpret_cast<const uint32_t*>(sA + TILES);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) xa[t] = sE[wr + 32 * t + frow];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) xb[t] = sE[256 + wc + 32 * t + frow];
       }
     }
 #pragma unroll
@@ -419,17 +452,66 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // PG: the stage's partial sums (one stage = one 128-wide group), computed
+  // transposed: the B fragment is the instruction's first operand, so a
+  // lane holds one A row (its column lane % 32) and its 16 registers hold B
+  // rows of one 128-wide B block.  The promotion then needs one product of
+  // scales per lane and fragment row (sa[m] sb), not one per element.
+  v16f_t part[PG ? TM : 1][PG ? TN : 1];
   // Without MX the scale operands are the constant 0, which the compiler
   // lowers to the unscaled instruction (checked in the generated assembly).
-  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa, const uint32_t* xb) {
+  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* ra, const uint32_t* rb,
+                   int h) {
     if constexpr (MX) {
+      // the exponents of substep h packed one per byte (fragment t in byte t,
+      // picked by the instruction's byte select): byte 2 h + lane / 32 of each
+      // row dword
+      const uint32_t bsel = 2 * h + fhalf;
+      const uint32_t pair = bsel | ((bsel + 4) << 8) | 0x0C0C0000u;   // -> bytes 0, 1; 0s above
+      const uint32_t xa = __builtin_amdgcn_perm(ra[1], ra[0], pair);
+      const uint32_t b01 = __builtin_amdgcn_perm(rb[1], rb[0], pair);
+      uint32_t xb;
+      if constexpr (TN == 2) {
+        xb = b01;
+      } else if constexpr (TN == 3) {
+        xb = __builtin_amdgcn_perm(rb[2], b01, 0x0C000100u | ((bsel + 4) << 16));
+      } else {
+        const uint32_t b23 = __builtin_amdgcn_perm(rb[3], rb[2], pair);
+        xb = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+      }
       static_for<TM>([&](auto I) {
         static_for<TN>([&](auto J) {
           acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[I], fb[J], acc[I][J], FA, FB, decltype(I)::value, (int)xa[0],
-              decltype(J)::value, (int)xb[0]);
+              fa[I], fb[J], acc[I][J], FA, FB, decltype(I)::value, (int)xa,
+              decltype(J)::value, (int)xb);
         });
       });
+    } else if constexpr (PG) {
+      if (h == 0) {
+        const v16f_t zero = {};
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], zero, FB,
+                                                                        FA, 0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], part[i][j],
+                                                                        FB, FA, 0, 0, 0, 0);
+        // promote with the group's scales: sa of this lane's A row, sb of the tile
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const float c = __uint_as_float(ra[i]) * __uint_as_float(rb[0]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[i][j][r], c, acc[i][j][r]);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -469,19 +551,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   }
   stage_barrier();
   v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  uint32_t xa0[1], xb0[1], xa1[1], xb1[1];   // MX: packed block exponents
+  uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
   load_frags(0, 0, fa0, fb0, xa0, xb0);
   for (int kt = 0; kt < KT; ++kt) {
+    if constexpr (PG) {
+      // the reads of substep 0 were issued a half stage ago: wait for them
+      // here, before the reads below (else the wait covers those as well)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // first half: read substep 1 of stage kt, multiply substep 0
     load_frags(kt, 1, fa1, fb1, xa1, xb1);
-    mfmas(fa0, fb0, xa0, xb0);
-    if constexpr (MX) {
+    mfmas(fa0, fb0, xa0, xb0, 0);
+    if constexpr (MX || PG) {
       // keep these products in the first half: without a use here the
       // compiler sinks them past the barrier (they only feed later ones)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (PG) asm volatile("" : "+v"(part[i][j]));
+          else asm volatile("" : "+v"(acc[i][j]));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
@@ -493,7 +584,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       if (kt + 2 == KT) issue_cache(cache_lds);
     }
     if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
-    mfmas(fa1, fb1, xa1, xb1);
+    mfmas(fa1, fb1, xa1, xb1, 1);
   }
 
   if constexpr (SPLIT) {
@@ -594,6 +685,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     return;
   }
 
+  if constexpr (PG) {
+    // transposed tiles: register r of lane l holds y[m][n] for A row
+    // m = wr + 32 i + l % 32 and B row n = wc + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4,
+    // so registers 4q .. 4q+3 are 4 adjacent outputs of one row: one 8-byte store
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = m0 + wr + i * 32 + (lane & 31);
+          const int col = n0 + wc + j * 32 + q * 8 + (lane >> 5) * 4;
+          const uint2 v = {pack2_bf16_hw(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                           pack2_bf16_hw(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<uint2*>(Y + (size_t)row * N + col) = v;
+        }
+    return;
+  }
+
   // epilogue: scale, round to BF16 and store pairs of adjacent columns.  In a
   // 32 x 32 MFMA tile the lane holds column lane % 32 and register r holds row
   // 8 (r / 4) + 4 (lane / 32) + r % 4; swapping one value with the neighbour
@@ -625,6 +735,15 @@ static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
                       const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
   hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
                      dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
+  return check_launch("fp8_gemm_scaled");
+}
+
+template <int FA, int FB>
+static int launch_pg(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                     const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, 2, false, false, false, -1, 1, 4, true>),
+                     dim3((unsigned)((M / 256) * (N / 128))), dim3(512), 0, stream, a, b, (int)M,
+                     (int)N, (int)K, sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
 }
 
@@ -669,9 +788,14 @@ static int launch_bwd_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_
 template <int FA, int FB, int TN>
 static int launch_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true>),
-                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
-                     (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea, eb);
+  const dim3 grid((unsigned)((M / 256) * (N / (64 * TN))));
+  if (K % 512 == 0 && aligned16(ea) && aligned16(eb))
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true, false, -1, 1, 4>), grid, dim3(512), 0,
+                       stream, a, b, (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea,
+                       eb);
+  else
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true>), grid, dim3(512), 0, stream, a, b,
+                       (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea, eb);
   return check_launch("fp8_gemm_mx");
 }
 
@@ -754,6 +878,9 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
     if (N % 256 == 0) return launch_big<FA, FB, 4>(a, b, M, N, K, sa, sb, y, stream);
     return launch_big<FA, FB, 2>(a, b, M, N, K, sa, sb, y, stream);
   }
+  if (mode == FP8DP_PER_GROUP128 && !exact && M % 256 == 0 && K % 512 == 0 && aligned16(sa) &&
+      aligned16(sb))
+    return launch_pg<FA, FB>(a, b, M, N, K, sa, sb, y, stream);
   if (mode == FP8DP_PER_TENSOR) {
     if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);
     else launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a, b, M, N, K, sa, sb, y, stream);

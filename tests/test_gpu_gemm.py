@@ -252,13 +252,7 @@ def test_large_tile_paths(M, N, K):
     _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
 
 
-@pytest.mark.parametrize("M,N,K,fa,fb", [(256, 128, 128, 0, 0), (512, 384, 256, 0, 0),
-                                         (768, 640, 1280, 0, 1), (2304, 1024, 384, 1, 0),
-                                         (1024, 256, 640, 1, 1)])
-def test_group_scaled_shapes(M, N, K, fa, fb):
-    # per-group FP8: per-stage partial sums promoted by sa[m, g] sb[n / 128, g]
-    # over 1, 2, 3, 5 and 10 stages, tile counts on and off the renumbering's
-    # multiple of 8, every format pair, scales that are not powers of two
+def _group_case(M, N, K, fa, fb):
     rng = np.random.default_rng(M * 7 + N + K)
     ta = O.fp8_decode_table(fa)
     tb = O.fp8_decode_table(fb)
@@ -268,9 +262,55 @@ def test_group_scaled_shapes(M, N, K, fa, fb):
     w8 = rng.choice(near_b, size=(N, K)).astype(np.uint8)
     sa = rng.uniform(0.05, 40.0, (M, K // 128)).astype(np.float32)
     sb = rng.uniform(0.05, 40.0, (N // 128, K // 128)).astype(np.float32)
+    return a8, w8, sa, sb
+
+
+# K = 128 .. 1280 not multiples of 512 (and M = 1024 with 768 not): the 128 x 128
+# tile kernel; K = 512, 1536, 2048, 4096 with M a multiple of 256: the 256 x 128
+# tile kernel with transposed partial sums and the scales' four-stage ring
+@pytest.mark.parametrize("M,N,K,fa,fb", [(256, 128, 128, 0, 0), (512, 384, 256, 0, 0),
+                                         (768, 640, 1280, 0, 1), (2304, 1024, 384, 1, 0),
+                                         (1024, 256, 640, 1, 1), (256, 128, 512, 0, 0),
+                                         (768, 384, 1536, 0, 1), (512, 640, 2048, 1, 0),
+                                         (2304, 256, 4096, 1, 1)])
+def test_group_scaled_shapes(M, N, K, fa, fb):
+    # per-group FP8: per-stage partial sums promoted by sa[m, g] sb[n / 128, g]
+    # over 1 to 32 stages, tile counts on and off the renumbering's multiple
+    # of 8, every format pair, scales that are not powers of two
+    a8, w8, sa, sb = _group_case(M, N, K, fa, fb)
     y = _gemm(a8, fa, w8, fb, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 48)), [M - 1]]))
     ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
     allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows)
     _check(y[rows], ref, absref, f"group {M}x{N}x{K} fa={fa} fb={fb}", allow,
            max_plain_violation_frac=1e-3)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 384, 2048), (256, 256, 512)])
+def test_group_scaled_kernels_agree(M, N, K):
+    """Scale arrays 4 bytes off 16-byte alignment send a K % 512 == 0 problem
+    to the 128 x 128 tile kernel instead of the ring kernel: both meet the
+    bound, and they differ at most by the FP8 instructions' truncation (the
+    two order a stage's k values differently inside the instruction)."""
+    a8, w8, sa, sb = _group_case(M, N, K, 0, 0)
+    y = _gemm(a8, 0, w8, 0, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
+
+    def off4(x):
+        x = np.ascontiguousarray(x, np.float32)
+        buf = torch.zeros(x.size + 4, dtype=torch.float32, device=DEV)
+        v = buf[1:1 + x.size].view(x.shape)
+        v.copy_(torch.from_numpy(x).to(DEV))
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(w8), 0, sq.PER_GROUP128, off4(1 / sa),
+                       off4(1 / sb), y2, FP8)
+    y2 = y2.float().cpu().numpy()
+    rows = np.arange(M)
+    ref, absref = O.gemm_f64(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows=rows)
+    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows)
+    for got, what in ((y, "ring kernel"), (y2, "small-tile kernel")):
+        _check(got, ref, absref, what, allow, max_plain_violation_frac=1e-3)
+    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
+    assert np.all(np.abs(y.astype(np.float64) - y2) <= 2 * (bound + allow))

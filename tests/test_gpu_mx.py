@@ -186,6 +186,33 @@ def test_gemm_mx_vs_oracle(M, N, K, fa, fb):
     _check(y[rows], ref, absref, allow, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 384, 1536), (256, 256, 512)])
+def test_gemm_mx_exponent_copy_paths_agree(M, N, K):
+    """With K a multiple of 512 and 16-byte aligned exponent arrays the kernel
+    copies four stages' exponents per row at once; exponent arrays 4 bytes off
+    that alignment take the per-stage copies.  Both read the same bytes, so the
+    outputs are equal bit for bit, and both match the oracle."""
+    rng = np.random.default_rng(K + N)
+    a8, ea, b8, eb = _gemm_case(rng, M, N, K, 0, 0)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y)
+
+    def off4(x):
+        buf = torch.zeros(x.size + 16, dtype=torch.uint8, device=DEV)
+        v = buf[4:4 + x.size].view(x.shape)
+        v.copy_(torch.from_numpy(np.ascontiguousarray(x)).to(DEV))
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    y2 = torch.empty_like(y)
+    sq.fp8_gemm_mx(to_dev_u8(a8), 0, off4(ea), to_dev_u8(b8), 0, off4(eb), y2)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rows = np.unique(np.concatenate([np.arange(0, M, 16), [M - 1]]))
+    ref, absref = O.gemm_mx_f64(a8, 0, ea, b8, 0, eb, rows)
+    allow = fp8_mfma_allowance_mx(a8, 0, ea, b8, 0, eb, rows)
+    _check(y.float().cpu().numpy()[rows], ref, absref, allow, f"{M}x{N}x{K}")
+
+
 def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
     """Exponent bytes 127 + i (A) and 127 + j (B) everywhere equal per-tensor
     scales 2^i, 2^j: the MX GEMM then matches fp8_gemm_scaled bit for bit."""
