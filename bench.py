@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BURST_WARM_MS = 8.0           # GPU time of a kernel's own launches before its timed bursts
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 METRIC = "fused FP8 quantize GB/s (% HBM peak); FP8 down-proj GEMM TFLOPS (% peak)"
 
@@ -143,15 +144,24 @@ def main():
     # step's own rotation of inputs and outputs, between two events on the
     # launch stream: the mean is the average launch duration, the figure a
     # kernel trace reports for the same launches.
-    # The kernel first runs --warmup launches of its own (the GPU's clocks
-    # settle over a few bursts after the mixed step); then 5 bursts of --steps
-    # launches are timed and the median burst's mean is reported (all five
-    # are listed in the JSON line).
+    # The kernel first runs launches of its own for at least BURST_WARM_MS of
+    # GPU time (at least --warmup launches): under a new sustained load the
+    # GPU's clock takes about 5 ms to settle, and until then the same launches
+    # run 3-10% longer.  Then 5 bursts of --steps launches are timed and the
+    # median burst's mean is reported (all five are listed in the JSON line).
     bursts = {}
 
     def burst(fn, name=None):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
         for i in range(args.warmup):
             fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        est = a.elapsed_time(b) / max(args.warmup, 1)
+        for i in range(min(4096, int(BURST_WARM_MS / max(est, 1e-3)))):
+            fn(args.warmup + i)
         per = []
         for rep in range(5):
             a, b = ev(), ev()
@@ -217,6 +227,7 @@ def main():
                           "frac": round(g_tflops / FP8_PEAK_TFLOPS, 4),
                           "traffic": measured_traffic("fp8_gemm_scaled_gpt2", "gemm.hip")},
         "burst_ms": bursts,
+        "burst_warmup_ms": BURST_WARM_MS,
         "last_step": {"scale": st_read["scale"], "amax": st_read["amax_last"],
                       "saturated": st_read["sat_last"]},
         "wall_s_timed": round(wall, 3),
