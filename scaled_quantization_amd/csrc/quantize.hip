@@ -46,8 +46,9 @@ constexpr int kBlocksPerCURead = 32;   // reads > writes
 // h/bout/qout are viewed as vectors of 8 elements (n8 of them); the last
 // `tail` elements (n % 8) are handled by thread 0 of block 0 with the scalar
 // routine.  scale_ptr: the multiplier (read once); slots: accumulators or
-// nullptr.
-template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW>
+// nullptr.  ONE: the grid has a thread for every vector (gridDim.x * kThreads
+// >= n8), so each thread loads its one vector first thing, with no loop.
+template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW, bool ONE = false>
 __global__ __launch_bounds__(kThreads) void k_quant_tensor(
     const uint4* __restrict__ h, uint4* __restrict__ bout, uint2* __restrict__ qout, int64_t n8,
     int tail, const float* __restrict__ scale_ptr, fp8dp_acc_slot* __restrict__ slots) {
@@ -63,17 +64,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(
     if constexpr (AMAX) amax16 = mx > amax16 ? mx : amax16;
     if constexpr (CAST) store_nt(qout + i, cast8<FMT, HW>(b, mx, s, sat));
   };
-  // kUnroll grid-strided vectors per iteration, all loads issued first: more
-  // bytes in flight per thread to cover HBM latency
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
-    uint4 x[kUnroll];
+  if constexpr (ONE) {
+    if (i < n8) one(load_nt(h + i), i);
+  } else {
+    // kUnroll grid-strided vectors per iteration, all loads issued first: more
+    // bytes in flight per thread to cover HBM latency
+    for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
+      uint4 x[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) x[u] = load_nt(h + i + u * stride);
+      for (int u = 0; u < kUnroll; ++u) x[u] = load_nt(h + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) one(x[u], i + u * stride);
+      for (int u = 0; u < kUnroll; ++u) one(x[u], i + u * stride);
+    }
+    for (; i < n8; i += stride) one(load_nt(h + i), i);
   }
-  for (; i < n8; i += stride) one(load_nt(h + i), i);
   if (tail && blockIdx.x == 0 && threadIdx.x == 0) {
     const uint16_t* ht = reinterpret_cast<const uint16_t*>(h + n8);
     for (int t = 0; t < tail; ++t) {
@@ -108,7 +113,7 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
 // Each group of 128 elements is 16 vectors, handled by the 16 lanes of one
 // DPP row (the grid stride is a multiple of 16 and n8 % 16 == 0, so a row is
 // active or inactive as a whole).  Current scaling: s_g = max / amax_g.
-template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC, bool HW>
+template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC, bool HW, bool ONE = false>
 __global__ __launch_bounds__(kThreads) void k_quant_group(
     const uint4* __restrict__ h, uint4* __restrict__ bout, uint2* __restrict__ qout,
     float* __restrict__ gsi, int64_t n8, fp8dp_acc_slot* __restrict__ slots) {
@@ -129,12 +134,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
     }
   };
   // two grid-strided vectors per iteration (the stride is a multiple of 16,
-  // so each DPP row still holds one whole group)
+  // so each DPP row still holds one whole group); ONE: a thread per vector
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < n8; i += 2 * stride) {
-    const uint4 x0 = load_nt(h + i), x1 = load_nt(h + i + stride);
-    one(x0, i);
-    one(x1, i + stride);
+  if constexpr (!ONE) {
+    for (; i + stride < n8; i += 2 * stride) {
+      const uint4 x0 = load_nt(h + i), x1 = load_nt(h + i + stride);
+      one(x0, i);
+      one(x1, i + stride);
+    }
   }
   if (i < n8) one(load_nt(h + i), i);
   if constexpr (ACC) block_fold<kThreads>(amax16, sat, slots);
@@ -205,7 +212,7 @@ __device__ __forceinline__ float mx_multiplier(int k) {
 // grid stride is a multiple of 4 and n8 % 4 == 0, so a quad is active or
 // inactive as a whole); two quad swaps give every lane the block maximum, and
 // the quad's first lane writes the exponent byte.
-template <int FMT, int ACT, bool WBF16, bool HW>
+template <int FMT, int ACT, bool WBF16, bool HW, bool ONE = false>
 __global__ __launch_bounds__(kThreads) void k_quant_mx(const uint4* __restrict__ h,
                                                        uint4* __restrict__ bout,
                                                        uint2* __restrict__ qout,
@@ -228,6 +235,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(const uint4* __restrict__
     store_nt(qout + i, cast8<FMT, HW>(b, mx, mx_multiplier(k), sat));
   };
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if constexpr (ONE) {   // a thread per vector (n8 % 4 == 0 keeps quads whole)
+    if (i < n8) one(load_nt(h + i), i);
+    return;
+  }
   for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
     uint4 x[kUnroll];
 #pragma unroll
@@ -481,7 +492,12 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
   const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0)
+  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
+    hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
+                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
+                       scale_ptr, slots);
+  else if (codec() == 0)
     hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
@@ -511,7 +527,12 @@ static int launch_group(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* q
                         fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0)
+  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
+    hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
+                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8,
+                       slots);
+  else if (codec() == 0)
     hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8,
@@ -548,7 +569,11 @@ static int launch_mx_quant(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t
                            uint8_t* e8, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0)
+  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
+    hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
+                       reinterpret_cast<uint2*>(qout), e8, n8);
+  else if (codec() == 0)
     hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true>), dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
                        reinterpret_cast<uint2*>(qout), e8, n8);

@@ -255,6 +255,40 @@ def test_results_do_not_depend_on_grid_size():
     assert outs[0][3] > 0
 
 
+@pytest.mark.parametrize("mode", ["group", "mx"])
+def test_group_and_mx_results_do_not_depend_on_grid_size(mode):
+    """With no grid limit each thread takes one vector (no loop); with small
+    limits the grid-stride loops run: the outputs are the same bytes, and the
+    oracle's."""
+    h = workloads.normal(46, 333, 768)
+    outs = []
+    for limit in (0, 1, 3, 64, 1000):
+        prev = sq.fp8dp_set_grid_limit(limit)
+        try:
+            if mode == "group":
+                st = sq.TensorState(sq.E4M3, 1, 1.25, 0.25)
+                b, q, g = _run(h, sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, st)
+                d = st.read()
+                outs.append((bf16_np(b).tobytes(), u8_np(q).tobytes(),
+                             g.cpu().numpy().tobytes(), d["amax_acc"], d["sat_acc"]))
+            else:
+                hd = to_dev_bf16(h)
+                b = torch.empty_like(hd)
+                q = torch.empty(h.shape, dtype=torch.uint8, device=DEV)
+                e = torch.empty((h.shape[0], h.shape[1] // 32), dtype=torch.uint8, device=DEV)
+                sq.quantize_mx(hd, sq.ACT_RELU2, sq.E4M3, q, e, b)
+                outs.append((bf16_np(b).tobytes(), u8_np(q).tobytes(), u8_np(e).tobytes()))
+        finally:
+            sq.fp8dp_set_grid_limit(prev)
+    assert all(o == outs[0] for o in outs)
+    if mode == "group":
+        r = oracle_quantize(h, O.ACT_RELU2, O.E4M3, O.PER_GROUP128)
+        assert outs[0][1] == r.fp8.tobytes() and outs[0][0] == r.bf16.tobytes()
+    else:
+        r = O.quantize_mx(h, O.ACT_RELU2, O.E4M3)
+        assert outs[0][1] == r.fp8.tobytes() and outs[0][2] == r.scale.tobytes()
+
+
 def test_two_calls_accumulate_into_one_step():
     h = workloads.normal(45, 512, 256)
     st = sq.TensorState(sq.E4M3, 1, 1.25, 1.0)
