@@ -89,7 +89,7 @@ __device__ __forceinline__ float dgrad_elem(float a, float da) {
   return __fmul_rn(__fmul_rn(2.0f, r), da);
 }
 
-template <int CACHE, int FMT, bool WBF16, bool HW>
+template <int CACHE, int FMT, bool WBF16, bool HW, int FORM = kFormLoop>
 __global__ __launch_bounds__(kThreads) void k_relu2_bwd(const uint4* __restrict__ dA,
                                                         const void* __restrict__ cache,
                                                         const float* __restrict__ a_si,
@@ -156,13 +156,31 @@ __global__ __launch_bounds__(kThreads) void k_relu2_bwd(const uint4* __restrict_
     store_nt(qout + i, cast8<FMT, HW>(b, mx, s, sat));
   };
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < n8; i += 2 * stride) {
-    const uint4 d0 = load_nt(dA + i), d1 = load_nt(dA + i + stride);
-    const uint4 c0 = load_cache<CACHE>(cache, i), c1 = load_cache<CACHE>(cache, i + stride);
-    one(d0, c0, i);
-    one(d1, c1, i + stride);
+  if constexpr (FORM == kFormOne) {
+    if (i < n8) one(load_nt(dA + i), load_cache<CACHE>(cache, i), i);
+  } else if constexpr (FORM == kFormPair) {
+    // vectors b*2T + t and b*2T + T + t, all four loads issued first
+    const int64_t i0 = (int64_t)blockIdx.x * (2 * kThreads) + threadIdx.x, i1 = i0 + kThreads;
+    uint4 d0 = {}, d1 = {}, c0 = {}, c1 = {};
+    if (i0 < n8) {
+      d0 = load_nt(dA + i0);
+      c0 = load_cache<CACHE>(cache, i0);
+    }
+    if (i1 < n8) {
+      d1 = load_nt(dA + i1);
+      c1 = load_cache<CACHE>(cache, i1);
+    }
+    if (i0 < n8) one(d0, c0, i0);
+    if (i1 < n8) one(d1, c1, i1);
+  } else {
+    for (; i + stride < n8; i += 2 * stride) {
+      const uint4 d0 = load_nt(dA + i), d1 = load_nt(dA + i + stride);
+      const uint4 c0 = load_cache<CACHE>(cache, i), c1 = load_cache<CACHE>(cache, i + stride);
+      one(d0, c0, i);
+      one(d1, c1, i + stride);
+    }
+    if (i < n8) one(load_nt(dA + i), load_cache<CACHE>(cache, i), i);
   }
-  if (i < n8) one(load_nt(dA + i), load_cache<CACHE>(cache, i), i);
   if (tail && blockIdx.x == 0 && threadIdx.x == 0) {
     const uint16_t* dt = reinterpret_cast<const uint16_t*>(dA + n8);
     for (int t = 0; t < tail; ++t) {
@@ -190,17 +208,31 @@ int launch_bwd(const uint16_t* dA, const void* cache, const float* a_si, uint16_
                uint8_t* qout, int64_t n, fp8dp_tensor_state* st, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0)
-    hipLaunchKernelGGL((k_relu2_bwd<CACHE, FMT, WBF16, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, reinterpret_cast<const uint4*>(dA), cache, a_si,
-                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
-                       &st->scale, st->acc);
+  // writes at least as many bytes as it reads only with the BF16 copy and an
+  // FP8 cache (3 B read, 3 B written per element)
+  constexpr bool write_heavy = WBF16 && CACHE != kCacheBf16;
+  const LaunchShape ls = launch_shape(n8, kThreads, write_heavy, kBlocksPerCURead);
+  const unsigned grid =
+      ls.form == kFormLoop || codec() != 0
+          ? grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead)
+          : ls.grid;
+#define FP8DP_LAUNCH_B(F)                                                                    \
+  hipLaunchKernelGGL((k_relu2_bwd<CACHE, FMT, WBF16, true, F>), dim3(grid), dim3(kThreads), 0, \
+                     stream, reinterpret_cast<const uint4*>(dA), cache, a_si,                 \
+                     reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail, \
+                     &st->scale, st->acc)
+  if (codec() == 0 && ls.form == kFormOne)
+    FP8DP_LAUNCH_B(kFormOne);
+  else if (codec() == 0 && ls.form == kFormPair)
+    FP8DP_LAUNCH_B(kFormPair);
+  else if (codec() == 0)
+    FP8DP_LAUNCH_B(kFormLoop);
   else
     hipLaunchKernelGGL((k_relu2_bwd<CACHE, FMT, WBF16, false>), dim3(grid), dim3(kThreads), 0,
                        stream, reinterpret_cast<const uint4*>(dA), cache, a_si,
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
                        &st->scale, st->acc);
+#undef FP8DP_LAUNCH_B
   return check_launch("relu2_backward_quantize");
 }
 

@@ -46,9 +46,9 @@ constexpr int kBlocksPerCURead = 32;   // reads > writes
 // h/bout/qout are viewed as vectors of 8 elements (n8 of them); the last
 // `tail` elements (n % 8) are handled by thread 0 of block 0 with the scalar
 // routine.  scale_ptr: the multiplier (read once); slots: accumulators or
-// nullptr.  ONE: the grid has a thread for every vector (gridDim.x * kThreads
-// >= n8), so each thread loads its one vector first thing, with no loop.
-template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW, bool ONE = false>
+// nullptr.  FORM: kFormOne / kFormPair (the grid covers every vector, one or
+// two per thread, loaded first thing, no loop) or kFormLoop (grid-stride).
+template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW, int FORM = kFormLoop>
 __global__ __launch_bounds__(kThreads) void k_quant_tensor(
     const uint4* __restrict__ h, uint4* __restrict__ bout, uint2* __restrict__ qout, int64_t n8,
     int tail, const float* __restrict__ scale_ptr, fp8dp_acc_slot* __restrict__ slots) {
@@ -65,8 +65,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(
     if constexpr (CAST) store_nt(qout + i, cast8<FMT, HW>(b, mx, s, sat));
   };
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if constexpr (ONE) {
+  if constexpr (FORM == kFormOne) {
     if (i < n8) one(load_nt(h + i), i);
+  } else if constexpr (FORM == kFormPair) {
+    const int64_t i0 = (int64_t)blockIdx.x * (2 * kThreads) + threadIdx.x, i1 = i0 + kThreads;
+    uint4 x0 = {}, x1 = {};
+    if (i0 < n8) x0 = load_nt(h + i0);
+    if (i1 < n8) x1 = load_nt(h + i1);
+    if (i0 < n8) one(x0, i0);
+    if (i1 < n8) one(x1, i1);
   } else {
     // kUnroll grid-strided vectors per iteration, all loads issued first: more
     // bytes in flight per thread to cover HBM latency
@@ -113,7 +120,7 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
 // Each group of 128 elements is 16 vectors, handled by the 16 lanes of one
 // DPP row (the grid stride is a multiple of 16 and n8 % 16 == 0, so a row is
 // active or inactive as a whole).  Current scaling: s_g = max / amax_g.
-template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC, bool HW, bool ONE = false>
+template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC, bool HW, int FORM = kFormLoop>
 __global__ __launch_bounds__(kThreads) void k_quant_group(
     const uint4* __restrict__ h, uint4* __restrict__ bout, uint2* __restrict__ qout,
     float* __restrict__ gsi, int64_t n8, fp8dp_acc_slot* __restrict__ slots) {
@@ -133,17 +140,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_group(
       store_nt(qout + i, cast8<FMT, HW>(b, mx, sg, sat));
     }
   };
-  // two grid-strided vectors per iteration (the stride is a multiple of 16,
-  // so each DPP row still holds one whole group); ONE: a thread per vector
+  // the loop takes two grid-strided vectors per iteration (the stride is a
+  // multiple of 16, so each DPP row still holds one whole group); the pair
+  // form's two ranges start at multiples of 16 vectors likewise
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if constexpr (!ONE) {
-    for (; i + stride < n8; i += 2 * stride) {
-      const uint4 x0 = load_nt(h + i), x1 = load_nt(h + i + stride);
-      one(x0, i);
-      one(x1, i + stride);
+  if constexpr (FORM == kFormPair) {
+    const int64_t i0 = (int64_t)blockIdx.x * (2 * kThreads) + threadIdx.x, i1 = i0 + kThreads;
+    uint4 x0 = {}, x1 = {};
+    if (i0 < n8) x0 = load_nt(h + i0);
+    if (i1 < n8) x1 = load_nt(h + i1);
+    if (i0 < n8) one(x0, i0);
+    if (i1 < n8) one(x1, i1);
+  } else {
+    if constexpr (FORM == kFormLoop) {
+      for (; i + stride < n8; i += 2 * stride) {
+        const uint4 x0 = load_nt(h + i), x1 = load_nt(h + i + stride);
+        one(x0, i);
+        one(x1, i + stride);
+      }
     }
+    if (i < n8) one(load_nt(h + i), i);
   }
-  if (i < n8) one(load_nt(h + i), i);
   if constexpr (ACC) block_fold<kThreads>(amax16, sat, slots);
 }
 
@@ -212,7 +229,7 @@ __device__ __forceinline__ float mx_multiplier(int k) {
 // grid stride is a multiple of 4 and n8 % 4 == 0, so a quad is active or
 // inactive as a whole); two quad swaps give every lane the block maximum, and
 // the quad's first lane writes the exponent byte.
-template <int FMT, int ACT, bool WBF16, bool HW, bool ONE = false>
+template <int FMT, int ACT, bool WBF16, bool HW, int FORM = kFormLoop>
 __global__ __launch_bounds__(kThreads) void k_quant_mx(const uint4* __restrict__ h,
                                                        uint4* __restrict__ bout,
                                                        uint2* __restrict__ qout,
@@ -235,8 +252,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(const uint4* __restrict__
     store_nt(qout + i, cast8<FMT, HW>(b, mx, mx_multiplier(k), sat));
   };
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if constexpr (ONE) {   // a thread per vector (n8 % 4 == 0 keeps quads whole)
+  // one or two vectors per thread without a loop (n8 % 4 == 0 and ranges that
+  // start at multiples of 4 vectors keep quads whole)
+  if constexpr (FORM == kFormOne) {
     if (i < n8) one(load_nt(h + i), i);
+    return;
+  } else if constexpr (FORM == kFormPair) {
+    const int64_t i0 = (int64_t)blockIdx.x * (2 * kThreads) + threadIdx.x, i1 = i0 + kThreads;
+    uint4 x0 = {}, x1 = {};
+    if (i0 < n8) x0 = load_nt(h + i0);
+    if (i1 < n8) x1 = load_nt(h + i1);
+    if (i0 < n8) one(x0, i0);
+    if (i1 < n8) one(x1, i1);
     return;
   }
   for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
@@ -491,22 +518,27 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
                          const float* scale_ptr, fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
-  const unsigned grid = grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
-    hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true, true>), dim3(grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
-                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
-                       scale_ptr, slots);
+  const LaunchShape ls = launch_shape(n8, kThreads, WBF16, kBlocksPerCURead);
+  const unsigned grid = ls.form == kFormLoop || codec() != 0
+                            ? grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead)
+                            : ls.grid;
+#define FP8DP_LAUNCH_T(F)                                                                     \
+  hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true, F>), dim3(grid),      \
+                     dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),            \
+                     reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail, \
+                     scale_ptr, slots)
+  if (codec() == 0 && ls.form == kFormOne)
+    FP8DP_LAUNCH_T(kFormOne);
+  else if (codec() == 0 && ls.form == kFormPair)
+    FP8DP_LAUNCH_T(kFormPair);
   else if (codec() == 0)
-    hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true>), dim3(grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
-                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
-                       scale_ptr, slots);
+    FP8DP_LAUNCH_T(kFormLoop);
   else
     hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, false>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
                        scale_ptr, slots);
+#undef FP8DP_LAUNCH_T
   return check_launch("quantize");
 }
 
@@ -526,22 +558,26 @@ template <int FMT, int ACT, bool WBF16, bool WFP8, bool ACC>
 static int launch_group(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout, float* gsi,
                         fp8dp_acc_slot* slots, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
-    hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true, true>), dim3(grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
-                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8,
-                       slots);
+  const LaunchShape ls = launch_shape(n8, kThreads, WBF16, kBlocksPerCURead);
+  const unsigned grid = ls.form == kFormLoop || codec() != 0
+                            ? grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead)
+                            : ls.grid;
+#define FP8DP_LAUNCH_G(F)                                                                      \
+  hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true, F>), dim3(grid),         \
+                     dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),             \
+                     reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8, slots)
+  if (codec() == 0 && ls.form == kFormOne)
+    FP8DP_LAUNCH_G(kFormOne);
+  else if (codec() == 0 && ls.form == kFormPair)
+    FP8DP_LAUNCH_G(kFormPair);
   else if (codec() == 0)
-    hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, true>), dim3(grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
-                       reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8,
-                       slots);
+    FP8DP_LAUNCH_G(kFormLoop);
   else
     hipLaunchKernelGGL((k_quant_group<FMT, ACT, WBF16, WFP8, ACC, false>), dim3(grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), gsi, n8,
                        slots);
+#undef FP8DP_LAUNCH_G
   return check_launch("quantize_fused(group)");
 }
 
@@ -568,19 +604,25 @@ template <int FMT, int ACT, bool WBF16>
 static int launch_mx_quant(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout,
                            uint8_t* e8, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  const unsigned grid = grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead);
-  if (codec() == 0 && (int64_t)grid * kThreads >= n8)
-    hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
-                       reinterpret_cast<uint2*>(qout), e8, n8);
+  const LaunchShape ls = launch_shape(n8, kThreads, WBF16, kBlocksPerCURead);
+  const unsigned grid = ls.form == kFormLoop || codec() != 0
+                            ? grid_for(n8, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead)
+                            : ls.grid;
+#define FP8DP_LAUNCH_M(F)                                                                   \
+  hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true, F>), dim3(grid), dim3(kThreads), 0, \
+                     stream, reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout), \
+                     reinterpret_cast<uint2*>(qout), e8, n8)
+  if (codec() == 0 && ls.form == kFormOne)
+    FP8DP_LAUNCH_M(kFormOne);
+  else if (codec() == 0 && ls.form == kFormPair)
+    FP8DP_LAUNCH_M(kFormPair);
   else if (codec() == 0)
-    hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, true>), dim3(grid), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
-                       reinterpret_cast<uint2*>(qout), e8, n8);
+    FP8DP_LAUNCH_M(kFormLoop);
   else
     hipLaunchKernelGGL((k_quant_mx<FMT, ACT, WBF16, false>), dim3(grid), dim3(kThreads), 0,
                        stream, reinterpret_cast<const uint4*>(h), reinterpret_cast<uint4*>(bout),
                        reinterpret_cast<uint2*>(qout), e8, n8);
+#undef FP8DP_LAUNCH_M
   return check_launch("quantize_mx");
 }
 

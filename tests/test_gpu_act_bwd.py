@@ -89,6 +89,33 @@ def test_relu2_backward_vs_oracle(n, cache, fmt, codec):
     assert d["amax_acc"] == r.amax_bits and d["sat_acc"] == r.sat
 
 
+@pytest.mark.parametrize("cache", [O.E4M3, O.CACHE_BF16], ids=["c-e4m3", "c-bf16"])
+@pytest.mark.parametrize("want_bf16", [True, False], ids=["bf16", "codes"])
+def test_relu2_backward_does_not_depend_on_grid_size(cache, want_bf16):
+    """No grid limit: one or two vectors per thread without a loop, by the
+    launch's read/write mix; small limits: the grid-stride loop.  Same bytes,
+    same accumulators, and the oracle's."""
+    n = 40000 + 3
+    rng = np.random.default_rng(77 + cache)
+    dA, c, si = _inputs(rng, n, cache)
+    outs = []
+    for limit in (0, 1, 7, 100):
+        prev = sq.fp8dp_set_grid_limit(limit)
+        try:
+            st = sq.TensorState(O.E5M2, 1, 1.25, 1.0)
+            b, q = _run(dA, c, cache, si, O.E5M2, st, want_bf16)
+            d = st.read()
+            outs.append((None if b is None else bf16_np(b).tobytes(), u8_np(q).tobytes(),
+                         d["amax_acc"], d["sat_acc"]))
+        finally:
+            sq.fp8dp_set_grid_limit(prev)
+    assert all(o == outs[0] for o in outs)
+    r = O.relu2_backward(dA, c, cache, si, O.E5M2, O.State(O.E5M2, 1, 1.25, 1.0).scale)
+    assert outs[0][1] == r.fp8.tobytes() and outs[0][2] == r.amax_bits
+    if want_bf16:
+        assert outs[0][0] == r.bf16.tobytes()
+
+
 def test_relu2_backward_special_values(codec):
     # zero, exact squares, NaN / negative / infinite cache values, zero and
     # infinite gradients
