@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 }
 
 // ------------------------------------------------------------------ large tiles
-// Per-tensor FP8 path for large problems.  A 512-thread workgroup (8 waves,
+// Per-tensor, MX and per-group FP8 paths for large problems.  A 512-thread workgroup (8 waves,
 // two per SIMD) owns a 256 x BN tile of y (BN = 64 TN = 128, 192 or 256); wave
 // w owns rows 64 (w / 2) .. +63 and columns (BN / 2)(w % 2) .. as 2 x TN tiles
 // of the 32 x 32 x 64 MFMA (TN = 4 uses 252 of the 256 registers a wave may

@@ -30,14 +30,16 @@
 namespace fp8dp {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 2;        // vectors of 8 per thread per iteration (per tensor)
-// Grid of the element-wise kernels, by their read/write mix (measured):
-// kernels that write at least as many bytes as they read stream fastest with
-// one 8-element vector per thread and no grid-stride loop (the quantizer with
-// its BF16 copy, 2 B read / 3 B written: 6.4 TB/s at 0.5 and 2 GiB against
-// 4.9 with 32 workgroups per CU looping); read-heavy ones with 32 workgroups
-// per CU looping (the cast without the copy, 2 B / 1 B: 14% slower with one
-// vector per thread).
+constexpr int kUnroll = 2;        // vectors of 8 per thread per loop iteration (per tensor)
+// Launch form of the element-wise kernels, by their read/write mix (measured;
+// launch_shape in common.hpp): kernels that write at least as many bytes as
+// they read take one 8-element vector per thread with no loop (the quantizer
+// with its BF16 copy, 2 B read / 3 B written: 6.4 TB/s at 0.5 and 2 GiB
+// against 4.9 with 32 workgroups per CU looping); read-heavy ones take two
+// vectors per thread over block-contiguous ranges with no loop.  Where the
+// grid of those forms would be capped, the grid-stride loop runs over
+// kBlocksPerCU / kBlocksPerCURead workgroups per CU (the best of a sweep of
+// 8-96 for the loop with reads > writes).
 constexpr int kBlocksPerCU = 1 << 20;  // writes >= reads: no cap below one vector per thread
 constexpr int kBlocksPerCURead = 32;   // reads > writes
 
