@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -812,16 +813,24 @@ def copy_ceiling(sq, torch, dev):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+def code_digest(src: bytes) -> str:
+    """SHA-256 of a C++ source with its comments and whitespace removed: it
+    changes with the code, not with its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", src.decode(), flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def measured_traffic(name, source):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    on the current kernel code (else None)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, "scaled_quantization_amd", "csrc", source), "rb").read()
-        if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        if rec.get("kernel_code_sha256") != code_digest(src):
             return None
         return rec.get("bytes_per_launch")
     except Exception:
