@@ -50,7 +50,9 @@ PINNED = {
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c (the mutation test loads copies
+# with planted mistakes this way, each in a process of its own).
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)
