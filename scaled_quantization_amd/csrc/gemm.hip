@@ -304,7 +304,7 @@ struct Relu2Bwd {
 // COND: the launch does nothing unless *run_flag != 0 (a device-side flag,
 // e.g. the overflow mark of a scaling state), read once by every workgroup.
 template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false, int BC = -1,
-          int BF = 1, int XG = 1, bool PG = false>
+          int BF = 1, int XG = 1, bool PG = false, bool PER = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ B, int M, int N,
                                                      int K, const float* __restrict__ sa,
@@ -325,6 +325,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
   static_assert(!PG || (TN == 2 && XG == 4 && !MX && !SPLIT && BC < 0),
                 "per-group scales: 256 x 128 tiles, scales through the ring");
+  static_assert(!PER || (!MX && !PG && !SPLIT && !COND && BC < 0),
+                "persistent grid: the plain per-tensor path");
   constexpr bool XR = (MX || PG) && XG == 4;                // exponents / scales in their own ring
   constexpr int SLOT = TILES + (MX && !XR ? 2048 : 0);      // + 256 A and 256 B exponent dwords
   constexpr int XSZ = XR ? 8192 : 0;                        // 512 rows x 16 bytes (4 stages)
@@ -334,8 +336,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
+  // PER: a persistent grid; workgroup b runs the tiles of its passes one after
+  // another through one pipeline, stage g being k-stage g % KT of the tile of
+  // pass g / KT, so the next tile's first stages are copied while a tile's
+  // last stage and its epilogue run
   int tile, split = 0;
-  if constexpr (SPLIT) {
+  if constexpr (PER) {
+    tile = tile_of_pass(blockIdx.x, 0, gridDim.x, ntiles);
+  } else if constexpr (SPLIT) {
     const int u = tile_of_block(blockIdx.x, ntiles * splits);
     split = u / ntiles;
     tile = u % ntiles;
@@ -350,6 +358,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   const int wc = (wave & 1) * (BN / 2);
   const int KT = K / kBK / (SPLIT ? splits : 1);
   const size_t kbase = (size_t)split * KT * kBK;
+  const int GS = PER ? tiles_of_block(blockIdx.x, gridDim.x, ntiles) * KT : KT;   // stages to run
+  if (GS == 0) return;   // (a persistent grid has no more workgroups than tiles)
 
   // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7; lane l
   // lands at chunk l % 8 of row l / 8 there, so it fetches the logical chunk
@@ -378,11 +388,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   }
   auto issue = [&](int kt) {
     uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
-    const size_t k0 = (size_t)kt * kBK;
+    int64_t oa = (int64_t)kt * kBK, ob = oa;
+    if constexpr (PER) {
+      // the tile of stage kt, as row offsets from this workgroup's first tile
+      const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
+      const int64_t k0 = (int64_t)(kt % KT) * kBK;
+      oa = (int64_t)((t / tiles_n) * BM - m0) * K + k0;
+      ob = (int64_t)((t % tiles_n) * BN - n0) * K + k0;
+    }
 #pragma unroll
-    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + k0, base + i * 8192);
+    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + oa, base + i * 8192);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + k0, base + ASZ + i * 8192);
+    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + ob, base + ASZ + i * 8192);
     if constexpr (XR) {
       if ((kt & 3) == 0)
         copy16_to_lds(gE + kt * 4, lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ + wave * 1024);
@@ -541,9 +558,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   };
   uint8_t* const cache_lds = lds + (KT & 1) * SLOT;
 
+  // epilogue: scale, round to BF16 and store pairs of adjacent columns of the
+  // tile at (tm0, tn0).  In a 32 x 32 MFMA tile the lane holds column
+  // lane % 32 and register r holds row 8 (r / 4) + 4 (lane / 32) + r % 4;
+  // swapping one value with the neighbour lane (DPP quad_perm 1,0,3,2) gives
+  // the even lane columns (c, c+1) of row r and the odd lane the same columns
+  // of row r+1.
+  auto epi_plain = [&](int tm0, int tn0) {
+    const float f = MX ? 1.0f : sa[0] * sb[0];
+    const bool odd = lane & 1;
+    const int colp = (lane & 31) & ~1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
+          const float give = odd ? v0 : v1;
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
+                                                 false));
+          const uint32_t packed = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
+          const int row =
+              tm0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
+          const int col = tn0 + wc + j * 32 + colp;
+          *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = packed;
+        }
+  };
+
   // prologue: stages 0 and 1 in flight, stage 0 landed and published
   issue(0);
-  if (KT > 1) {
+  if (GS > 1) {
     issue(1);
     wait_vmcnt<NCOPY>();
   } else {
@@ -553,7 +599,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
   load_frags(0, 0, fa0, fb0, xa0, xb0);
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < GS; ++kt) {
     if constexpr (PG) {
       // the reads of substep 0 were issued a half stage ago: wait for them
       // here, before the reads below (else the wait covers those as well)
@@ -579,13 +625,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
     stage_barrier();
     // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
-    if (kt + 2 < KT) issue(kt + 2);
+    if (kt + 2 < GS) issue(kt + 2);
     if constexpr (BC >= 0) {
       if (kt + 2 == KT) issue_cache(cache_lds);
     }
-    if (kt + 1 < KT) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
+    if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
     mfmas(fa1, fb1, xa1, xb1, 1);
+    if constexpr (PER) {
+      if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum
+        const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
+        epi_plain((t / tiles_n) * BM, (t % tiles_n) * BN);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      }
+    }
   }
+  if constexpr (PER) return;
 
   if constexpr (SPLIT) {
     // FP32 partial sums: lanes 0-31 of a store cover 32 consecutive columns
@@ -704,37 +763,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     return;
   }
 
-  // epilogue: scale, round to BF16 and store pairs of adjacent columns.  In a
-  // 32 x 32 MFMA tile the lane holds column lane % 32 and register r holds row
-  // 8 (r / 4) + 4 (lane / 32) + r % 4; swapping one value with the neighbour
-  // lane (DPP quad_perm 1,0,3,2) gives the even lane columns (c, c+1) of row
-  // r and the odd lane the same columns of row r+1.
-  const float f = MX ? 1.0f : sa[0] * sb[0];
-  const bool odd = lane & 1;
-  const int colp = (lane & 31) & ~1;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
-        const float give = odd ? v0 : v1;
-        const float got = __builtin_bit_cast(
-            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
-                                               false));
-        const uint32_t packed = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
-        const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
-        const int col = n0 + wc + j * 32 + colp;
-        *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = packed;
-      }
+  epi_plain(m0, n0);
 }
 
 template <int FA, int FB, int TN>
 static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                       const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)((M / 256) * (N / (64 * TN)))),
-                     dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
+  const int64_t ntiles = (M / 256) * (N / (64 * TN));
+  // more tiles than compute units and short tiles (at most 16 stages of K): a
+  // persistent grid (one workgroup per CU -- the LDS ring takes more than half
+  // of a CU's 160 KiB -- a multiple of 8 for the XCD order), each running its
+  // tiles through one pipeline.  Measured (same outputs bit for bit): 10-14%
+  // faster at K = 512-1024, 2-5% at 1536-2048, but 2-5% slower at K = 4096 and
+  // beyond, where the per-tile grid's dynamic dispatch keeps the compute units
+  // out of step and spreads the epilogues' store bursts
+  const int64_t cus = num_cus() & ~7;
+  if (cus >= 8 && ntiles > cus && K / kBK <= 16)
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, false, -1, 1, 1, false, true>),
+                       dim3((unsigned)cus), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
+                       sb, y, nullptr, 1);
+  else
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)ntiles), dim3(512), 0,
+                       stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
 }
 
@@ -780,8 +830,8 @@ static int launch_bwd_epi(const uint8_t* a, const uint8_t* b, int64_t M, int64_t
 template <int BC, int BF>
 static int launch_bwd_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                            const float* sa, const float* sb, Relu2Bwd bwd, hipStream_t stream) {
+  // no 256-wide tile: with the backward epilogue's registers it would spill
   if (N % 192 == 0) return launch_bwd_epi<BC, BF, 3>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
-  if (N % 256 == 0) return launch_bwd_epi<BC, BF, 4>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
   return launch_bwd_epi<BC, BF, 2>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
 }
 
