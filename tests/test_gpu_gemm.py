@@ -252,6 +252,27 @@ def test_large_tile_paths(M, N, K):
     _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
 
 
+@pytest.mark.parametrize("M,N,K", [(5376, 3072, 512), (33024, 384, 256), (20480, 1024, 1024),
+                                   (16384, 3072, 2048)])
+def test_persistent_grid_paths(M, N, K):
+    # more tiles than compute units with at most 16 stages of K: the
+    # persistent grid, whose workgroups run tile after tile through one
+    # pipeline -- 336 tiles (some workgroups run two, some one), 258 tiles
+    # (not a multiple of 8: plain tile order), 320 tiles of 256 x 256, and
+    # 1024 tiles of 16 stages; rows sampled from every tile row-block
+    rng = np.random.default_rng(M + 3 * N + K)
+    t = O.fp8_decode_table(O.E4M3)
+    near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
+    a8 = rng.choice(near, size=(M, K)).astype(np.uint8)
+    w8 = rng.choice(near, size=(N, K)).astype(np.uint8)
+    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, FP8)
+    rows = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(255, M, 256),
+                                     rng.integers(0, M, 16)]))
+    ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
+    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows)
+    _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
+
+
 def _group_case(M, N, K, fa, fb):
     rng = np.random.default_rng(M * 7 + N + K)
     ta = O.fp8_decode_table(fa)
