@@ -320,6 +320,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   if constexpr (COND) {
     if (*run_flag == 0) return;
   }
+  // BC: the backward epilogue's two scalars, read before any store (read
+  // later, every use after a store would wait for all stores in flight)
+  float bwd_si = 0.0f, bwd_sg = 0.0f;
+  if constexpr (BC >= 0) {
+    bwd_si = *bwd.cache_si;
+    bwd_sg = *bwd.scale;
+  }
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
   static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
@@ -666,18 +673,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     // has passed the stage's barrier after its last fragment reads)
     if (KT < 2) issue_cache(cache_lds);
     // 2 sqrt(dec(c) * si) for the 256 codes (threads 0-255, the per-element
-    // operations of relu2_backward_quantize)
-    __shared__ float two_root[256];
+    // operations of relu2_backward_quantize), in the ring slot of stage KT-1
+    // (every wave passed the last stage's barrier after reading it) -- one
+    // LDS array, see block_fold_in
+    float* const two_root = reinterpret_cast<float*>(lds + ((KT - 1) & 1) * SLOT);
     if (threadIdx.x < 256) {
       float d;
       if constexpr (BC == 0) d = __builtin_amdgcn_cvt_pk_f32_fp8((int)threadIdx.x, false)[0];
       else d = __builtin_amdgcn_cvt_pk_f32_bf8((int)threadIdx.x, false)[0];
-      two_root[threadIdx.x] = __fmul_rn(2.0f, __builtin_sqrtf(__fmul_rn(d, *bwd.cache_si)));
+      two_root[threadIdx.x] = __fmul_rn(2.0f, __builtin_sqrtf(__fmul_rn(d, bwd_si)));
     }
     wait_vmcnt<0>();
     __syncthreads();
     const float f = sa[0] * sb[0];
-    const float sg = *bwd.scale;
+    const float sg = bwd_sg;
     const bool odd = lane & 1;
     const int colp = (lane & 31) & ~1;
     uint32_t amax16 = 0, sat = 0;
@@ -740,7 +749,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
               (uint16_t)code;
         }
       }
-    block_fold<512>(amax16, sat, bwd.slots);
+    block_fold_in<512>(amax16, sat, bwd.slots,
+                       reinterpret_cast<uint32_t*>(lds + ((KT - 1) & 1) * SLOT + 1024));
     return;
   }
 

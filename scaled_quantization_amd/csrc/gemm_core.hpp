@@ -65,13 +65,23 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Global -> LDS copies (global_load_lds): lane i's 16 bytes land at l + 16 i,
+// l the wave-uniform LDS address in M0.  Issued as inline assembly, with the
+// one wait state a write of M0 needs before the copy reads it, so that the
+// compiler does not track them: it cannot tell which LDS bytes a copy writes,
+// and it would make every LDS access after one (the fragment reads of other
+// stages, an epilogue's staging) wait for every copy in flight -- and for
+// every store, which shares the same counter.  The kernels wait for their
+// copies themselves (wait_vmcnt, then a barrier) before any read of them.
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void_t*)l;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(la) : "memory");
 }
 
 // The 4-byte form: lane i's dword lands at l + 4 i.
 __device__ __forceinline__ void copy4_to_lds(const uint8_t* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void_t*)l;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(la) : "memory");
 }
 
 

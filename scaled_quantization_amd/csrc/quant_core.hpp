@@ -103,10 +103,15 @@ __device__ __forceinline__ void quant_one(uint16_t h, float s, uint16_t& b, uint
 
 // Block-wide reduction of (amax16, sat) and one atomic pair into a slot.
 // NT: threads of the block (a multiple of 64); every thread must call it.
+// sm: 2 NT / 64 words of LDS scratch.  Kernels that copy global memory
+// straight into LDS keep all their LDS in one array and pass a part of it:
+// with a second LDS variable the compiler tracks the copies per variable and
+// makes every read of the copied array wait for all copies in flight.
 template <int NT>
-__device__ __forceinline__ void block_fold(uint32_t amax16, uint32_t sat, fp8dp_acc_slot* slots) {
-  __shared__ uint32_t s_max[NT / 64];
-  __shared__ uint32_t s_sat[NT / 64];
+__device__ __forceinline__ void block_fold_in(uint32_t amax16, uint32_t sat,
+                                              fp8dp_acc_slot* slots, uint32_t* sm) {
+  uint32_t* s_max = sm;
+  uint32_t* s_sat = sm + NT / 64;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const uint32_t om = __shfl_xor(amax16, off);
@@ -131,6 +136,12 @@ __device__ __forceinline__ void block_fold(uint32_t amax16, uint32_t sat, fp8dp_
     if (m) atomicMax(&slot->amax, m << 16);
     if (c) atomicAdd((unsigned long long*)&slot->sat, (unsigned long long)c);
   }
+}
+
+template <int NT>
+__device__ __forceinline__ void block_fold(uint32_t amax16, uint32_t sat, fp8dp_acc_slot* slots) {
+  __shared__ uint32_t sm[2 * (NT / 64)];
+  block_fold_in<NT>(amax16, sat, slots, sm);
 }
 
 }  // namespace fp8dp
