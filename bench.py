@@ -821,6 +821,30 @@ def code_digest(src: bytes) -> str:
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
+def kernel_code_digest(source):
+    """code_digest of a csrc source followed by the local headers it includes
+    (transitively, each once, in include order): the code the kernel is
+    compiled from."""
+    dirs = (os.path.join(ROOT, "scaled_quantization_amd", "csrc"), os.path.join(ROOT, "include"))
+    seen, parts = set(), []
+
+    def add(path):
+        if path in seen:
+            return
+        seen.add(path)
+        src = open(path, "rb").read()
+        parts.append(src)
+        for inc in re.findall(rb'#include "([^"]+)"', src):
+            for d in dirs:
+                p = os.path.join(d, inc.decode())
+                if os.path.exists(p):
+                    add(p)
+                    break
+
+    add(os.path.join(dirs[0], source))
+    return code_digest(b"\n".join(parts))
+
+
 def measured_traffic(name, source):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel code (else None)."""
@@ -829,8 +853,7 @@ def measured_traffic(name, source):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "scaled_quantization_amd", "csrc", source), "rb").read()
-        if rec.get("kernel_code_sha256") != code_digest(src):
+        if rec.get("kernel_code_sha256") != kernel_code_digest(source):
             return None
         return rec.get("bytes_per_launch")
     except Exception:
