@@ -256,13 +256,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // LDS read waits in front of the MFMA pipe.
 // The epilogue pairs adjacent output columns between neighbour lanes (one DPP
 // swap) and stores BF16 pairs straight to Y.
-// PG (per-128-group scales, 256 x 128 tiles): one stage is one 128-wide
-// group of k, so each stage's two substeps accumulate a partial sum that is
-// then promoted, acc += part * (sa[m, g] * sb[n / 128, g]) -- the small-tile
-// kernel's arithmetic.  The tiles are computed transposed (B fragment first),
-// which leaves one scale product per lane and fragment row instead of one per
-// element: with the A rows in the registers the promotion cost a product per
-// element and was slower than the small-tile kernel.
+// PG (per-128-group scales, 256 x 128 or 256 x 192 tiles): one stage is one
+// 128-wide group of k, so each stage's two substeps accumulate a partial sum
+// that is then promoted, acc += part * (sa[m, g] * sb[n / 128, g]) -- the
+// small-tile kernel's arithmetic.  The tiles are computed transposed (B
+// fragment first), which leaves one scale product per lane and fragment row
+// instead of one per element: with the A rows in the registers the promotion
+// cost a product per element and was slower than the small-tile kernel.
+// A 192-wide tile spans two B blocks (one scale per fragment) and runs its
+// stage by A fragment row rather than by substep (see the loop).
 // Measured alternatives (GPT-2 shape, same tile): no half-stage pipelining
 // (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
 // deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
@@ -330,8 +332,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
   static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
-  static_assert(!PG || (TN == 2 && XG == 4 && !MX && !SPLIT && BC < 0),
-                "per-group scales: 256 x 128 tiles, scales through the ring");
+  static_assert(!PG || ((TN == 2 || TN == 3) && XG == 4 && !MX && !SPLIT && BC < 0),
+                "per-group scales: 256 x 128 or 256 x 192 tiles, scales through the ring");
   static_assert(!PER || (!MX && !PG && !SPLIT && !COND && BC < 0),
                 "persistent grid: the plain per-tensor path");
   constexpr bool XR = (MX || PG) && XG == 4;                // exponents / scales in their own ring
@@ -386,9 +388,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   if constexpr (MX || PG) {
     const int r = (wave & 3) * 64 + lane;
     const size_t kb = (size_t)K / 32;
-    if constexpr (PG)
+    if constexpr (PG) {
+      // B block rows n0 / 128 and, for a 192-wide tile, n0 / 128 + 1 (lane 1 of wave 4)
+      const int nbr = n0 / 128 + ((TN == 3 && r == 1) ? 1 : 0);
       gE = wave < 4 ? reinterpret_cast<const uint8_t*>(sa) + (size_t)(m0 + r) * kb
-                    : reinterpret_cast<const uint8_t*>(sb) + (size_t)(n0 / 128) * kb;
+                    : reinterpret_cast<const uint8_t*>(sb) + (size_t)nbr * kb;
+    }
     else
       gE = wave < 4 ? ea + (size_t)(m0 + r) * kb + kbase / 32
                     : eb + (size_t)(n0 + (r < BN ? r : BN - 1)) * kb + kbase / 32;
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 #pragma unroll
         for (int t = 0; t < TM; ++t) xa[t] = sE[4 * (wr + 32 * t + frow)];
         if constexpr (PG) {
-          xb[0] = sE[4 * 256];             // the tile's B block scale
+          xb[0] = sE[4 * 256];             // the tile's B block scale (128-wide tiles)
         } else {
 #pragma unroll
           for (int t = 0; t < TN; ++t) xb[t] = sE[4 * (256 + wc + 32 * t + frow)];
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   // lane holds one A row (its column lane % 32) and its 16 registers hold B
   // rows of one 128-wide B block.  The promotion then needs one product of
   // scales per lane and fragment row (sa[m] sb), not one per element.
-  v16f_t part[PG ? TM : 1][PG ? TN : 1];
+  v16f_t part[PG && TN == 2 ? TM : 1][PG && TN == 2 ? TN : 1];
   // Without MX the scale operands are the constant 0, which the compiler
   // lowers to the unscaled instruction (checked in the generated assembly).
   auto mfmas = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* ra, const uint32_t* rb,
@@ -603,51 +608,148 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     wait_vmcnt<0>();
   }
   stage_barrier();
-  v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
-  load_frags(0, 0, fa0, fb0, xa0, xb0);
-  for (int kt = 0; kt < GS; ++kt) {
-    if constexpr (PG) {
-      // the reads of substep 0 were issued a half stage ago: wait for them
-      // here, before the reads below (else the wait covers those as well)
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // first half: read substep 1 of stage kt, multiply substep 0
-    load_frags(kt, 1, fa1, fb1, xa1, xb1);
-    mfmas(fa0, fb0, xa0, xb0, 0);
-    if constexpr (MX || PG) {
-      // keep these products in the first half: without a use here the
-      // compiler sinks them past the barrier (they only feed later ones)
+  if constexpr (PG && TN == 3) {
+    // 256 x 192 tiles: the partial sums of all six fragments cannot stay live
+    // across the half stage beside the accumulators, so the stage is split by
+    // A fragment instead of by substep: the first half runs fragment row 0's
+    // three chains (both substeps, then the promotion), the second half row
+    // 1's.  Each chain is the 256 x 128 path's arithmetic -- part = B0 A0,
+    // part += B1 A1, acc = fma(part, sa sb, acc) -- so the outputs are the
+    // same bit for bit.  All of stage kt's B fragments and row 0's A
+    // fragments are read in the previous second half, row 1's in the first
+    // half, so every read of a slot is done by the barrier that frees it.
+    v8i_t gb[2][TN], ga0[2], ga1[2];
+    uint32_t ya0, ya1, yb[TN];
+    auto read_b = [&](int kt) {
+      const uint8_t* sB = lds + (kt & 1) * SLOT + ASZ;
+      const uint32_t* sE =
+          reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TN; ++t) yb[t] = sE[4 * (256 + ((n0 + wc + 32 * t) >> 7) - (n0 >> 7))];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const int r = wc + t * 32 + frow, c0 = h * 4 + fhalf;
+          const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
+          const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 2));
+          gb[h][t] =
+              __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    auto read_a = [&](int kt, int t, v8i_t* ga, uint32_t& ya) {
+      const uint8_t* sA = lds + (kt & 1) * SLOT;
+      const uint32_t* sE =
+          reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
+      const int r = wr + t * 32 + frow;
+      ya = sE[4 * r];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c0 = h * 4 + fhalf;
+        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
+        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 2));
+        ga[h] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    auto chains = [&](const v8i_t* ga, v16f_t* p) {
+      const v16f_t zero = {};
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        p[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[0][j], ga[0], zero, FB, FA, 0, 0,
+                                                              0, 0);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        p[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[1][j], ga[1], p[j], FB, FA, 0, 0,
+                                                              0, 0);
+    };
+    read_b(0);
+    read_a(0, 0, ga0, ya0);
+    for (int kt = 0; kt < GS; ++kt) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // stage kt's B and row-0 A fragments
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        v16f_t p[TN];
+        chains(ga0, p);
+        // row 1's reads after the instructions that read row 0's fragments
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(kt, 1, ga1, ya1);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          if constexpr (PG) asm volatile("" : "+v"(part[i][j]));
-          else asm volatile("" : "+v"(acc[i][j]));
+          const float c = __uint_as_float(ya0) * __uint_as_float(yb[j]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[0][j][r] = __builtin_fmaf(p[j][r], c, acc[0][j][r]);
         }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[0][j]));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
+      wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
+      stage_barrier();
+      if (kt + 2 < GS) issue(kt + 2);
+      float c1[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) c1[j] = __uint_as_float(ya1) * __uint_as_float(yb[j]);
+      v16f_t p[TN];
+      chains(ga1, p);
+      // the next stage's reads go after the instructions that still read gb
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < GS) {
+        read_b(kt + 1);
+        read_a(kt + 1, 0, ga0, ya0);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[1][j][r] = __builtin_fmaf(p[j][r], c1[j], acc[1][j][r]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
-    wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
-    stage_barrier();
-    // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
-    if (kt + 2 < GS) issue(kt + 2);
-    if constexpr (BC >= 0) {
-      if (kt + 2 == KT) issue_cache(cache_lds);
-    }
-    if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
-    mfmas(fa1, fb1, xa1, xb1, 1);
-    if constexpr (PER) {
-      if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum
-        const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
-        epi_plain((t / tiles_n) * BM, (t % tiles_n) * BN);
+  } else {
+    v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
+    load_frags(0, 0, fa0, fb0, xa0, xb0);
+    for (int kt = 0; kt < GS; ++kt) {
+      if constexpr (PG) {
+        // the reads of substep 0 were issued a half stage ago: wait for them
+        // here, before the reads below (else the wait covers those as well)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // first half: read substep 1 of stage kt, multiply substep 0
+      load_frags(kt, 1, fa1, fb1, xa1, xb1);
+      mfmas(fa0, fb0, xa0, xb0, 0);
+      if constexpr (MX || PG) {
+        // keep these products in the first half: without a use here the
+        // compiler sinks them past the barrier (they only feed later ones)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (PG && TN == 2) asm volatile("" : "+v"(part[i][j]));
+            else asm volatile("" : "+v"(acc[i][j]));
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
+      wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
+      stage_barrier();
+      // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
+      if (kt + 2 < GS) issue(kt + 2);
+      if constexpr (BC >= 0) {
+        if (kt + 2 == KT) issue_cache(cache_lds);
+      }
+      if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
+      mfmas(fa1, fb1, xa1, xb1, 1);
+      if constexpr (PER) {
+        if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum
+          const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
+          epi_plain((t / tiles_n) * BM, (t % tiles_n) * BN);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        }
       }
     }
   }
@@ -801,9 +903,22 @@ static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
 template <int FA, int FB>
 static int launch_pg(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                      const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, 2, false, false, false, -1, 1, 4, true>),
-                     dim3((unsigned)((M / 256) * (N / 128))), dim3(512), 0, stream, a, b, (int)M,
-                     (int)N, (int)K, sa, sb, y, nullptr, 1);
+  // 256 x 192 tiles when they take fewer rounds of the grid: one takes about
+  // 1.6x as long as a 256 x 128 tile (GPT-2 shape 16384 x 768 x 3072: 256
+  // tiles in one round 50.0 us against 384 in two, 62.9 us; with fewer tiles
+  // than compute units the narrow tiles win, 12.8 against 17.2 us at 4096 x
+  // 384 x 1024)
+  const int64_t cus = num_cus();
+  const int64_t t2 = (M / 256) * (N / 128), t3 = N % 192 == 0 ? (M / 256) * (N / 192) : 0;
+  const int64_t r2 = (t2 + cus - 1) / cus, r3 = (t3 + cus - 1) / cus;
+  if (t3 > 0 && 8 * r3 < 5 * r2)
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, 3, false, false, false, -1, 1, 4, true>),
+                       dim3((unsigned)t3), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
+                       sb, y, nullptr, 1);
+  else
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, 2, false, false, false, -1, 1, 4, true>),
+                       dim3((unsigned)t2), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
+                       sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
 }
 

@@ -307,6 +307,27 @@ def test_group_scaled_shapes(M, N, K, fa, fb):
            max_plain_violation_frac=1e-3)
 
 
+# On a 256-CU GPU these shapes take the 256 x 192 per-group tiles (one round
+# of 256 tiles where 256 x 128 tiles need two); their column halves take the
+# 256 x 128 tiles.  Each output's arithmetic does not depend on which tile
+# computes it, so the halves must agree with the whole bit for bit.
+@pytest.mark.parametrize("M,N,K,fa,fb", [(16384, 768, 512, 0, 0), (8192, 1536, 1024, 1, 0)])
+def test_group_wide_tiles_match_narrow_tiles(M, N, K, fa, fb):
+    a8, w8, sa, sb = _group_case(M, N, K, fa, fb)
+    y = _gemm(a8, fa, w8, fb, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
+    h = N // 2
+    left = _gemm(a8, fa, w8[:h], fb, sq.PER_GROUP128, 1 / sa, 1 / sb[: h // 128], FP8)
+    right = _gemm(a8, fa, w8[h:], fb, sq.PER_GROUP128, 1 / sa, 1 / sb[h // 128:], FP8)
+    whole = np.concatenate([left, right], axis=1)
+    diff = np.flatnonzero(y.view(np.uint32) != whole.view(np.uint32))
+    assert diff.size == 0, f"{diff.size} outputs differ, first at {np.unravel_index(diff[0], y.shape)}"
+    rows = np.unique(np.concatenate([np.arange(0, M, M // 24), [M - 1]]))
+    ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
+    allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows)
+    _check(y[rows], ref, absref, f"wide group tiles {M}x{N}x{K}", allow,
+           max_plain_violation_frac=1e-3)
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 384, 2048), (256, 256, 512)])
 def test_group_scaled_kernels_agree(M, N, K):
     """Scale arrays 4 bytes off 16-byte alignment send a K % 512 == 0 problem
