@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-naive", action="store_true")
     p.add_argument("--no-large", action="store_true",
-                   help="skip the large-configuration leg (H 65536 x 16384)")
+                   help="skip the large-configuration leg (H 65536 x 16384) and the "
+                        "fine-grained one (H 65536 x 4096, per-128 groups)")
     p.add_argument("--only", choices=("quantize", "gemm", "copy", "quantize_mx", "gemm_mx",
                                       "relu2_bwd", "gemm_pg"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
@@ -253,6 +254,7 @@ def main():
     out["copy_ceiling_GBs"] = copy_ceiling(sq, torch, dev)
     if not args.no_large:
         out["large_config"] = large_config(sq, torch, dev, args)
+        out["fine_grained_config"] = fine_grained(sq, torch, dev, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
@@ -717,6 +719,31 @@ def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):
     return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1), "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
 
 
+def burst_median(torch, stream, fn, per_burst):
+    """ms per launch of fn: BURST_WARM_MS of its own launches first, then 5
+    bursts of per_burst launches between two events; the median burst."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record(stream)
+    fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    for _ in range(min(4096, int(BURST_WARM_MS / max(a.elapsed_time(b), 1e-3)))):
+        fn()
+    per = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(per_burst):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / per_burst)
+    return sorted(per)[2]
+
+
 def large_config(sq, torch, dev, args):
     """The large layer's forward and gradient casts and its GEMM at full size:
     H[65536 x 16384] -> relu2 -> BF16 copy + E4M3 (delayed, margin 1.25),
@@ -749,28 +776,7 @@ def large_config(sq, torch, dev, args):
     sq.quantize_fused(DY, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, None)
     sq.amax_history_update(st_g)
 
-    def timed(fn, per_burst):
-        ev = lambda: torch.cuda.Event(enable_timing=True)
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record(stream)
-        fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        for _ in range(min(4096, int(BURST_WARM_MS / max(a.elapsed_time(b), 1e-3)))):
-            fn()
-        per = []
-        for _ in range(5):
-            a, b = ev(), ev()
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(per_burst):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            per.append(a.elapsed_time(b) / per_burst)
-        return sorted(per)[2]
-
+    timed = lambda fn, per_burst: burst_median(torch, stream, fn, per_burst)
     q = timed(lambda: sq.quantize_fused(H, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, A16, A8),
               16)
     gm = timed(lambda: sq.fp8_gemm_scaled(A8, sq.E4M3, W8, sq.E4M3, sq.PER_TENSOR,
@@ -790,6 +796,50 @@ def large_config(sq, torch, dev, args):
                                       "frac_of_hbm_peak": round(dyb / (dy * 1e-3) / 1e9
                                                                 / HBM_PEAK_GBS, 4)}}
     del H, A16, A8, W8, DY, DY8, Y
+    torch.cuda.empty_cache()
+    return out
+
+
+def fine_grained(sq, torch, dev, args):
+    """The fine-grained configuration at full size: H[65536 x 4096] with
+    Student-t (nu = 3) values (z / sqrt(chi2_3 / 3) from torch's seeded device
+    generator) cast with current per-128-group scales (identity, E4M3 codes
+    and one FP32 inverse scale per 1 x 128 group, no BF16 copy); W[1024 x 4096]
+    ~ N(0, 0.02) cast with 128 x 128 block scales; the per-group GEMM
+    Y[65536 x 1024] = A8 x W8^T promoting every 128-wide partial sum by
+    sa[m, g] sb[n / 128, g].  Timed like the large configuration's kernels."""
+    M, K, N = 65536, 4096, 1024
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    g.manual_seed(30303)
+    z = torch.randn((M, K), generator=g, device=dev)
+    chi2 = torch.zeros_like(z)
+    for _ in range(3):
+        chi2 += torch.randn((M, K), generator=g, device=dev) ** 2
+    H = (z / torch.sqrt(chi2 / 3.0)).to(torch.bfloat16)
+    del z, chi2
+    A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    GS = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    W8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    sq.quantize_weight(W, sq.E4M3, sq.PER_GROUP128, W8, ws)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    q = burst_median(torch, stream, lambda: sq.quantize_fused(
+        H, sq.ACT_IDENTITY, sq.E4M3, sq.PER_GROUP128, None, None, A8, GS), 16)
+    gm = burst_median(torch, stream, lambda: sq.fp8_gemm_scaled(
+        A8, sq.E4M3, W8, sq.E4M3, sq.PER_GROUP128, GS, ws, Y), 4)
+    qb, fl = M * K * 3 + M * (K // 128) * 4, 2 * M * N * K
+    out = {"shape": f"H[{M}x{K}] student-t -> e4m3 + per-128 group scales; "
+                    f"Y[{M}x{N}] = A8 x W8[{N}x{K}]^T with 128 x 128 weight blocks",
+           "quantize_fused_per_group": {
+               "ms": round(q, 4), "GB/s": round(qb / (q * 1e-3) / 1e9, 1),
+               "bytes_per_launch": qb,
+               "frac_of_hbm_peak": round(qb / (q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "fp8_gemm_scaled_per_group": {
+               "ms": round(gm, 4), "TFLOP/s": round(fl / (gm * 1e-3) / 1e12, 1),
+               "frac_of_fp8_peak": round(fl / (gm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}}
+    del H, A8, GS, W, W8, Y
     torch.cuda.empty_cache()
     return out
 
