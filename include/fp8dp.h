@@ -174,8 +174,10 @@ int amax_history_update(fp8dp_tensor_state* st, hipStream_t stream);
  * accum selects how products are summed (fp8dp_accum above).
  * For delayed scaling, pass &st_a->scale_inv when the GEMM is enqueued before
  * amax_history_update of that step, or &st_a->scale_inv_used after it.
- * Errors: EINVAL for NULL pointers, M, N or K not positive multiples of 128,
- * misaligned pointers, bad formats, mode or accum. */
+ * M is any positive row count (the number of tokens need not fill a tile);
+ * N and K are multiples of 128.  Only rows 0 .. M-1 of y are written.
+ * Errors: EINVAL for NULL pointers, M < 1, N or K not positive multiples of
+ * 128, misaligned pointers, bad formats, mode or accum. */
 int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
                     int64_t M, int64_t N, int64_t K, fp8dp_scale_mode mode, fp8dp_accum accum,
                     const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,

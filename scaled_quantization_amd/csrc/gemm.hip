@@ -69,8 +69,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBM * kBK];
   __shared__ float lds_sa[2][kBM];
 
+  // M may be ragged: the last row tile reads row M - 1 in place of the rows
+  // past the end and does not store them
   const int tiles_n = N / kBN;
-  const int ntiles = (M / kBM) * tiles_n;
+  const int ntiles = ((M + kBM - 1) / kBM) * tiles_n;
   const int tile = tile_of_block(blockIdx.x, ntiles);
   const int m0 = (tile / tiles_n) * kBM;
   const int n0 = (tile % tiles_n) * kBN;
@@ -85,24 +87,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
   // Global -> register staging: thread t moves chunks t + 256 i (i = 0..3) of
   // each 128 x 128-byte tile: row (t + 256 i) / 8, 16-byte chunk t % 8.
   const int srow = tid >> 3, sch = tid & 7;
-  const uint8_t* gA = A + (size_t)(m0 + srow) * K + sch * 16;
+  auto a_row = [&](int r) { return A + (size_t)(r < M ? r : M - 1) * K + sch * 16; };
+  const uint8_t* const gA0 = a_row(m0 + srow);
+  const uint8_t* const gA1 = a_row(m0 + srow + 32);
+  const uint8_t* const gA2 = a_row(m0 + srow + 64);
+  const uint8_t* const gA3 = a_row(m0 + srow + 96);
   const uint8_t* gB = B + (size_t)(n0 + srow) * K + sch * 16;
   const size_t gstep = (size_t)32 * K;   // 256 threads / 8 chunks = 32 rows apart
+  const int sa_row = (m0 + (tid & (kBM - 1))) < M ? m0 + (tid & (kBM - 1)) : M - 1;
   u32x4_t ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
   float rsa = 0.0f;
 #define FP8DP_GLOAD(kt)                                                                  \
   do {                                                                                   \
     const size_t k0 = (size_t)(kt) * kBK;                                                \
-    ra0 = *reinterpret_cast<const u32x4_t*>(gA + k0);                                    \
-    ra1 = *reinterpret_cast<const u32x4_t*>(gA + gstep + k0);                            \
-    ra2 = *reinterpret_cast<const u32x4_t*>(gA + 2 * gstep + k0);                        \
-    ra3 = *reinterpret_cast<const u32x4_t*>(gA + 3 * gstep + k0);                        \
+    ra0 = *reinterpret_cast<const u32x4_t*>(gA0 + k0);                                   \
+    ra1 = *reinterpret_cast<const u32x4_t*>(gA1 + k0);                                   \
+    ra2 = *reinterpret_cast<const u32x4_t*>(gA2 + k0);                                   \
+    ra3 = *reinterpret_cast<const u32x4_t*>(gA3 + k0);                                   \
     rb0 = *reinterpret_cast<const u32x4_t*>(gB + k0);                                    \
     rb1 = *reinterpret_cast<const u32x4_t*>(gB + gstep + k0);                            \
     rb2 = *reinterpret_cast<const u32x4_t*>(gB + 2 * gstep + k0);                        \
     rb3 = *reinterpret_cast<const u32x4_t*>(gB + 3 * gstep + k0);                        \
     if constexpr (MODE == FP8DP_PER_GROUP128) {                                          \
-      if (tid < kBM) rsa = sa[(size_t)(m0 + tid) * kgroups + (kt)];                      \
+      if (tid < kBM) rsa = sa[(size_t)sa_row * kgroups + (kt)];                          \
     }                                                                                    \
   } while (0)
 #define FP8DP_SSTORE(buf)                                                                \
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
         const int row = m0 + wm + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int col = n0 + wn + j * 32 + (lane & 31);
         const float v = (MODE == FP8DP_PER_TENSOR) ? acc[i][j][r] * f : acc[i][j][r];
-        Y[(size_t)row * N + col] = (uint16_t)bf16_rne_int(v);
+        if (row < M) Y[(size_t)row * N + col] = (uint16_t)bf16_rne_int(v);
       }
 }
 
@@ -1037,7 +1044,7 @@ static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int6
 template <int FA, int FB, int MODE, bool EXACT>
 static void launch_gemm_t(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                           const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((M / kBM) * (N / kBN));
+  const unsigned blocks = (unsigned)(((M + kBM - 1) / kBM) * (N / kBN));
   hipLaunchKernelGGL((k_gemm<FA, FB, MODE, EXACT>), dim3(blocks), dim3(kGemmThreads), 0, stream,
                      a, b, (int)M, (int)N, (int)K, sa, sb, y);
 }
@@ -1047,15 +1054,30 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
                        fp8dp_scale_mode mode, fp8dp_accum accum, const float* sa, const float* sb,
                        uint16_t* y, hipStream_t stream) {
   const bool exact = accum == FP8DP_ACCUM_EXACT;
-  if (mode == FP8DP_PER_TENSOR && !exact && M % 256 == 0) {
-    // the widest tile that divides N (one workgroup per compute unit at a time)
-    if (N % 192 == 0) return launch_big<FA, FB, 3>(a, b, M, N, K, sa, sb, y, stream);
-    if (N % 256 == 0) return launch_big<FA, FB, 4>(a, b, M, N, K, sa, sb, y, stream);
-    return launch_big<FA, FB, 2>(a, b, M, N, K, sa, sb, y, stream);
+  // The large-tile kernels take the rows that fill whole 256-row tiles; the
+  // rest (M % 256 rows, any M) go to the small-tile kernel, which masks the
+  // rows past M.  Each output row comes from one kernel, so a row's value
+  // does not depend on M beyond which kernel computed it.
+  const int64_t Mb = M / 256 * 256;
+  const bool big_t = mode == FP8DP_PER_TENSOR && !exact;
+  const bool big_g = mode == FP8DP_PER_GROUP128 && !exact && K % 512 == 0 && aligned16(sa) &&
+                     aligned16(sb);
+  if (Mb > 0 && (big_t || big_g)) {
+    int rc;
+    if (big_g)
+      rc = launch_pg<FA, FB>(a, b, Mb, N, K, sa, sb, y, stream);
+    else if (N % 192 == 0)   // the widest tile that divides N
+      rc = launch_big<FA, FB, 3>(a, b, Mb, N, K, sa, sb, y, stream);
+    else if (N % 256 == 0)
+      rc = launch_big<FA, FB, 4>(a, b, Mb, N, K, sa, sb, y, stream);
+    else
+      rc = launch_big<FA, FB, 2>(a, b, Mb, N, K, sa, sb, y, stream);
+    if (rc != FP8DP_OK || Mb == M) return rc;
+    a += Mb * K;
+    y += Mb * N;
+    if (big_g) sa += Mb * (K / 128);
+    M -= Mb;
   }
-  if (mode == FP8DP_PER_GROUP128 && !exact && M % 256 == 0 && K % 512 == 0 && aligned16(sa) &&
-      aligned16(sb))
-    return launch_pg<FA, FB>(a, b, M, N, K, sa, sb, y, stream);
   if (mode == FP8DP_PER_TENSOR) {
     if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);
     else launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a, b, M, N, K, sa, sb, y, stream);
@@ -1080,13 +1102,13 @@ extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t*
     set_error("fp8_gemm_scaled: NULL pointer argument");
     return FP8DP_EINVAL;
   }
-  if (M < kBM || N < kBN || K < kBK || M % kBM || N % kBN || K % kBK) {
-    set_error("fp8_gemm_scaled: M, N, K must be positive multiples of 128 (got %lld, %lld, %lld)",
-              (long long)M, (long long)N, (long long)K);
+  if (M < 1 || N < kBN || K < kBK || N % kBN || K % kBK) {
+    set_error("fp8_gemm_scaled: M must be positive, N and K positive multiples of 128 (got %lld, "
+              "%lld, %lld)", (long long)M, (long long)N, (long long)K);
     return FP8DP_EINVAL;
   }
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
-      (M / kBM) * (N / kBN) > (int64_t)0x7FFFFFFF) {
+      ((M + kBM - 1) / kBM) * (N / kBN) > (int64_t)0x7FFFFFFF) {
     set_error("fp8_gemm_scaled: shape too large");
     return FP8DP_EINVAL;
   }

@@ -61,6 +61,8 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1
     rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 100, 0, 0, 16, 16, 16, None)
     assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled(16, 0, 16, 0, 0, 128, 128, 0, 0, 16, 16, 16, None)
+    assert rc == -1 and b"M must be positive" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled(16, 0, 16, 3, 128, 128, 128, 0, 0, 16, 16, 16, None)
     assert rc == -1 and b"format" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled(None, 0, 16, 0, 128, 128, 128, 0, 0, 16, 16, 16, None)

@@ -307,6 +307,42 @@ def test_group_scaled_shapes(M, N, K, fa, fb):
            max_plain_violation_frac=1e-3)
 
 
+# Ragged M (a token count that does not fill a tile): the rows that fill
+# whole 256-row tiles run on the large-tile kernels, the rest on the small-tile
+# kernel, which reads row M - 1 in place of rows past the end and does not
+# store them.  Rows past M in the output buffer must keep their contents; rows
+# below the last whole tile must equal the product of those rows alone, bit
+# for bit (the same kernel computes them); every row meets the bound.
+@pytest.mark.parametrize("M", [1, 37, 128, 255, 333, 4096 + 77])
+@pytest.mark.parametrize("mode,accum", [(sq.PER_TENSOR, FP8), (sq.PER_GROUP128, FP8),
+                                        (sq.PER_TENSOR, EXACT)],
+                         ids=["tensor", "group", "tensor-exact"])
+def test_ragged_rows(M, mode, accum):
+    N, K = 384, 1024
+    a8, w8, sa, sb = _group_case(M, N, K, 0, 0)
+    if mode == sq.PER_TENSOR:
+        sa, sb = np.float32(0.75), np.float32(3.0)
+    guard = 3
+    y_all = torch.empty((M + guard, N), dtype=torch.bfloat16, device=DEV)
+    y_all.view(torch.int16).fill_(0x7FC1)   # a NaN pattern no output can take
+    sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(w8), 0, mode, _dev_f32(1 / sa),
+                       _dev_f32(1 / sb), y_all[:M], accum)
+    bits = y_all.view(torch.int16).cpu().numpy()
+    assert np.all(bits[M:] == 0x7FC1), "rows past M were written"
+    y = y_all[:M].float().cpu().numpy()
+    rows = np.arange(M) if M <= 512 else np.unique(np.concatenate(
+        [np.arange(0, M, 61), np.arange(M - 90, M)]))
+    ref, absref = O.gemm_f64(a8, 0, w8, 0, mode, sa, sb, rows=rows)
+    allow = None if accum == EXACT else fp8_mfma_allowance(a8, 0, w8, 0, mode, sa, sb, rows)
+    _check(y[rows], ref, absref, f"ragged M={M} mode={mode}", allow,
+           max_plain_violation_frac=1e-3)
+    Mb = M // 256 * 256
+    if Mb > 0 and accum == FP8:
+        sa_b = sa if mode == sq.PER_TENSOR else sa[:Mb]
+        y_b = _gemm(a8[:Mb], 0, w8, 0, mode, 1 / sa_b, 1 / sb, accum)
+        assert np.array_equal(y[:Mb].view(np.uint32), y_b.view(np.uint32))
+
+
 # On a 256-CU GPU these shapes take the 256 x 192 per-group tiles (one round
 # of 256 tiles where 256 x 128 tiles need two); their column halves take the
 # 256 x 128 tiles.  Each output's arithmetic does not depend on which tile
