@@ -128,6 +128,31 @@ def test_fine_grained_block_scaled_gemm_sampled_rows(accum):
 
 
 @pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+def test_gpt2_per_group_gemm_full_size_sampled_rows(accum):
+    # the benchmark's per-group launch: the GPT-2 activation (relu2) cast with
+    # per-128 group scales, the weight with 128 x 128 block scales; in FP8
+    # mode on a 256-CU GPU this shape runs the 256 x 192 per-group tiles
+    w = workloads.get("gpt2")
+    r = oracle_quantize(w.h0(), O.ACT_RELU2, O.E4M3, O.PER_GROUP128, want_bf16=False)
+    q_w, si_w, s_w = O.quantize_weight_blocks(w.weight(), O.E4M3, with_scale=True)
+    y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_scaled(to_dev_u8(r.fp8), 0, to_dev_u8(q_w), 0, sq.PER_GROUP128,
+                       torch.from_numpy(r.group_scale_inv).to(DEV),
+                       torch.from_numpy(si_w).to(DEV), y, accum)
+    yv = y.float().cpu().numpy()
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(w.M, size=128, replace=False))
+    rows[0], rows[-1] = 0, w.M - 1
+    ref, absref = oracle_gemm_rows(r.fp8, O.E4M3, q_w, O.E4M3, O.PER_GROUP128, r.group_scale,
+                                   s_w, rows)
+    allow = None
+    if accum == FP8:
+        allow = fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, r.group_scale, s_w, rows)
+    _check(yv[rows], ref, absref, "gpt2 per-group", allow, max_plain_violation_frac=1e-3)
+    assert np.isfinite(yv).all()
+
+
+@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
 @pytest.mark.parametrize("K", [128, 256, 1024, 4096, 16384])
 def test_random_full_range_codes_over_long_k(K, accum):
     # every finite code equally likely: products span ~2^36, the hardest case
