@@ -449,7 +449,7 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
            "dgrad": {"shape": f"dY8[{M}x{N}] e5m2 x W8^T[{K}x{N}] e4m3 -> [{M}x{K}]",
                      "ms": round(t_dgrad, 5), "TFLOP/s": round(flops / (t_dgrad * 1e-3) / 1e12, 1)},
            "wgrad": {"shape": f"dY8^T[{N}x{M}] e5m2 x A8^T[{K}x{M}] e4m3 -> [{N}x{K}]"}}
-    for splits in (1, 4, 8, 16):
+    for splits in (1, 4, 5, 8, 16):
         t = timed(lambda: sq.fp8_gemm_scaled_splitk(dyt, sq.E5M2, at, sq.E4M3, splits, si_g, si_a,
                                                     ws, dw))
         res["wgrad"][f"splits_{splits}"] = {"ms": round(t, 5),

@@ -187,8 +187,9 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
  * over `splits` workgroups per output tile, for outputs too small to fill the
  * GPU on their own -- the weight-gradient GEMM of the FP8 recipe ("FP8
  * Training & Inference", FP8 Training Recipe) has a [N x K] output and a
- * contraction over all tokens.  Split s sums k in [s K/splits, (s+1)
- * K/splits) into workspace[s][m][n] (FP32, unscaled); a second kernel adds
+ * contraction over all tokens.  With KS = K/128 blocks of 128 k, split s
+ * sums the blocks [floor(s KS/splits), floor((s+1) KS/splits)) into
+ * workspace[s][m][n] (FP32, unscaled); a second kernel adds
  * the splits in order s = 0, 1, ... and writes
  *   y = bf16_rne((sum_s workspace[s]) * a_scale_inv[0] * b_scale_inv[0]),
  * so the result is deterministic; with splits = 1 it equals fp8_gemm_scaled
@@ -196,8 +197,8 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
  * workspace: caller-owned device memory of splits * M * N floats, 16-byte
  * aligned; its contents are overwritten.
  * Errors: EINVAL for NULL pointers, splits outside 1..64, M not a positive
- * multiple of 256, N of 128, K of 128 * splits, misaligned pointers or a bad
- * format. */
+ * multiple of 256, N or K not of 128, K < 128 * splits, misaligned pointers
+ * or a bad format. */
 int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
                            int64_t M, int64_t N, int64_t K, int32_t splits,
                            const float* a_scale_inv, const float* b_scale_inv, float* workspace,

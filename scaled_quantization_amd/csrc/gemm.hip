@@ -277,9 +277,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
 // deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
 // the two waves of each SIMD with a barrier per phase were all slower.
 // SPLIT: workgroup u of (M/256)(N/BN) x splits runs split s = u' / ntiles of
-// tile u' % ntiles (u' = the XCD-ordered index), over K bytes
-// [s K/splits, (s+1) K/splits), and writes its FP32 sums, unscaled, to
-// ws[s][m][n]; k_splitk_reduce then adds the splits in order.
+// tile u' % ntiles (u' = the XCD-ordered index), over the 128-byte stages
+// [s KS/splits, (s+1) KS/splits) of the KS = K/128, and writes its FP32 sums,
+// unscaled, to ws[s][m][n]; k_splitk_reduce then adds the splits in order.
 // MX: microscaled operands (32-value blocks along k, E8M0 block exponents
 // ea [M x K/32], eb [N x K/32]).  A stage's 128 k bytes are 4 blocks, so each
 // tile row needs one dword of exponents per stage: waves 0-3 copy the 256 A
@@ -372,8 +372,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = (wave >> 1) * 64;
   const int wc = (wave & 1) * (BN / 2);
-  const int KT = K / kBK / (SPLIT ? splits : 1);
-  const size_t kbase = (size_t)split * KT * kBK;
+  // SPLIT: split s runs stages [s KS / splits, (s + 1) KS / splits) of the
+  // KS = K / 128 stages (equal ranges when splits divides KS)
+  const int KS = K / kBK;
+  const int s0 = SPLIT ? (int)((int64_t)split * KS / splits) : 0;
+  const int KT = SPLIT ? (int)((int64_t)(split + 1) * KS / splits) - s0 : KS;
+  const size_t kbase = (size_t)s0 * kBK;
   const int GS = PER ? tiles_of_block(blockIdx.x, gridDim.x, ntiles) * KT : KT;   // stages to run
   if (GS == 0) return;   // (a persistent grid has no more workgroups than tiles)
 
@@ -1147,11 +1151,10 @@ extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const u
     set_error("fp8_gemm_scaled_splitk: splits must be in 1..64 (got %d)", (int)splits);
     return FP8DP_EINVAL;
   }
-  if (M < 256 || N < 128 || K < 128 * (int64_t)splits || M % 256 || N % 128 ||
-      K % (128 * (int64_t)splits)) {
-    set_error("fp8_gemm_scaled_splitk: M must be a positive multiple of 256, N of 128 and K of "
-              "128 * splits (got %lld, %lld, %lld, splits %d)", (long long)M, (long long)N,
-              (long long)K, (int)splits);
+  if (M < 256 || N < 128 || K < 128 * (int64_t)splits || M % 256 || N % 128 || K % 128) {
+    set_error("fp8_gemm_scaled_splitk: M must be a positive multiple of 256, N and K of 128, "
+              "K at least 128 * splits (got %lld, %lld, %lld, splits %d)", (long long)M,
+              (long long)N, (long long)K, (int)splits);
     return FP8DP_EINVAL;
   }
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||

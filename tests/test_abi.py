@@ -101,8 +101,10 @@ def test_argument_checks_reject_without_launching(L):
     # fp8_gemm_scaled_splitk(a, fa, b, fb, M, N, K, splits, sa, sb, ws, y, stream)
     rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 0, 16, 16, 16, 16, None)
     assert rc == -1 and b"splits" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 384, 2, 16, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 128, 2, 16, 16, 16, 16, None)
     assert rc == -1 and b"128 * splits" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 200, 1, 16, 16, 16, 16, None)
+    assert rc == -1 and b"of 128" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, None, 16, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, 24, 16, None)

@@ -85,8 +85,12 @@ def test_splitk_one_split_equals_gemm_and_is_deterministic(M, N, K):
     assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
 
 
+# the last three: splits that do not divide K / 128 (uneven stage ranges,
+# down to one stage per split)
 @pytest.mark.parametrize("M,N,K,splits,fa,fb", [(256, 384, 1024, 2, 0, 0), (768, 3072, 4096, 4, 1, 0),
-                                                (512, 512, 4096, 8, 1, 1), (256, 128, 256, 2, 0, 1)])
+                                                (512, 512, 4096, 8, 1, 1), (256, 128, 256, 2, 0, 1),
+                                                (256, 384, 640, 3, 0, 0), (768, 3072, 4096, 5, 1, 0),
+                                                (256, 256, 896, 7, 1, 1)])
 def test_splitk_vs_oracle(M, N, K, splits, fa, fb):
     rng = np.random.default_rng(3 * M + N + K + splits)
     a8, w8 = _codes(rng, (M, K), fa), _codes(rng, (N, K), fb)
@@ -138,7 +142,7 @@ def test_gpt2_dgrad(gpt2_codes):
     _check(dx.float().cpu().numpy()[rows], ref, absref, None, "dgrad exact")
 
 
-@pytest.mark.parametrize("splits", [4, 8])
+@pytest.mark.parametrize("splits", [4, 5, 8])
 def test_gpt2_wgrad(gpt2_codes, splits):
     a8, s_a, w8, s_w, dy8, s_dy = gpt2_codes
     M, K = a8.shape            # 16384 x 3072
