@@ -49,29 +49,33 @@ inline unsigned grid_for(int64_t work_items, int block_threads, int blocks_per_c
 
 // Launch forms of the element-wise kernels over n8 8-element vectors:
 //   kFormOne  -- a thread per vector, no loop (kernels that write at least as
-//                many bytes as they read);
+//                many bytes as they read, and small read-heavy launches);
 //   kFormPair -- two vectors per thread, vectors b*2T + t and b*2T + T + t of
 //                block b (T threads), both loaded first, no loop (kernels that
-//                read more than they write);
+//                read more than they write, from kPairMinVectors vectors on);
 //   kFormLoop -- grid-stride loop over a capped grid, where the grid of the
 //                other forms would exceed the grid cap or a set grid limit.
 // Measured at the GPT-2 shape and on a 512 MiB gradient (E5M2 cast):
 // one vector per thread is 5% faster than two for the quantizer with its BF16
 // copy; for the cast without it two per thread match the loop at 96 MiB and
 // beat it by 30% at 512 MiB (6.56 vs 5.03 TB/s); one per thread is 7-22% slower
-// than the loop there.
+// than the loop there.  Below about 2^21 vectors one per thread wins for
+// read-heavy kernels too (E5M2 cast of a [16384 x 768] gradient, 1.6 M
+// vectors: 9.12 us against 9.52 with two; at [65536 x 4096] two win, 124.1
+// against 134.7 us; at 6.3 M vectors the cast without the BF16 copy ties).
 enum : int { kFormLoop = 0, kFormOne = 1, kFormPair = 2 };
+constexpr int64_t kPairMinVectors = (int64_t)1 << 21;
 struct LaunchShape {
   unsigned grid;
   int form;
 };
 inline LaunchShape launch_shape(int64_t n8, int block_threads, bool write_heavy,
                                 int loop_blocks_per_cu) {
-  const int per = write_heavy ? 1 : 2;
+  const int per = write_heavy || n8 < kPairMinVectors ? 1 : 2;
   int64_t need = (n8 + (int64_t)per * block_threads - 1) / ((int64_t)per * block_threads);
   if (need < 1) need = 1;
   const unsigned g = grid_for(need * block_threads, block_threads, 1 << 20);
-  if ((int64_t)g == need) return {g, write_heavy ? kFormOne : kFormPair};
+  if ((int64_t)g == need) return {g, per == 1 ? kFormOne : kFormPair};
   return {grid_for(n8 > 0 ? n8 : 1, block_threads, loop_blocks_per_cu), kFormLoop};
 }
 
