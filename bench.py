@@ -761,7 +761,7 @@ def large_config(sq, torch, dev, args):
     A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
     W = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
     W8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    wsc = torch.empty(1, dtype=torch.float32, device=dev)
+    wsc = torch.empty(2, dtype=torch.float32, device=dev)   # [1/s, s]
     sq.quantize_weight(W, sq.E4M3, sq.PER_TENSOR, W8, wsc)
     del W
     DY = (torch.exp(3.0 * torch.randn((M, N), generator=g, device=dev, dtype=torch.float32))

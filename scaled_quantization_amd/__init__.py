@@ -313,6 +313,11 @@ def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,
                     stream=None) -> None:
     N, K = w.shape
+    if isinstance(scale_out, torch.Tensor):
+        need = 2 if mode == PER_TENSOR else (N // 128) * (K // 128)
+        if scale_out.dtype != torch.float32 or scale_out.numel() < need:
+            raise Fp8dpError(f"quantize_weight: scale_out needs {need} float32 values "
+                             "(per tensor: [1/s, s]; per group: one per 128 x 128 block)")
     _check(lib().quantize_weight(_p(w), N, K, fmt, mode, _p(w8), _p(scale_out), _stream(stream)),
            "quantize_weight")
 

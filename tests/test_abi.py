@@ -130,6 +130,18 @@ def test_binding_refuses_host_tensors(L):
                           stream=0)
 
 
+def test_binding_checks_weight_scale_buffer(L):
+    # a per-tensor weight cast writes [1/s, s]; a one-float buffer is refused
+    # before anything is launched
+    import torch
+    w = torch.zeros(128, 256, dtype=torch.bfloat16)
+    w8 = torch.zeros(128, 256, dtype=torch.uint8)
+    with pytest.raises(sq.Fp8dpError, match="2 float32"):
+        sq.quantize_weight(w, sq.E4M3, sq.PER_TENSOR, w8, torch.zeros(1))
+    with pytest.raises(sq.Fp8dpError, match="2 float32"):
+        sq.quantize_weight(w, sq.E4M3, sq.PER_GROUP128, w8, torch.zeros(1))
+
+
 def test_mx_argument_checks_reject_without_launching(L):
     rc = L.quantize_mx(16, 4, 48, 0, 0, None, 16, 16, None)
     assert rc == -1 and b"32" in L.fp8dp_last_error()
