@@ -167,6 +167,12 @@ class TensorState:
         return self.buf.cpu().numpy().tobytes()
 
 
+def _room(t, nbytes: int, what: str) -> None:
+    """Refuse a tensor argument smaller than the nbytes the call writes or reads."""
+    if isinstance(t, torch.Tensor) and t.numel() * t.element_size() < nbytes:
+        raise Fp8dpError(f"{what}: needs {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
 def _state_ptr(st) -> Optional[int]:
     if st is None:
         return None
@@ -187,6 +193,10 @@ def quantize_fused(h: torch.Tensor, act: int, fmt: int, mode: int, st=None,
                    stream=None) -> None:
     """h: BF16 (or 16-bit) device tensor [rows, cols] (1-D counts as one row)."""
     rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    _room(bf16_out, rows * cols * 2, "quantize_fused: bf16_out")
+    _room(fp8_out, rows * cols, "quantize_fused: fp8_out")
+    if mode == PER_GROUP128:
+        _room(group_scale_inv, rows * (cols // 128) * 4, "quantize_fused: group_scale_inv")
     _check(lib().quantize_fused(_p(h), rows, cols, act, fmt, mode, _state_ptr(st), _p(bf16_out),
                                 _p(fp8_out), _p(group_scale_inv), _stream(stream)),
            "quantize_fused")
@@ -205,6 +215,10 @@ def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: in
     N = b.shape[0]
     if b.shape[1] != K or tuple(y.shape) != (M, N):
         raise Fp8dpError("fp8_gemm_scaled: shape mismatch")
+    group = mode == PER_GROUP128
+    _room(a_scale_inv, (M * (K // 128) if group else 1) * 4, "fp8_gemm_scaled: a_scale_inv")
+    _room(b_scale_inv, ((N // 128) * (K // 128) if group else 1) * 4,
+          "fp8_gemm_scaled: b_scale_inv")
     _check(lib().fp8_gemm_scaled(_p(a), fa, _p(b), fb, M, N, K, mode, accum, _p(a_scale_inv),
                                  _p(b_scale_inv), _p(y), _stream(stream)), "fp8_gemm_scaled")
 
@@ -330,6 +344,9 @@ def gemm_bf16_quantize_fused(x: torch.Tensor, w: torch.Tensor, act: int = ACT_RE
     N = w.shape[0]
     if w.shape[1] != K:
         raise Fp8dpError("gemm_bf16_quantize_fused: shape mismatch")
+    _room(h_out, M * N * 2, "gemm_bf16_quantize_fused: h_out")
+    _room(bf16_out, M * N * 2, "gemm_bf16_quantize_fused: bf16_out")
+    _room(fp8_out, M * N, "gemm_bf16_quantize_fused: fp8_out")
     _check(lib().gemm_bf16_quantize_fused(_p(x), _p(w), M, N, K, act, fmt, _state_ptr(st),
                                           _p(h_out), _p(bf16_out), _p(fp8_out), _stream(stream)),
            "gemm_bf16_quantize_fused")

@@ -142,6 +142,24 @@ def test_binding_checks_weight_scale_buffer(L):
         sq.quantize_weight(w, sq.E4M3, sq.PER_GROUP128, w8, torch.zeros(1))
 
 
+def test_binding_checks_output_and_scale_sizes(L):
+    # outputs and scale arrays smaller than the call would write or read are
+    # refused before anything is launched
+    import torch
+    h = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(sq.Fp8dpError, match="fp8_out"):
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, None, None,
+                          torch.zeros(1000, dtype=torch.uint8))
+    with pytest.raises(sq.Fp8dpError, match="group_scale_inv"):
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, None, None,
+                          torch.zeros(1024, dtype=torch.uint8), torch.zeros(7))
+    a8 = torch.zeros(256, 512, dtype=torch.uint8)
+    w8 = torch.zeros(128, 512, dtype=torch.uint8)
+    y = torch.zeros(256, 128, dtype=torch.bfloat16)
+    with pytest.raises(sq.Fp8dpError, match="a_scale_inv"):
+        sq.fp8_gemm_scaled(a8, 0, w8, 0, sq.PER_GROUP128, torch.zeros(4), torch.zeros(4), y)
+
+
 def test_mx_argument_checks_reject_without_launching(L):
     rc = L.quantize_mx(16, 4, 48, 0, 0, None, 16, 16, None)
     assert rc == -1 and b"32" in L.fp8dp_last_error()
