@@ -61,7 +61,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
