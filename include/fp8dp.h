@@ -283,10 +283,10 @@ int quantize_recompute(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act 
  * *run_flag != 0, read on the GPU -- the GEMM half of the recompute above:
  * pass &st->overflow of the operand whose cast overflowed and
  * &st->scale_inv (the corrected scale's inverse).  With *run_flag == 0 y is
- * untouched.
- * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
- * not of 128, misaligned pointers (operands 16 bytes, scales and flag 4), or
- * a bad format. */
+ * untouched.  Any M >= 1, as fp8_gemm_scaled; N and K multiples of 128.
+ * Errors: EINVAL for NULL pointers, M < 1, N or K not positive multiples of
+ * 128, misaligned pointers (operands 16 bytes, scales and flag 4), or a bad
+ * format. */
 int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
                        int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
                        const float* b_scale_inv, uint16_t* y, const uint32_t* run_flag,

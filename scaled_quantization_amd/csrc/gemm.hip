@@ -65,7 +65,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restr
                                                           int N, int K,
                                                           const float* __restrict__ sa,
                                                           const float* __restrict__ sb,
-                                                          uint16_t* __restrict__ Y) {
+                                                          uint16_t* __restrict__ Y,
+                                                          const uint32_t* run_flag = nullptr) {
+  // run_flag: the conditional GEMM's flag (a device word); zero leaves Y untouched
+  if (run_flag != nullptr && *run_flag == 0u) return;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBM * kBK];
   __shared__ float lds_sa[2][kBM];
 
@@ -1047,10 +1050,11 @@ static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int6
 
 template <int FA, int FB, int MODE, bool EXACT>
 static void launch_gemm_t(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                          const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
+                          const float* sa, const float* sb, uint16_t* y, hipStream_t stream,
+                          const uint32_t* run_flag = nullptr) {
   const unsigned blocks = (unsigned)(((M + kBM - 1) / kBM) * (N / kBN));
   hipLaunchKernelGGL((k_gemm<FA, FB, MODE, EXACT>), dim3(blocks), dim3(kGemmThreads), 0, stream,
-                     a, b, (int)M, (int)N, (int)K, sa, sb, y);
+                     a, b, (int)M, (int)N, (int)K, sa, sb, y, run_flag);
 }
 
 template <int FA, int FB>
@@ -1090,6 +1094,23 @@ static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N,
     else launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, false>(a, b, M, N, K, sa, sb, y, stream);
   }
   return check_launch("fp8_gemm_scaled");
+}
+
+// fp8_gemm_scaled_if over any M: the same split of rows as launch_gemm (whole
+// 256-row tiles on the large-tile kernel, the rest on the small-tile one),
+// both reading the flag, so a run gives fp8_gemm_scaled's output bit for bit
+template <int FA, int FB>
+static int launch_cond_rows(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
+                            hipStream_t stream) {
+  const int64_t Mb = M / 256 * 256;
+  if (Mb > 0) {
+    const int rc = launch_cond_tile<FA, FB>(a, b, Mb, N, K, sa, sb, y, flag, stream);
+    if (rc != FP8DP_OK || Mb == M) return rc;
+  }
+  launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a + Mb * K, b, M - Mb, N, K, sa, sb, y + Mb * N,
+                                                 stream, flag);
+  return check_launch("fp8_gemm_scaled_if");
 }
 
 }  // namespace fp8dp
@@ -1226,13 +1247,13 @@ extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8
     set_error("fp8_gemm_scaled_if: NULL pointer argument");
     return FP8DP_EINVAL;
   }
-  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
-    set_error("fp8_gemm_scaled_if: M must be a positive multiple of 256, N and K of 128 (got "
+  if (M < 1 || N < 128 || K < 128 || N % 128 || K % 128) {
+    set_error("fp8_gemm_scaled_if: M must be positive, N and K positive multiples of 128 (got "
               "%lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
     return FP8DP_EINVAL;
   }
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
-      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
+      ((M + 127) / 128) * (N / 128) > (int64_t)0x7FFFFFFF) {
     set_error("fp8_gemm_scaled_if: shape too large");
     return FP8DP_EINVAL;
   }
@@ -1249,12 +1270,12 @@ extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8
     return FP8DP_EINVAL;
   }
   if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_cond_tile<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+    return launch_cond_rows<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
   if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_cond_tile<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+    return launch_cond_rows<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
   if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_cond_tile<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
-  return launch_cond_tile<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+    return launch_cond_rows<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+  return launch_cond_rows<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
 }
 
 extern "C" int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const uint8_t* b,

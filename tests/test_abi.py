@@ -184,8 +184,10 @@ def test_recompute_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, None, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 128, 128, 128, 16, 16, 16, 16, None)
-    assert rc == -1 and b"256" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 0, 128, 128, 16, 16, 16, 16, None)
+    assert rc == -1 and b"M must be positive" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 128, 100, 128, 16, 16, 16, 16, None)
+    assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 18, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
 

@@ -125,3 +125,28 @@ def test_recompute_is_a_no_op_without_overflow():
     sq.fp8_gemm_scaled_if(q, 0, w8, 0, one, one, y, st.field_ptr("overflow"))
     torch.cuda.synchronize()
     assert (sentinel == 0x5A).all() and (y == 7.0).all()
+
+
+@pytest.mark.parametrize("M", [100, 256 + 77])
+def test_conditional_gemm_ragged_rows(M):
+    # any row count, as fp8_gemm_scaled: with the flag clear the output stays
+    # untouched; with it set the output is fp8_gemm_scaled's, bit for bit
+    # (the same split of rows over the same kernels)
+    rng = np.random.default_rng(M)
+    K, N = 512, 384
+    codes = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E4M3))).astype(np.uint8)
+    a = torch.from_numpy(rng.choice(codes, (M, K))).to(DEV)
+    w = torch.from_numpy(rng.choice(codes, (N, K))).to(DEV)
+    sa = torch.tensor([0.5], dtype=torch.float32, device=DEV)
+    sb = torch.tensor([0.25], dtype=torch.float32, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    sq.fp8_gemm_scaled_if(a, 0, w, 0, sa, sb, y, flag)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+    flag.fill_(1)
+    sq.fp8_gemm_scaled_if(a, 0, w, 0, sa, sb, y, flag)
+    ref = torch.empty_like(y)
+    sq.fp8_gemm_scaled(a, 0, w, 0, sq.PER_TENSOR, sa, sb, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
