@@ -183,7 +183,7 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
                     const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
                     hipStream_t stream);
 
-/* The same GEMM (per-tensor scales, FP8 matrix instructions) with K split
+/* The same GEMM (per-tensor scales) with K split
  * over `splits` workgroups per output tile, for outputs too small to fill the
  * GPU on their own -- the weight-gradient GEMM of the FP8 recipe ("FP8
  * Training & Inference", FP8 Training Recipe) has a [N x K] output and a
@@ -193,14 +193,14 @@ int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_f
  * the splits in order s = 0, 1, ... and writes
  *   y = bf16_rne((sum_s workspace[s]) * a_scale_inv[0] * b_scale_inv[0]),
  * so the result is deterministic; with splits = 1 it equals fp8_gemm_scaled
- * (ACCUM_MFMA_FP8) bit for bit.
+ * with the same accum bit for bit.  accum as in fp8_gemm_scaled.
  * workspace: caller-owned device memory of splits * M * N floats, 16-byte
  * aligned; its contents are overwritten.
  * Errors: EINVAL for NULL pointers, splits outside 1..64, M not a positive
- * multiple of 256, N or K not of 128, K < 128 * splits, misaligned pointers
- * or a bad format. */
+ * multiple of 256, N or K not of 128, K < 128 * splits, misaligned pointers,
+ * a bad format or accum. */
 int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
-                           int64_t M, int64_t N, int64_t K, int32_t splits,
+                           int64_t M, int64_t N, int64_t K, int32_t splits, fp8dp_accum accum,
                            const float* a_scale_inv, const float* b_scale_inv, float* workspace,
                            uint16_t* y, hipStream_t stream);
 
@@ -245,7 +245,7 @@ int relu2_backward_quantize(const uint16_t* dA, const void* a_cache, fp8dp_cache
  * epilogue ("FP8 training ...", Step 3: activations kept for the backward
  * pass in FP8; "FP8 Training & Inference", FP8 Training Recipe: E5M2
  * gradients x E4M3 weights).  Equal, bit for bit, to
- *   fp8_gemm_scaled(a, E5M2, b, E4M3, M, N, K, PER_TENSOR, ACCUM_MFMA_FP8,
+ *   fp8_gemm_scaled(a, E5M2, b, E4M3, M, N, K, PER_TENSOR, accum,
  *                   a_scale_inv, b_scale_inv, dA)           (dA [M x N] BF16)
  *   relu2_backward_quantize(dA, act_cache, cache, act_scale_inv, M, N, fmt,
  *                           st, NULL, dh_out)
@@ -255,10 +255,12 @@ int relu2_backward_quantize(const uint16_t* dA, const void* a_cache, fp8dp_cache
  * of the activation A with act_scale_inv the inverse scale they were cast
  * with.
  * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
- * not of 128, misaligned pointers (16 bytes; scales 4) or unknown formats;
- * EUNSUPPORTED for operand formats other than E5M2 x E4M3 or a BF16 cache. */
+ * not of 128, misaligned pointers (16 bytes; scales 4), unknown formats or
+ * accum; EUNSUPPORTED for operand formats other than E5M2 x E4M3 or a BF16
+ * cache. */
 int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
-                            int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
+                            int64_t M, int64_t N, int64_t K, fp8dp_accum accum,
+                            const float* a_scale_inv,
                             const float* b_scale_inv, const uint8_t* act_cache, fp8dp_cache cache,
                             const float* act_scale_inv, fp8dp_format fmt, fp8dp_tensor_state* st,
                             uint8_t* dh_out, hipStream_t stream);
@@ -279,16 +281,17 @@ int quantize_recompute(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act 
                        fp8dp_format fmt, const fp8dp_tensor_state* st, uint8_t* fp8_out,
                        hipStream_t stream);
 
-/* fp8_gemm_scaled (PER_TENSOR, ACCUM_MFMA_FP8) that runs only when
+/* fp8_gemm_scaled (PER_TENSOR, the given accum) that runs only when
  * *run_flag != 0, read on the GPU -- the GEMM half of the recompute above:
  * pass &st->overflow of the operand whose cast overflowed and
  * &st->scale_inv (the corrected scale's inverse).  With *run_flag == 0 y is
  * untouched.  Any M >= 1, as fp8_gemm_scaled; N and K multiples of 128.
  * Errors: EINVAL for NULL pointers, M < 1, N or K not positive multiples of
  * 128, misaligned pointers (operands 16 bytes, scales and flag 4), or a bad
- * format. */
+ * format or accum. */
 int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8dp_format fb,
-                       int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
+                       int64_t M, int64_t N, int64_t K, fp8dp_accum accum,
+                       const float* a_scale_inv,
                        const float* b_scale_inv, uint16_t* y, const uint32_t* run_flag,
                        hipStream_t stream);
 

@@ -46,16 +46,16 @@ _SIGS = {
     "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                          _vp], ctypes.c_int),
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
-    "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
-                                _vp], ctypes.c_int),
+    "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
+                                _vp, _vp, _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
-    "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
-                                 _vp, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
+                                 _i32, _vp, _i32, _vp, _vp, _vp], ctypes.c_int),
     "quantize_recompute": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
-    "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
-                           ctypes.c_int),
+    "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                            _vp], ctypes.c_int),
     "quantize_mx": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_mx": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -173,6 +173,34 @@ def _room(t, nbytes: int, what: str) -> None:
         raise Fp8dpError(f"{what}: needs {nbytes} bytes, got {t.numel() * t.element_size()}")
 
 
+def _elem(t, sizes, what: str) -> None:
+    """Refuse a tensor whose element size is not one the kernel reads or writes
+    (e.g. a uint8 tensor passed as a BF16 output would be written past its end)."""
+    if isinstance(t, torch.Tensor) and t.element_size() not in sizes:
+        raise Fp8dpError(f"{what}: expected {'/'.join(str(x) for x in sizes)}-byte elements, "
+                         f"got {t.dtype}")
+
+
+def _codes(t, what: str) -> None:
+    if isinstance(t, torch.Tensor) and t.dtype not in (torch.uint8, torch.int8) and \
+            not str(t.dtype).startswith("torch.float8"):
+        raise Fp8dpError(f"{what}: expected 8-bit codes (uint8), got {t.dtype}")
+
+
+def _gemm_operands(name: str, a, b, y=None) -> tuple:
+    """Shapes (M, N, K) of a GEMM's code operands a [M, K], b [N, K] and its
+    16-bit output y [M, N], with their element sizes checked."""
+    _codes(a, f"{name}: a")
+    _codes(b, f"{name}: b")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or (y is not None and tuple(y.shape) != (M, N)):
+        raise Fp8dpError(f"{name}: shape mismatch")
+    if y is not None:
+        _elem(y, (2,), f"{name}: y")
+    return M, N, K
+
+
 def _state_ptr(st) -> Optional[int]:
     if st is None:
         return None
@@ -192,6 +220,9 @@ def quantize_fused(h: torch.Tensor, act: int, fmt: int, mode: int, st=None,
                    bf16_out: Ptr = None, fp8_out: Ptr = None, group_scale_inv: Ptr = None,
                    stream=None) -> None:
     """h: BF16 (or 16-bit) device tensor [rows, cols] (1-D counts as one row)."""
+    _elem(h, (2,), "quantize_fused: h")
+    _elem(bf16_out, (2,), "quantize_fused: bf16_out")
+    _codes(fp8_out, "quantize_fused: fp8_out")
     rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
     _room(bf16_out, rows * cols * 2, "quantize_fused: bf16_out")
     _room(fp8_out, rows * cols, "quantize_fused: fp8_out")
@@ -208,13 +239,11 @@ def amax_history_update(st, stream=None) -> None:
 
 def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: int,
                     a_scale_inv: Ptr, b_scale_inv: Ptr, y: torch.Tensor,
-                    accum: int = ACCUM_MFMA_FP8, stream=None) -> None:
+                    accum: int = ACCUM_EXACT, stream=None) -> None:
     """a [M, K] codes, b [N, K] codes, y [M, N] BF16; scales are device pointers/tensors;
-    accum: ACCUM_MFMA_FP8 (FP8 matrix instructions) or ACCUM_EXACT (FP16 widening)."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or tuple(y.shape) != (M, N):
-        raise Fp8dpError("fp8_gemm_scaled: shape mismatch")
+    accum: ACCUM_EXACT (FP16 widening, FP32-accurate sums; the default) or
+    ACCUM_MFMA_FP8 (the FP8 matrix instructions, which truncate small products)."""
+    M, N, K = _gemm_operands("fp8_gemm_scaled", a, b, y)
     group = mode == PER_GROUP128
     _room(a_scale_inv, (M * (K // 128) if group else 1) * 4, "fp8_gemm_scaled: a_scale_inv")
     _room(b_scale_inv, ((N // 128) * (K // 128) if group else 1) * 4,
@@ -225,16 +254,14 @@ def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: in
 
 def fp8_gemm_scaled_splitk(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, splits: int,
                            a_scale_inv: Ptr, b_scale_inv: Ptr, workspace: torch.Tensor,
-                           y: torch.Tensor, stream=None) -> None:
+                           y: torch.Tensor, accum: int = ACCUM_EXACT, stream=None) -> None:
     """Per-tensor FP8 GEMM with K split `splits` ways; workspace: float32 device
     tensor of at least splits * M * N elements."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or tuple(y.shape) != (M, N):
-        raise Fp8dpError("fp8_gemm_scaled_splitk: shape mismatch")
+    M, N, K = _gemm_operands("fp8_gemm_scaled_splitk", a, b, y)
     if workspace.dtype != torch.float32 or workspace.numel() < splits * M * N:
         raise Fp8dpError("fp8_gemm_scaled_splitk: workspace needs splits * M * N float32")
-    _check(lib().fp8_gemm_scaled_splitk(_p(a), fa, _p(b), fb, M, N, K, splits, _p(a_scale_inv),
+    _check(lib().fp8_gemm_scaled_splitk(_p(a), fa, _p(b), fb, M, N, K, splits, accum,
+                                        _p(a_scale_inv),
                                         _p(b_scale_inv), _p(workspace), _p(y), _stream(stream)),
            "fp8_gemm_scaled_splitk")
 
@@ -266,14 +293,15 @@ def relu2_backward_quantize(dA: torch.Tensor, a_cache: torch.Tensor, cache: int,
 def fp8_gemm_relu2_backward(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, a_scale_inv: Ptr,
                             b_scale_inv: Ptr, act_cache: torch.Tensor, cache: int,
                             act_scale_inv: Ptr, fmt: int, st, dh_out: torch.Tensor,
-                            stream=None) -> None:
+                            accum: int = ACCUM_EXACT, stream=None) -> None:
     """dgrad a [M, K] x b [N, K]^T with the squared ReLU's backward in the epilogue:
     dh_out [M, N] gradient codes from the cached activation codes act_cache [M, N]."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or tuple(act_cache.shape) != (M, N) or tuple(dh_out.shape) != (M, N):
+    M, N, K = _gemm_operands("fp8_gemm_relu2_backward", a, b)
+    _codes(act_cache, "fp8_gemm_relu2_backward: act_cache")
+    _codes(dh_out, "fp8_gemm_relu2_backward: dh_out")
+    if tuple(act_cache.shape) != (M, N) or tuple(dh_out.shape) != (M, N):
         raise Fp8dpError("fp8_gemm_relu2_backward: shape mismatch")
-    _check(lib().fp8_gemm_relu2_backward(_p(a), fa, _p(b), fb, M, N, K, _p(a_scale_inv),
+    _check(lib().fp8_gemm_relu2_backward(_p(a), fa, _p(b), fb, M, N, K, accum, _p(a_scale_inv),
                                          _p(b_scale_inv), _p(act_cache), cache, _p(act_scale_inv),
                                          fmt, _state_ptr(st), _p(dh_out), _stream(stream)),
            "fp8_gemm_relu2_backward")
@@ -289,13 +317,11 @@ def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.T
 
 
 def fp8_gemm_scaled_if(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, a_scale_inv: Ptr,
-                       b_scale_inv: Ptr, y: torch.Tensor, run_flag: Ptr, stream=None) -> None:
+                       b_scale_inv: Ptr, y: torch.Tensor, run_flag: Ptr,
+                       accum: int = ACCUM_EXACT, stream=None) -> None:
     """Per-tensor FP8 GEMM that runs only when the device word *run_flag is nonzero."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or tuple(y.shape) != (M, N):
-        raise Fp8dpError("fp8_gemm_scaled_if: shape mismatch")
-    _check(lib().fp8_gemm_scaled_if(_p(a), fa, _p(b), fb, M, N, K, _p(a_scale_inv),
+    M, N, K = _gemm_operands("fp8_gemm_scaled_if", a, b, y)
+    _check(lib().fp8_gemm_scaled_if(_p(a), fa, _p(b), fb, M, N, K, accum, _p(a_scale_inv),
                                     _p(b_scale_inv), _p(y), _p(run_flag), _stream(stream)),
            "fp8_gemm_scaled_if")
 

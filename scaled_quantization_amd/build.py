@@ -1,7 +1,8 @@
 """Compile libfp8dp.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Every call recompiles.  The library is written next to this file so that it
-travels with the source tree.
+Every call recompiles: each csrc/*.hip becomes an object under _build/ (the
+files compile in parallel), then one link writes the library next to this
+file so that it travels with the source tree.
 """
 from __future__ import annotations
 
@@ -9,12 +10,14 @@ import glob
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8dp.so")
+OBJ = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 # -ffp-contract=off: no multiply-add contraction anywhere (the quantizer's
@@ -22,7 +25,7 @@ ARCH = "gfx950"
 #   fused multiply-adds explicitly).
 # -packed-fp32-ops disabled: no packed FP32 instructions are emitted.
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-ffp-contract=off", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -40,20 +43,31 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile all csrc/*.hip into libfp8dp.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}",
-           *sources(), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stderr or "").splitlines()
                      if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}) on {cmd[-3]}:\n{errs}")
     if verbose and errs.strip():
         print(errs)
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile all csrc/*.hip into libfp8dp.so (always recompiles)."""
+    os.makedirs(OBJ, exist_ok=True)
+    cc = hipcc()
+    srcs = sources()
+    objs = [os.path.join(OBJ, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([cc, *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}",
+                                     f"-I{CSRC}", "-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,898 +1,13 @@
-// gemm.hip -- scaled FP8 x FP8 GEMM with FP32 accumulation and BF16 output.
-//
-// "FP8 training: what it is and how it works", Step 3: the multiplication
-// reads FP8 inputs and keeps its running sum in a wider format; partial sums
-// are promoted to FP32 every 128 elements.  "FP8 Training & Inference",
-// Per-Tensor Scaling: the scales are factored out of the matmul and the
-// output is rescaled.  Trade-offs: 1 x 128 activation tiles and 128 x 128
-// weight blocks each carry their own scale.
-//
-//   y[m, n] = bf16_rne( sum_k dec(a[m, k]) dec(b[n, k]) * sa * sb )        per tensor
-//   y[m, n] = bf16_rne( sum_g P_g[m, n] * sa[m, g] * sb[n/128, g] )      per group,
-//             P_g = FP32 MFMA sum over the 128 k of block g
-//
-// Kernel (gfx950): a 256-thread workgroup owns a 128 x 128 tile of y; each of
-// its four waves owns 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x64_f8f6f4
-// (the format of each operand is selected by the instruction's cbsz / blgp
-// fields: 0 = E4M3, 1 = E5M2).  K advances 128 bytes at a time; A and B tiles
-// (128 rows x 128 bytes each) are staged in LDS, double-buffered, with an XOR
-// swizzle of the 16-byte chunks (swz() below) so the 16-byte LDS reads of 16
-// consecutive rows hit distinct banks.  Global loads for the next K step are
-// issued before the MFMAs of the current one.
+// gemm.hip -- scaled FP8 x FP8 GEMM with FP32 accumulation and BF16 output:
+// fp8_gemm_scaled (per tensor / per 128-group scales) and its conditional form
+// fp8_gemm_scaled_if.  The kernels are in gemm_kernels.hpp.
 #include <hip/hip_runtime.h>
 
-#include "codec.hpp"
-#include "common.hpp"
-#include "gemm_core.hpp"
-#include "quant_core.hpp"
+#include "gemm_kernels.hpp"
 
 namespace fp8dp {
 
-typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
-
-// Widens the 32 FP8 codes of an MFMA fragment into four groups of 8 FP16
-// values (exact: every E4M3 and E5M2 value is an FP16 value); group j holds
-// bytes 8j .. 8j+7 in order.
-template <int F>
-__device__ __forceinline__ void widen_fp8(const v8i_t& x, v8h_t out[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v2h_t p0, p1, p2, p3;
-    if constexpr (F == 0) {
-      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j], 1.0f, false);
-      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j], 1.0f, true);
-      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j + 1], 1.0f, false);
-      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[2 * j + 1], 1.0f, true);
-    } else {
-      p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j], 1.0f, false);
-      p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j], 1.0f, true);
-      p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j + 1], 1.0f, false);
-      p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(x[2 * j + 1], 1.0f, true);
-    }
-    out[j] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                     __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
-                                     5, 6, 7);
-  }
-}
-
-constexpr int kBM = 128, kBN = 128;
-constexpr int kGemmThreads = 256;
-
-template <int FA, int FB, int MODE, bool EXACT>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(const uint8_t* __restrict__ A,
-                                                          const uint8_t* __restrict__ B, int M,
-                                                          int N, int K,
-                                                          const float* __restrict__ sa,
-                                                          const float* __restrict__ sb,
-                                                          uint16_t* __restrict__ Y,
-                                                          const uint32_t* run_flag = nullptr) {
-  // run_flag: the conditional GEMM's flag (a device word); zero leaves Y untouched
-  if (run_flag != nullptr && *run_flag == 0u) return;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBM * kBK];
-  __shared__ float lds_sa[2][kBM];
-
-  // M may be ragged: the last row tile reads row M - 1 in place of the rows
-  // past the end and does not store them
-  const int tiles_n = N / kBN;
-  const int ntiles = ((M + kBM - 1) / kBM) * tiles_n;
-  const int tile = tile_of_block(blockIdx.x, ntiles);
-  const int m0 = (tile / tiles_n) * kBM;
-  const int n0 = (tile % tiles_n) * kBN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = (wave >> 1) * 64;   // wave's row offset in the tile
-  const int wn = (wave & 1) * 64;    // wave's column offset
-  const int kgroups = K / kBK;
-
-  // Global -> register staging: thread t moves chunks t + 256 i (i = 0..3) of
-  // each 128 x 128-byte tile: row (t + 256 i) / 8, 16-byte chunk t % 8.
-  const int srow = tid >> 3, sch = tid & 7;
-  auto a_row = [&](int r) { return A + (size_t)(r < M ? r : M - 1) * K + sch * 16; };
-  const uint8_t* const gA0 = a_row(m0 + srow);
-  const uint8_t* const gA1 = a_row(m0 + srow + 32);
-  const uint8_t* const gA2 = a_row(m0 + srow + 64);
-  const uint8_t* const gA3 = a_row(m0 + srow + 96);
-  const uint8_t* gB = B + (size_t)(n0 + srow) * K + sch * 16;
-  const size_t gstep = (size_t)32 * K;   // 256 threads / 8 chunks = 32 rows apart
-  const int sa_row = (m0 + (tid & (kBM - 1))) < M ? m0 + (tid & (kBM - 1)) : M - 1;
-  u32x4_t ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-  float rsa = 0.0f;
-#define FP8DP_GLOAD(kt)                                                                  \
-  do {                                                                                   \
-    const size_t k0 = (size_t)(kt) * kBK;                                                \
-    ra0 = *reinterpret_cast<const u32x4_t*>(gA0 + k0);                                   \
-    ra1 = *reinterpret_cast<const u32x4_t*>(gA1 + k0);                                   \
-    ra2 = *reinterpret_cast<const u32x4_t*>(gA2 + k0);                                   \
-    ra3 = *reinterpret_cast<const u32x4_t*>(gA3 + k0);                                   \
-    rb0 = *reinterpret_cast<const u32x4_t*>(gB + k0);                                    \
-    rb1 = *reinterpret_cast<const u32x4_t*>(gB + gstep + k0);                            \
-    rb2 = *reinterpret_cast<const u32x4_t*>(gB + 2 * gstep + k0);                        \
-    rb3 = *reinterpret_cast<const u32x4_t*>(gB + 3 * gstep + k0);                        \
-    if constexpr (MODE == FP8DP_PER_GROUP128) {                                          \
-      if (tid < kBM) rsa = sa[(size_t)sa_row * kgroups + (kt)];                          \
-    }                                                                                    \
-  } while (0)
-#define FP8DP_SSTORE(buf)                                                                \
-  do {                                                                                   \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(srow, sch)]) = ra0;                     \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(srow + 32, sch)]) = ra1;                \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(srow + 64, sch)]) = ra2;                \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][0][swz(srow + 96, sch)]) = ra3;                \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(srow, sch)]) = rb0;                     \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(srow + 32, sch)]) = rb1;                \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(srow + 64, sch)]) = rb2;                \
-    *reinterpret_cast<u32x4_t*>(&lds[buf][1][swz(srow + 96, sch)]) = rb3;                \
-    if constexpr (MODE == FP8DP_PER_GROUP128) {                                          \
-      if (tid < kBM) lds_sa[buf][tid] = rsa;                                             \
-    }                                                                                    \
-  } while (0)
-
-  v16f_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  FP8DP_GLOAD(0);
-  FP8DP_SSTORE(0);
-  __syncthreads();
-
-  const int frow = lane & 31;        // row of A / column of B this lane feeds
-  const int fhalf = (lane >> 5) * 2; // which 32-byte half of each 64-wide K step
-
-  for (int kt = 0; kt < kgroups; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < kgroups) FP8DP_GLOAD(kt + 1);
-
-    v16f_t part[2][2];
-    if constexpr (MODE == FP8DP_PER_GROUP128) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8i_t fa[2], fb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int ra_row = wm + t * 32 + frow;
-        const int rb_row = wn + t * 32 + frow;
-        const int c0 = ks * 4 + fhalf;
-        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(&lds[buf][0][swz(ra_row, c0)]);
-        const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(&lds[buf][0][swz(ra_row, c0 + 1)]);
-        const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(&lds[buf][1][swz(rb_row, c0)]);
-        const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(&lds[buf][1][swz(rb_row, c0 + 1)]);
-        fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-      if constexpr (EXACT) {
-        v8h_t ha[2][4], hb[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          widen_fp8<FA>(fa[t], ha[t]);
-          widen_fp8<FB>(fb[t], hb[t]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              if constexpr (MODE == FP8DP_PER_GROUP128)
-                part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i][q], hb[j][q], part[i][j],
-                                                                    0, 0, 0);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i][q], hb[j][q], acc[i][j],
-                                                                   0, 0, 0);
-            }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            if constexpr (MODE == FP8DP_PER_GROUP128)
-              part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  fa[i], fb[j], part[i][j], FA, FB, 0, 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  fa[i], fb[j], acc[i][j], FA, FB, 0, 0, 0, 0);
-          }
-      }
-    }
-    if constexpr (MODE == FP8DP_PER_GROUP128) {
-      // promote the 128-wide partial sums with their scales
-      const float sbv = sb[(size_t)(n0 / kBN) * kgroups + kt];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float f = lds_sa[buf][row] * sbv;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j][r] = __builtin_fmaf(part[i][j][r], f, acc[i][j][r]);
-        }
-    }
-    if (kt + 1 < kgroups) FP8DP_SSTORE(buf ^ 1);
-    __syncthreads();
-  }
-#undef FP8DP_GLOAD
-#undef FP8DP_SSTORE
-
-  float f = 1.0f;
-  if constexpr (MODE == FP8DP_PER_TENSOR) f = sa[0] * sb[0];
-  // Output layout of a 32 x 32 MFMA tile: lane holds column lane % 32, and
-  // register r holds row 8 (r / 4) + 4 (lane / 32) + r % 4.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = n0 + wn + j * 32 + (lane & 31);
-        const float v = (MODE == FP8DP_PER_TENSOR) ? acc[i][j][r] * f : acc[i][j][r];
-        if (row < M) Y[(size_t)row * N + col] = (uint16_t)bf16_rne_int(v);
-      }
-}
-
-// ------------------------------------------------------------------ large tiles
-// Per-tensor, MX and per-group FP8 paths for large problems.  A 512-thread workgroup (8 waves,
-// two per SIMD) owns a 256 x BN tile of y (BN = 64 TN = 128, 192 or 256); wave
-// w owns rows 64 (w / 2) .. +63 and columns (BN / 2)(w % 2) .. as 2 x TN tiles
-// of the 32 x 32 x 64 MFMA (TN = 4 uses 252 of the 256 registers a wave may
-// have at two waves per SIMD).  K advances 128 bytes per stage through a two-slot LDS
-// ring.  Global memory is copied straight into LDS with
-// global_load_lds_dwordx4 (no register staging): one instruction moves 64
-// lanes x 16 bytes = 8 rows of 128 bytes, lane i landing at byte 16 i; lane i
-// therefore fetches the global chunk of row i / 8 that swz() places at chunk
-// i % 8 (the same layout as the small-tile kernel).
-//
-// The loop is software-pipelined by half stages, with the fragments double
-// buffered: the first half of stage t reads the fragments of its second
-// 64-wide k substep while the MFMAs of the first substep run; then every wave
-// waits for its own copies of stage t+1, and one barrier per stage publishes
-// them and shows that every wave has finished reading stage t; the second half
-// refills stage t's slot with the copies of stage t+2, reads the first
-// substep of stage t+1 and runs the MFMAs of stage t's second substep.  The
-// copies of a stage therefore have a whole stage of MFMAs to land, and no
-// LDS read waits in front of the MFMA pipe.
-// The epilogue pairs adjacent output columns between neighbour lanes (one DPP
-// swap) and stores BF16 pairs straight to Y.
-// PG (per-128-group scales, 256 x 128 or 256 x 192 tiles): one stage is one
-// 128-wide group of k, so each stage's two substeps accumulate a partial sum
-// that is then promoted, acc += part * (sa[m, g] * sb[n / 128, g]) -- the
-// small-tile kernel's arithmetic.  The tiles are computed transposed (B
-// fragment first), which leaves one scale product per lane and fragment row
-// instead of one per element: with the A rows in the registers the promotion
-// cost a product per element and was slower than the small-tile kernel.
-// A 192-wide tile spans two B blocks (one scale per fragment) and runs its
-// stage by A fragment row rather than by substep (see the loop).
-// Measured alternatives (GPT-2 shape, same tile): no half-stage pipelining
-// (barrier at the stage start) about 4% slower; 64-byte stages with a 4-5
-// deep ring, a 3-slot ring for A, four waves of 128 x 96, and a ping-pong of
-// the two waves of each SIMD with a barrier per phase were all slower.
-// SPLIT: workgroup u of (M/256)(N/BN) x splits runs split s = u' / ntiles of
-// tile u' % ntiles (u' = the XCD-ordered index), over the 128-byte stages
-// [s KS/splits, (s+1) KS/splits) of the KS = K/128, and writes its FP32 sums,
-// unscaled, to ws[s][m][n]; k_splitk_reduce then adds the splits in order.
-// MX: microscaled operands (32-value blocks along k, E8M0 block exponents
-// ea [M x K/32], eb [N x K/32]).  A stage's 128 k bytes are 4 blocks, so each
-// tile row needs one dword of exponents per stage: waves 0-3 copy the 256 A
-// rows' dwords and waves 4-7 the B rows' into the ring slot next to the
-// tiles, with the same waits and barrier.  In the 32 x 32 x 64 instruction a
-// lane supplies the operand exponent of its fragment row for its 32 k bytes
-// (lane / 32 selects the half), which is exactly one block: the MFMA applies
-// 2^(ea - 127) 2^(eb - 127) to each block's products, and the epilogue has
-// no scale to apply.
-// XG = 4 (K a multiple of 512, exponent arrays 16-byte aligned): a lane's
-// 4-byte exponent copy touches a row of its own, so per stage it costs as
-// many cache-line requests as all the tile copies of its wave together;
-// instead one 16-byte copy per row carries 4 stages' exponents, issued with
-// the tiles of every fourth stage into a two-slot exponent ring (slot g % 2
-// for stages 4g .. 4g+3).  Group g is issued with stage 4g, two stages before
-// its first read, and its slot was last read by stage 4g - 5.
-// The squared ReLU's backward applied in the epilogue (BC >= 0): the GEMM's
-// output is dA, and each element leaves as the gradient code
-//   code = sat_rne(bf16(two_root[c] * bf16(dA)) * scale),
-//   two_root[c] = 2 sqrt(dec(c) * cache_si), c = the cached activation's code,
-// i.e. exactly fp8_gemm_scaled followed by relu2_backward_quantize on its
-// output, without dA's round trip through memory.
-struct Relu2Bwd {
-  const uint8_t* cache;     // [M x N] FP8 codes of the cached activation (format BC)
-  const float* cache_si;    // the inverse scale they were cast with
-  uint8_t* out;             // [M x N] gradient codes (format BF)
-  const float* scale;       // the gradient state's scale
-  fp8dp_acc_slot* slots;    // the gradient state's accumulators
-};
-
-// COND: the launch does nothing unless *run_flag != 0 (a device-side flag,
-// e.g. the overflow mark of a scaling state), read once by every workgroup.
-template <int FA, int FB, int TN, bool SPLIT, bool MX = false, bool COND = false, int BC = -1,
-          int BF = 1, int XG = 1, bool PG = false, bool PER = false>
-__global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__ A,
-                                                     const uint8_t* __restrict__ B, int M, int N,
-                                                     int K, const float* __restrict__ sa,
-                                                     const float* __restrict__ sb,
-                                                     uint16_t* __restrict__ Y,
-                                                     float* __restrict__ ws, int splits,
-                                                     const uint8_t* __restrict__ ea = nullptr,
-                                                     const uint8_t* __restrict__ eb = nullptr,
-                                                     const uint32_t* __restrict__ run_flag = nullptr,
-                                                     Relu2Bwd bwd = {}) {
-  static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
-  static_assert(BC < 0 || !(MX || SPLIT), "the backward epilogue follows the per-tensor GEMM");
-  if constexpr (COND) {
-    if (*run_flag == 0) return;
-  }
-  // BC: the backward epilogue's two scalars, read before any store (read
-  // later, every use after a store would wait for all stores in flight)
-  float bwd_si = 0.0f, bwd_sg = 0.0f;
-  if constexpr (BC >= 0) {
-    bwd_si = *bwd.cache_si;
-    bwd_sg = *bwd.scale;
-  }
-  constexpr int BM = 256, BN = 64 * TN, TM = 2;
-  constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
-  static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
-  static_assert(!PG || ((TN == 2 || TN == 3) && XG == 4 && !MX && !SPLIT && BC < 0),
-                "per-group scales: 256 x 128 or 256 x 192 tiles, scales through the ring");
-  static_assert(!PER || (!MX && !PG && !SPLIT && !COND && BC < 0),
-                "persistent grid: the plain per-tensor path");
-  constexpr bool XR = (MX || PG) && XG == 4;                // exponents / scales in their own ring
-  constexpr int SLOT = TILES + (MX && !XR ? 2048 : 0);      // + 256 A and 256 B exponent dwords
-  constexpr int XSZ = XR ? 8192 : 0;                        // 512 rows x 16 bytes (4 stages)
-  constexpr int LA = BM / 64, LB = BN / 64;                 // tile copies per wave per stage
-  constexpr int NCOPY = LA + LB + (MX && !XR ? 1 : 0);      // copies of a stage with no exponents
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT + 2 * XSZ];
-
-  const int tiles_n = N / BN;
-  const int ntiles = (M / BM) * tiles_n;
-  // PER: a persistent grid; workgroup b runs the tiles of its passes one after
-  // another through one pipeline, stage g being k-stage g % KT of the tile of
-  // pass g / KT, so the next tile's first stages are copied while a tile's
-  // last stage and its epilogue run
-  int tile, split = 0;
-  if constexpr (PER) {
-    tile = tile_of_pass(blockIdx.x, 0, gridDim.x, ntiles);
-  } else if constexpr (SPLIT) {
-    const int u = tile_of_block(blockIdx.x, ntiles * splits);
-    split = u / ntiles;
-    tile = u % ntiles;
-  } else {
-    tile = tile_of_block(blockIdx.x, ntiles);
-  }
-  const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = (wave >> 1) * 64;
-  const int wc = (wave & 1) * (BN / 2);
-  // SPLIT: split s runs stages [s KS / splits, (s + 1) KS / splits) of the
-  // KS = K / 128 stages (equal ranges when splits divides KS)
-  const int KS = K / kBK;
-  const int s0 = SPLIT ? (int)((int64_t)split * KS / splits) : 0;
-  const int KT = SPLIT ? (int)((int64_t)(split + 1) * KS / splits) - s0 : KS;
-  const size_t kbase = (size_t)s0 * kBK;
-  const int GS = PER ? tiles_of_block(blockIdx.x, gridDim.x, ntiles) * KT : KT;   // stages to run
-  if (GS == 0) return;   // (a persistent grid has no more workgroups than tiles)
-
-  // copy instruction i of this wave covers rows 8 (wave + 8 i) .. +7; lane l
-  // lands at chunk l % 8 of row l / 8 there, so it fetches the logical chunk
-  // that swz() places at that position: (l % 8) ^ ((row / 2) % 8), where
-  // (row / 2) % 8 = (4 wave + (l / 8) / 2) % 8 for every i
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ ((4 * wave + (lrow >> 1)) & 7);
-  const uint8_t* gA = A + (size_t)(m0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
-  const uint8_t* gB = B + (size_t)(n0 + wave * 8 + lrow) * K + kbase + lchunk * 16;
-  const size_t rstep = (size_t)64 * K;
-  // exponent dwords: wave w < 4 fetches A row 64 w + lane, wave w >= 4 B row
-  // 64 (w - 4) + lane (clamped into the tile; the surplus dwords are unused)
-  // PG: the same copies move the FP32 group scales, whose rows (K / 128
-  // floats) are as long as the exponent rows: A row 64 w + lane, and for
-  // waves 4-7 the tile's one row of B block scales
-  const uint8_t* gE = nullptr;
-  if constexpr (MX || PG) {
-    const int r = (wave & 3) * 64 + lane;
-    const size_t kb = (size_t)K / 32;
-    if constexpr (PG) {
-      // B block rows n0 / 128 and, for a 192-wide tile, n0 / 128 + 1 (lane 1 of wave 4)
-      const int nbr = n0 / 128 + ((TN == 3 && r == 1) ? 1 : 0);
-      gE = wave < 4 ? reinterpret_cast<const uint8_t*>(sa) + (size_t)(m0 + r) * kb
-                    : reinterpret_cast<const uint8_t*>(sb) + (size_t)nbr * kb;
-    }
-    else
-      gE = wave < 4 ? ea + (size_t)(m0 + r) * kb + kbase / 32
-                    : eb + (size_t)(n0 + (r < BN ? r : BN - 1)) * kb + kbase / 32;
-  }
-  auto issue = [&](int kt) {
-    uint8_t* base = lds + (kt & 1) * SLOT + wave * 1024;
-    int64_t oa = (int64_t)kt * kBK, ob = oa;
-    if constexpr (PER) {
-      // the tile of stage kt, as row offsets from this workgroup's first tile
-      const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
-      const int64_t k0 = (int64_t)(kt % KT) * kBK;
-      oa = (int64_t)((t / tiles_n) * BM - m0) * K + k0;
-      ob = (int64_t)((t % tiles_n) * BN - n0) * K + k0;
-    }
-#pragma unroll
-    for (int i = 0; i < LA; ++i) copy16_to_lds(gA + i * rstep + oa, base + i * 8192);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) copy16_to_lds(gB + i * rstep + ob, base + ASZ + i * 8192);
-    if constexpr (XR) {
-      if ((kt & 3) == 0)
-        copy16_to_lds(gE + kt * 4, lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ + wave * 1024);
-    } else if constexpr (MX) {
-      copy4_to_lds(gE + kt * 4, lds + (kt & 1) * SLOT + TILES + wave * 256);
-    }
-  };
-
-  // this lane's fragment rows: A rows wr + 32 t + lane % 32, B rows wc + 32 t + lane % 32.
-  // The instruction takes the 64 k of a substep as two 32-wide blocks: bytes
-  // 0-15 of lane l are k 16 (l / 32) .. +15 of the first block and bytes 16-31
-  // the same k of the second (measured with single-instruction probes), so
-  // the lane reads 16-byte chunks h*4 + l/32 and h*4 + 2 + l/32 of substep h.
-  // MX: lane l supplies the exponent of block l / 32 of its row, i.e. block
-  // 2 h + l / 32 of the stage, byte 2 h + l / 32 of the row's dword; the
-  // instruction reads the low byte of the scale operand.
-  const int frow = lane & 31;
-  const int fhalf = lane >> 5;
-  auto load_frags = [&](int kt, int h, v8i_t* fa, v8i_t* fb, uint32_t* xa, uint32_t* xb) {
-    const uint8_t* sA = lds + (kt & 1) * SLOT;
-    const uint8_t* sB = sA + ASZ;
-    const int c0 = h * 4 + fhalf;
-    if constexpr (MX || PG) {
-      // the row dwords of this lane's fragments (packed just before the
-      // MFMAs that use them, so that no wait on these reads sits in front of
-      // the MFMAs in between)
-      if constexpr (XR) {
-        // row r's 16 bytes at 16 r (B rows from 256 on); stage kt's dword is the (kt % 4)-th
-        const uint32_t* sE =
-            reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
-#pragma unroll
-        for (int t = 0; t < TM; ++t) xa[t] = sE[4 * (wr + 32 * t + frow)];
-        if constexpr (PG) {
-          xb[0] = sE[4 * 256];             // the tile's B block scale (128-wide tiles)
-        } else {
-#pragma unroll
-          for (int t = 0; t < TN; ++t) xb[t] = sE[4 * (256 + wc + 32 * t + frow)];
-        }
-      } else {
-        const uint32_t* sE = reinterpret_cast<const uint32_t*>(sA + TILES);
-#pragma unroll
-        for (int t = 0; t < TM; ++t) xa[t] = sE[wr + 32 * t + frow];
-#pragma unroll
-        for (int t = 0; t < TN; ++t) xb[t] = sE[256 + wc + 32 * t + frow];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const int r = wr + t * 32 + frow;
-      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
-      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 2));
-      fa[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const int r = wc + t * 32 + frow;
-      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
-      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 2));
-      fb[t] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
-
-  v16f_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // PG: the stage's partial sums (one stage = one 128-wide group), computed
-  // transposed: the B fragment is the instruction's first operand, so a
-  // lane holds one A row (its column lane % 32) and its 16 registers hold B
-  // rows of one 128-wide B block.  The promotion then needs one product of
-  // scales per lane and fragment row (sa[m] sb), not one per element.
-  v16f_t part[PG && TN == 2 ? TM : 1][PG && TN == 2 ? TN : 1];
-  // Without MX the scale operands are the constant 0, which the compiler
-  // lowers to the unscaled instruction (checked in the generated assembly).
-  auto mfmas = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* ra, const uint32_t* rb,
-                   int h) {
-    if constexpr (MX) {
-      // the exponents of substep h packed one per byte (fragment t in byte t,
-      // picked by the instruction's byte select): byte 2 h + lane / 32 of each
-      // row dword
-      const uint32_t bsel = 2 * h + fhalf;
-      const uint32_t pair = bsel | ((bsel + 4) << 8) | 0x0C0C0000u;   // -> bytes 0, 1; 0s above
-      const uint32_t xa = __builtin_amdgcn_perm(ra[1], ra[0], pair);
-      const uint32_t b01 = __builtin_amdgcn_perm(rb[1], rb[0], pair);
-      uint32_t xb;
-      if constexpr (TN == 2) {
-        xb = b01;
-      } else if constexpr (TN == 3) {
-        xb = __builtin_amdgcn_perm(rb[2], b01, 0x0C000100u | ((bsel + 4) << 16));
-      } else {
-        const uint32_t b23 = __builtin_amdgcn_perm(rb[3], rb[2], pair);
-        xb = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
-      }
-      static_for<TM>([&](auto I) {
-        static_for<TN>([&](auto J) {
-          acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[I], fb[J], acc[I][J], FA, FB, decltype(I)::value, (int)xa,
-              decltype(J)::value, (int)xb);
-        });
-      });
-    } else if constexpr (PG) {
-      if (h == 0) {
-        const v16f_t zero = {};
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], zero, FB,
-                                                                        FA, 0, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], part[i][j],
-                                                                        FB, FA, 0, 0, 0, 0);
-        // promote with the group's scales: sa of this lane's A row, sb of the tile
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const float c = __uint_as_float(ra[i]) * __uint_as_float(rb[0]);
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[i][j][r], c, acc[i][j][r]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j],
-                                                                     FA, FB, 0, 0, 0, 0);
-    }
-  };
-
-  // BC >= 0: the tile's cached codes [256 x BN], row-major, copied with the
-  // 16-byte global->LDS copies into the ring slot stage KT would have used
-  // (free once iteration KT-2's barrier has shown every wave done with stage
-  // KT-2): issued there, they have the last stage and a half to land, and the
-  // last stage's wait and barrier publish them.  Copy k of wave w moves chunks
-  // 64 (8 k + w) .. +63 (chunk q = row q / (BN/16), 16-byte column q % (BN/16)).
-  auto issue_cache = [&](uint8_t* dst) {
-    if constexpr (BC >= 0) {
-      constexpr int CPR = BN / 16, NCC = BM * CPR / 512;
-#pragma unroll
-      for (int k = 0; k < NCC; ++k) {
-        const int q = (8 * k + wave) * 64 + lane;
-        copy16_to_lds(bwd.cache + (size_t)(m0 + q / CPR) * N + n0 + (q % CPR) * 16,
-                      dst + (8 * k + wave) * 1024);
-      }
-    }
-  };
-  uint8_t* const cache_lds = lds + (KT & 1) * SLOT;
-
-  // epilogue: scale, round to BF16 and store pairs of adjacent columns of the
-  // tile at (tm0, tn0).  In a 32 x 32 MFMA tile the lane holds column
-  // lane % 32 and register r holds row 8 (r / 4) + 4 (lane / 32) + r % 4;
-  // swapping one value with the neighbour lane (DPP quad_perm 1,0,3,2) gives
-  // the even lane columns (c, c+1) of row r and the odd lane the same columns
-  // of row r+1.
-  auto epi_plain = [&](int tm0, int tn0) {
-    const float f = MX ? 1.0f : sa[0] * sb[0];
-    const bool odd = lane & 1;
-    const int colp = (lane & 31) & ~1;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
-          const float give = odd ? v0 : v1;
-          const float got = __builtin_bit_cast(
-              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
-                                                 false));
-          const uint32_t packed = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
-          const int row =
-              tm0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
-          const int col = tn0 + wc + j * 32 + colp;
-          *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = packed;
-        }
-  };
-
-  // prologue: stages 0 and 1 in flight, stage 0 landed and published
-  issue(0);
-  if (GS > 1) {
-    issue(1);
-    wait_vmcnt<NCOPY>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  stage_barrier();
-  if constexpr (PG && TN == 3) {
-    // 256 x 192 tiles: the partial sums of all six fragments cannot stay live
-    // across the half stage beside the accumulators, so the stage is split by
-    // A fragment instead of by substep: the first half runs fragment row 0's
-    // three chains (both substeps, then the promotion), the second half row
-    // 1's.  Each chain is the 256 x 128 path's arithmetic -- part = B0 A0,
-    // part += B1 A1, acc = fma(part, sa sb, acc) -- so the outputs are the
-    // same bit for bit.  All of stage kt's B fragments and row 0's A
-    // fragments are read in the previous second half, row 1's in the first
-    // half, so every read of a slot is done by the barrier that frees it.
-    v8i_t gb[2][TN], ga0[2], ga1[2];
-    uint32_t ya0, ya1, yb[TN];
-    auto read_b = [&](int kt) {
-      const uint8_t* sB = lds + (kt & 1) * SLOT + ASZ;
-      const uint32_t* sE =
-          reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
-#pragma unroll
-      for (int t = 0; t < TN; ++t) yb[t] = sE[4 * (256 + ((n0 + wc + 32 * t) >> 7) - (n0 >> 7))];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          const int r = wc + t * 32 + frow, c0 = h * 4 + fhalf;
-          const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0));
-          const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sB + swz(r, c0 + 2));
-          gb[h][t] =
-              __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    };
-    auto read_a = [&](int kt, int t, v8i_t* ga, uint32_t& ya) {
-      const uint8_t* sA = lds + (kt & 1) * SLOT;
-      const uint32_t* sE =
-          reinterpret_cast<const uint32_t*>(lds + 2 * SLOT + ((kt >> 2) & 1) * XSZ) + (kt & 3);
-      const int r = wr + t * 32 + frow;
-      ya = sE[4 * r];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c0 = h * 4 + fhalf;
-        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0));
-        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(sA + swz(r, c0 + 2));
-        ga[h] = __builtin_bit_cast(v8i_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    auto chains = [&](const v8i_t* ga, v16f_t* p) {
-      const v16f_t zero = {};
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        p[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[0][j], ga[0], zero, FB, FA, 0, 0,
-                                                              0, 0);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        p[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[1][j], ga[1], p[j], FB, FA, 0, 0,
-                                                              0, 0);
-    };
-    read_b(0);
-    read_a(0, 0, ga0, ya0);
-    for (int kt = 0; kt < GS; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // stage kt's B and row-0 A fragments
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        v16f_t p[TN];
-        chains(ga0, p);
-        // row 1's reads after the instructions that read row 0's fragments
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(kt, 1, ga1, ya1);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float c = __uint_as_float(ya0) * __uint_as_float(yb[j]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[0][j][r] = __builtin_fmaf(p[j][r], c, acc[0][j][r]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[0][j]));
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
-      wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
-      stage_barrier();
-      if (kt + 2 < GS) issue(kt + 2);
-      float c1[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) c1[j] = __uint_as_float(ya1) * __uint_as_float(yb[j]);
-      v16f_t p[TN];
-      chains(ga1, p);
-      // the next stage's reads go after the instructions that still read gb
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < GS) {
-        read_b(kt + 1);
-        read_a(kt + 1, 0, ga0, ya0);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[1][j][r] = __builtin_fmaf(p[j][r], c1[j], acc[1][j][r]);
-    }
-  } else {
-    v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
-    load_frags(0, 0, fa0, fb0, xa0, xb0);
-    for (int kt = 0; kt < GS; ++kt) {
-      if constexpr (PG) {
-        // the reads of substep 0 were issued a half stage ago: wait for them
-        // here, before the reads below (else the wait covers those as well)
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // first half: read substep 1 of stage kt, multiply substep 0
-      load_frags(kt, 1, fa1, fb1, xa1, xb1);
-      mfmas(fa0, fb0, xa0, xb0, 0);
-      if constexpr (MX || PG) {
-        // keep these products in the first half: without a use here the
-        // compiler sinks them past the barrier (they only feed later ones)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            if constexpr (PG && TN == 2) asm volatile("" : "+v"(part[i][j]));
-            else asm volatile("" : "+v"(acc[i][j]));
-          }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage kt are done
-      wait_vmcnt<0>();                      // this wave's copies of stage kt+1 have landed
-      stage_barrier();
-      // second half: refill stage kt's slot, read substep 0 of stage kt+1, multiply substep 1
-      if (kt + 2 < GS) issue(kt + 2);
-      if constexpr (BC >= 0) {
-        if (kt + 2 == KT) issue_cache(cache_lds);
-      }
-      if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
-      mfmas(fa1, fb1, xa1, xb1, 1);
-      if constexpr (PER) {
-        if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum
-          const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
-          epi_plain((t / tiles_n) * BM, (t % tiles_n) * BN);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        }
-      }
-    }
-  }
-  if constexpr (PER) return;
-
-  if constexpr (SPLIT) {
-    // FP32 partial sums: lanes 0-31 of a store cover 32 consecutive columns
-    float* out = ws + (size_t)split * M * N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          out[(size_t)row * N + n0 + wc + j * 32 + (lane & 31)] = acc[i][j][r];
-        }
-    return;
-  }
-
-  if constexpr (BC >= 0) {
-    // with a single stage there was no iteration KT-2: copy now (every wave
-    // has passed the stage's barrier after its last fragment reads)
-    if (KT < 2) issue_cache(cache_lds);
-    // 2 sqrt(dec(c) * si) for the 256 codes (threads 0-255, the per-element
-    // operations of relu2_backward_quantize), in the ring slot of stage KT-1
-    // (every wave passed the last stage's barrier after reading it) -- one
-    // LDS array, see block_fold_in
-    float* const two_root = reinterpret_cast<float*>(lds + ((KT - 1) & 1) * SLOT);
-    if (threadIdx.x < 256) {
-      float d;
-      if constexpr (BC == 0) d = __builtin_amdgcn_cvt_pk_f32_fp8((int)threadIdx.x, false)[0];
-      else d = __builtin_amdgcn_cvt_pk_f32_bf8((int)threadIdx.x, false)[0];
-      two_root[threadIdx.x] = __fmul_rn(2.0f, __builtin_sqrtf(__fmul_rn(d, bwd_si)));
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    const float f = sa[0] * sb[0];
-    const float sg = bwd_sg;
-    const bool odd = lane & 1;
-    const int colp = (lane & 31) & ~1;
-    uint32_t amax16 = 0, sat = 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        // per 32 x 32 tile, in three passes so that the LDS reads of its 8
-        // row pairs are in flight together: (1) dA pairs and their cached
-        // codes, (2) the table entries, (3) the gradient codes
-        uint32_t da[8], c2[8];
-        int lrow[8];
-        const int lcol = wc + j * 32 + colp;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // the pair of adjacent columns (col, col+1) of one row, as in the
-          // BF16 epilogue below: dA exactly as fp8_gemm_scaled stores it
-          const int r = 2 * k;
-          const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
-          const float give = odd ? v0 : v1;
-          const float got = __builtin_bit_cast(
-              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
-                                                 false));
-          da[k] = odd ? pack2_bf16_hw(got, v1) : pack2_bf16_hw(v0, got);
-          lrow[k] = wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) + (odd ? 1 : 0);
-          c2[k] = *reinterpret_cast<const uint16_t*>(cache_lds + lrow[k] * BN + lcol);
-        }
-        float t0[8], t1[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          t0[k] = two_root[c2[k] & 0xFFu];
-          t1[k] = two_root[c2[k] >> 8];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float g0 = __fmul_rn(t0[k], __uint_as_float(da[k] << 16));
-          const float g1 = __fmul_rn(t1[k], __uint_as_float(da[k] & 0xFFFF0000u));
-          const uint32_t m0g = __float_as_uint(g0) & 0x7FFFFFFFu, m1g = __float_as_uint(g1) & 0x7FFFFFFFu;
-          uint32_t b, code;
-          if (m0g <= kF32Inf && m1g <= kF32Inf) {
-            // no NaN: the hardware conversions (the clamp saturates, the
-            // convert rounds to nearest even: the integer codec's codes), and
-            // the saturation count from the scaled values directly
-            b = pack2_bf16_hw(g0, g1);
-            const float q0 = __fmul_rn(__uint_as_float(b << 16), sg);
-            const float q1 = __fmul_rn(__uint_as_float(b & 0xFFFF0000u), sg);
-            code = pack2_hw<BF>(q0, q1);
-            sat += saturates<BF>(q0) + saturates<BF>(q1);
-          } else {
-            b = pack2_bf16_int(g0, g1);
-            const float q0 = __fmul_rn(__uint_as_float(b << 16), sg);
-            const float q1 = __fmul_rn(__uint_as_float(b & 0xFFFF0000u), sg);
-            code = enc_int<BF>(q0) | (enc_int<BF>(q1) << 8);
-            sat += saturates<BF>(q0) + saturates<BF>(q1);
-          }
-          const uint32_t b0 = b & 0x7FFFu, b1 = (b >> 16) & 0x7FFFu;
-          const uint32_t mx = b0 > b1 ? b0 : b1;
-          amax16 = mx > amax16 ? mx : amax16;
-          *reinterpret_cast<uint16_t*>(bwd.out + (size_t)(m0 + lrow[k]) * N + n0 + lcol) =
-              (uint16_t)code;
-        }
-      }
-    block_fold_in<512>(amax16, sat, bwd.slots,
-                       reinterpret_cast<uint32_t*>(lds + ((KT - 1) & 1) * SLOT + 1024));
-    return;
-  }
-
-  if constexpr (PG) {
-    // transposed tiles: register r of lane l holds y[m][n] for A row
-    // m = wr + 32 i + l % 32 and B row n = wc + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4,
-    // so registers 4q .. 4q+3 are 4 adjacent outputs of one row: one 8-byte store
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = m0 + wr + i * 32 + (lane & 31);
-          const int col = n0 + wc + j * 32 + q * 8 + (lane >> 5) * 4;
-          const uint2 v = {pack2_bf16_hw(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                           pack2_bf16_hw(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-          *reinterpret_cast<uint2*>(Y + (size_t)row * N + col) = v;
-        }
-    return;
-  }
-
-  epi_plain(m0, n0);
-}
-
-template <int FA, int FB, int TN>
+template <int FA, int FB, int TN, bool EX>
 static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                       const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
   const int64_t ntiles = (M / 256) * (N / (64 * TN));
@@ -905,16 +20,17 @@ static int launch_big(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
   // out of step and spreads the epilogues' store bursts
   const int64_t cus = num_cus() & ~7;
   if (cus >= 8 && ntiles > cus && K / kBK <= 16)
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, false, -1, 1, 1, false, true>),
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, false, -1, 1, 1, false, true, EX>),
                        dim3((unsigned)cus), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
                        sb, y, nullptr, 1);
   else
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false>), dim3((unsigned)ntiles), dim3(512), 0,
-                       stream, a, b, (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1);
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, false, -1, 1, 1, false, false, EX>),
+                       dim3((unsigned)ntiles), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K,
+                       sa, sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool EX>
 static int launch_pg(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                      const float* sa, const float* sb, uint16_t* y, hipStream_t stream) {
   // 256 x 192 tiles when they take fewer rounds of the grid: one takes about
@@ -922,130 +38,29 @@ static int launch_pg(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, i
   // tiles in one round 50.0 us against 384 in two, 62.9 us; with fewer tiles
   // than compute units the narrow tiles win, 12.8 against 17.2 us at 4096 x
   // 384 x 1024)
+  // (exact accumulation: 256 x 128 only -- its 192-wide tile spills)
   const int64_t cus = num_cus();
-  const int64_t t2 = (M / 256) * (N / 128), t3 = N % 192 == 0 ? (M / 256) * (N / 192) : 0;
+  const int64_t t2 = (M / 256) * (N / 128), t3 = !EX && N % 192 == 0 ? (M / 256) * (N / 192) : 0;
   const int64_t r2 = (t2 + cus - 1) / cus, r3 = (t3 + cus - 1) / cus;
   if (t3 > 0 && 8 * r3 < 5 * r2)
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, 3, false, false, false, -1, 1, 4, true>),
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, 3, false, false, false, -1, 1, 4, true, false, false>),
                        dim3((unsigned)t3), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
                        sb, y, nullptr, 1);
   else
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, 2, false, false, false, -1, 1, 4, true>),
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, 2, false, false, false, -1, 1, 4, true, false, EX>),
                        dim3((unsigned)t2), dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, sa,
                        sb, y, nullptr, 1);
   return check_launch("fp8_gemm_scaled");
 }
 
-template <int FA, int FB, int TN>
+template <int FA, int FB, int TN, bool EX>
 static int launch_cond(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                        const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
                        hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, true>),
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, false, true, -1, 1, 1, false, false, EX>),
                      dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
                      (int)M, (int)N, (int)K, sa, sb, y, nullptr, 1, nullptr, nullptr, flag);
   return check_launch("fp8_gemm_scaled_if");
-}
-
-template <int FA, int FB>
-static int launch_cond_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                            const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
-                            hipStream_t stream) {
-  if (N % 192 == 0) return launch_cond<FA, FB, 3>(a, b, M, N, K, sa, sb, y, flag, stream);
-  if (N % 256 == 0) return launch_cond<FA, FB, 4>(a, b, M, N, K, sa, sb, y, flag, stream);
-  return launch_cond<FA, FB, 2>(a, b, M, N, K, sa, sb, y, flag, stream);
-}
-
-template <int BC, int BF, int TN>
-static int launch_bwd_epi(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                          const float* sa, const float* sb, uint16_t* y_unused, Relu2Bwd bwd,
-                          hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<1, 0, TN, false, false, false, BC, BF>),
-                     dim3((unsigned)((M / 256) * (N / (64 * TN)))), dim3(512), 0, stream, a, b,
-                     (int)M, (int)N, (int)K, sa, sb, y_unused, nullptr, 1, nullptr, nullptr,
-                     nullptr, bwd);
-  return check_launch("fp8_gemm_relu2_backward");
-}
-
-template <int BC, int BF>
-static int launch_bwd_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                           const float* sa, const float* sb, Relu2Bwd bwd, hipStream_t stream) {
-  // no 256-wide tile: with the backward epilogue's registers it would spill
-  if (N % 192 == 0) return launch_bwd_epi<BC, BF, 3>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
-  return launch_bwd_epi<BC, BF, 2>(a, b, M, N, K, sa, sb, nullptr, bwd, stream);
-}
-
-template <int FA, int FB, int TN>
-static int launch_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
-                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((M / 256) * (N / (64 * TN))));
-  if (K % 512 == 0 && aligned16(ea) && aligned16(eb))
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true, false, -1, 1, 4>), grid, dim3(512), 0,
-                       stream, a, b, (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea,
-                       eb);
-  else
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true>), grid, dim3(512), 0, stream, a, b,
-                       (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea, eb);
-  return check_launch("fp8_gemm_mx");
-}
-
-template <int FA, int FB>
-static int launch_mx_tile(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
-                          const uint8_t* eb, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                          hipStream_t stream) {
-  // no 256-wide tile here: with the exponent registers it would spill
-  if (N % 192 == 0) return launch_mx<FA, FB, 3>(a, ea, b, eb, M, N, K, y, stream);
-  return launch_mx<FA, FB, 2>(a, ea, b, eb, M, N, K, y, stream);
-}
-
-// y[m, n] = bf16_rne((sum over s in order of ws[s][m][n]) * sa[0] * sb[0]):
-// 8 consecutive elements per thread per iteration, grid-stride.
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits,
-                                                       int64_t mn, const float* __restrict__ sa,
-                                                       const float* __restrict__ sb,
-                                                       uint16_t* __restrict__ y) {
-  const float f = sa[0] * sb[0];
-  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
-  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < mn; i += stride) {
-    float v[8];
-    {
-      const float4 a = *reinterpret_cast<const float4*>(ws + i);
-      const float4 b = *reinterpret_cast<const float4*>(ws + i + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-    for (int s = 1; s < splits; ++s) {
-      const float* p = ws + (size_t)s * mn + i;
-      const float4 a = *reinterpret_cast<const float4*>(p);
-      const float4 b = *reinterpret_cast<const float4*>(p + 4);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-      v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-    }
-    *reinterpret_cast<uint4*>(y + i) =
-        make_uint4(pack2_bf16_hw(v[0] * f, v[1] * f), pack2_bf16_hw(v[2] * f, v[3] * f),
-                   pack2_bf16_hw(v[4] * f, v[5] * f), pack2_bf16_hw(v[6] * f, v[7] * f));
-  }
-}
-
-template <int FA, int FB, int TN>
-static int launch_split(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                        int splits, const float* sa, const float* sb, float* ws, uint16_t* y,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, true>),
-                     dim3((unsigned)((M / 256) * (N / (64 * TN)) * splits)), dim3(512), 0, stream,
-                     a, b, (int)M, (int)N, (int)K, sa, sb, y, ws, splits);
-  if (check_launch("fp8_gemm_scaled_splitk")) return FP8DP_EHIP;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3(grid_for(M * N / 8, 256, 8)), dim3(256), 0, stream, ws,
-                     splits, M * N, sa, sb, y);
-  return check_launch("fp8_gemm_scaled_splitk");
-}
-
-template <int FA, int FB>
-static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                             int splits, const float* sa, const float* sb, float* ws, uint16_t* y,
-                             hipStream_t stream) {
-  if (N % 192 == 0) return launch_split<FA, FB, 3>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
-  if (N % 256 == 0) return launch_split<FA, FB, 4>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
-  return launch_split<FA, FB, 2>(a, b, M, N, K, splits, sa, sb, ws, y, stream);
 }
 
 template <int FA, int FB, int MODE, bool EXACT>
@@ -1057,59 +72,54 @@ static void launch_gemm_t(const uint8_t* a, const uint8_t* b, int64_t M, int64_t
                      a, b, (int)M, (int)N, (int)K, sa, sb, y, run_flag);
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool EX>
 static int launch_gemm(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                       fp8dp_scale_mode mode, fp8dp_accum accum, const float* sa, const float* sb,
-                       uint16_t* y, hipStream_t stream) {
-  const bool exact = accum == FP8DP_ACCUM_EXACT;
+                       fp8dp_scale_mode mode, const float* sa, const float* sb, uint16_t* y,
+                       hipStream_t stream) {
   // The large-tile kernels take the rows that fill whole 256-row tiles; the
   // rest (M % 256 rows, any M) go to the small-tile kernel, which masks the
   // rows past M.  Each output row comes from one kernel, so a row's value
   // does not depend on M beyond which kernel computed it.
   const int64_t Mb = M / 256 * 256;
-  const bool big_t = mode == FP8DP_PER_TENSOR && !exact;
-  const bool big_g = mode == FP8DP_PER_GROUP128 && !exact && K % 512 == 0 && aligned16(sa) &&
-                     aligned16(sb);
+  const bool big_t = mode == FP8DP_PER_TENSOR;
+  const bool big_g = mode == FP8DP_PER_GROUP128 && K % 512 == 0 && aligned16(sa) && aligned16(sb);
   if (Mb > 0 && (big_t || big_g)) {
     int rc;
     if (big_g)
-      rc = launch_pg<FA, FB>(a, b, Mb, N, K, sa, sb, y, stream);
-    else if (N % 192 == 0)   // the widest tile that divides N
-      rc = launch_big<FA, FB, 3>(a, b, Mb, N, K, sa, sb, y, stream);
-    else if (N % 256 == 0)
-      rc = launch_big<FA, FB, 4>(a, b, Mb, N, K, sa, sb, y, stream);
+      rc = launch_pg<FA, FB, EX>(a, b, Mb, N, K, sa, sb, y, stream);
     else
-      rc = launch_big<FA, FB, 2>(a, b, Mb, N, K, sa, sb, y, stream);
+      rc = with_tile_width<EX>(N, [&](auto T) {
+        return launch_big<FA, FB, decltype(T)::value, EX>(a, b, Mb, N, K, sa, sb, y, stream);
+      });
     if (rc != FP8DP_OK || Mb == M) return rc;
     a += Mb * K;
     y += Mb * N;
     if (big_g) sa += Mb * (K / 128);
     M -= Mb;
   }
-  if (mode == FP8DP_PER_TENSOR) {
-    if (exact) launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, true>(a, b, M, N, K, sa, sb, y, stream);
-    else launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a, b, M, N, K, sa, sb, y, stream);
-  } else {
-    if (exact) launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, true>(a, b, M, N, K, sa, sb, y, stream);
-    else launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, false>(a, b, M, N, K, sa, sb, y, stream);
-  }
+  if (mode == FP8DP_PER_TENSOR)
+    launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, EX>(a, b, M, N, K, sa, sb, y, stream);
+  else
+    launch_gemm_t<FA, FB, FP8DP_PER_GROUP128, EX>(a, b, M, N, K, sa, sb, y, stream);
   return check_launch("fp8_gemm_scaled");
 }
 
 // fp8_gemm_scaled_if over any M: the same split of rows as launch_gemm (whole
 // 256-row tiles on the large-tile kernel, the rest on the small-tile one),
 // both reading the flag, so a run gives fp8_gemm_scaled's output bit for bit
-template <int FA, int FB>
+template <int FA, int FB, bool EX>
 static int launch_cond_rows(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                             const float* sa, const float* sb, uint16_t* y, const uint32_t* flag,
                             hipStream_t stream) {
   const int64_t Mb = M / 256 * 256;
   if (Mb > 0) {
-    const int rc = launch_cond_tile<FA, FB>(a, b, Mb, N, K, sa, sb, y, flag, stream);
+    const int rc = with_tile_width<EX>(N, [&](auto T) {
+      return launch_cond<FA, FB, decltype(T)::value, EX>(a, b, Mb, N, K, sa, sb, y, flag, stream);
+    });
     if (rc != FP8DP_OK || Mb == M) return rc;
   }
-  launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, false>(a + Mb * K, b, M - Mb, N, K, sa, sb, y + Mb * N,
-                                                 stream, flag);
+  launch_gemm_t<FA, FB, FP8DP_PER_TENSOR, EX>(a + Mb * K, b, M - Mb, N, K, sa, sb, y + Mb * N,
+                                              stream, flag);
   return check_launch("fp8_gemm_scaled_if");
 }
 
@@ -1149,99 +159,17 @@ extern "C" int fp8_gemm_scaled(const uint8_t* a, fp8dp_format fa, const uint8_t*
     set_error("fp8_gemm_scaled: operands must be 16-byte aligned, scales 4-byte aligned");
     return FP8DP_EINVAL;
   }
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_gemm<0, 0>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_gemm<0, 1>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
-  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_gemm<1, 0>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
-  return launch_gemm<1, 1>(a, b, M, N, K, mode, accum, a_scale_inv, b_scale_inv, y, stream);
-}
-
-extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
-                                      fp8dp_format fb, int64_t M, int64_t N, int64_t K,
-                                      int32_t splits, const float* a_scale_inv,
-                                      const float* b_scale_inv, float* workspace, uint16_t* y,
-                                      hipStream_t stream) {
-  if (a == nullptr || b == nullptr || y == nullptr || workspace == nullptr ||
-      a_scale_inv == nullptr || b_scale_inv == nullptr) {
-    set_error("fp8_gemm_scaled_splitk: NULL pointer argument");
-    return FP8DP_EINVAL;
-  }
-  if (splits < 1 || splits > 64) {
-    set_error("fp8_gemm_scaled_splitk: splits must be in 1..64 (got %d)", (int)splits);
-    return FP8DP_EINVAL;
-  }
-  if (M < 256 || N < 128 || K < 128 * (int64_t)splits || M % 256 || N % 128 || K % 128) {
-    set_error("fp8_gemm_scaled_splitk: M must be a positive multiple of 256, N and K of 128, "
-              "K at least 128 * splits (got %lld, %lld, %lld, splits %d)", (long long)M,
-              (long long)N, (long long)K, (int)splits);
-    return FP8DP_EINVAL;
-  }
-  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
-      (M / 256) * (N / 128) * splits > (int64_t)0x7FFFFFFF) {
-    set_error("fp8_gemm_scaled_splitk: shape too large");
-    return FP8DP_EINVAL;
-  }
-  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
-    set_error("fp8_gemm_scaled_splitk: unknown format");
-    return FP8DP_EINVAL;
-  }
-  if (!aligned16(a) || !aligned16(b) || !aligned16(y) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
-      (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u)) {
-    set_error("fp8_gemm_scaled_splitk: operands and workspace must be 16-byte aligned, scales "
-              "4-byte aligned");
-    return FP8DP_EINVAL;
-  }
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_split_tile<0, 0>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_split_tile<0, 1>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
-  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_split_tile<1, 0>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
-  return launch_split_tile<1, 1>(a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
-}
-
-extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale,
-                           const uint8_t* b, fp8dp_format fb, const uint8_t* b_scale, int64_t M,
-                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  if (a == nullptr || b == nullptr || y == nullptr || a_scale == nullptr || b_scale == nullptr) {
-    set_error("fp8_gemm_mx: NULL pointer argument");
-    return FP8DP_EINVAL;
-  }
-  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
-    set_error("fp8_gemm_mx: M must be a positive multiple of 256, N and K of 128 (got %lld, "
-              "%lld, %lld)", (long long)M, (long long)N, (long long)K);
-    return FP8DP_EINVAL;
-  }
-  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
-      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
-    set_error("fp8_gemm_mx: shape too large");
-    return FP8DP_EINVAL;
-  }
-  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
-    set_error("fp8_gemm_mx: unknown format");
-    return FP8DP_EINVAL;
-  }
-  if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
-      (reinterpret_cast<uintptr_t>(a_scale) & 3u) || (reinterpret_cast<uintptr_t>(b_scale) & 3u)) {
-    set_error("fp8_gemm_mx: operands must be 16-byte aligned, block exponents 4-byte aligned");
-    return FP8DP_EINVAL;
-  }
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_mx_tile<0, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_mx_tile<0, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_mx_tile<1, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  return launch_mx_tile<1, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
+  return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
+    return launch_gemm<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
+        a, b, M, N, K, mode, a_scale_inv, b_scale_inv, y, stream);
+  });
 }
 
 extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
                                   fp8dp_format fb, int64_t M, int64_t N, int64_t K,
-                                  const float* a_scale_inv, const float* b_scale_inv, uint16_t* y,
-                                  const uint32_t* run_flag, hipStream_t stream) {
+                                  fp8dp_accum accum, const float* a_scale_inv,
+                                  const float* b_scale_inv, uint16_t* y, const uint32_t* run_flag,
+                                  hipStream_t stream) {
   if (a == nullptr || b == nullptr || y == nullptr || a_scale_inv == nullptr ||
       b_scale_inv == nullptr || run_flag == nullptr) {
     set_error("fp8_gemm_scaled_if: NULL pointer argument");
@@ -1257,8 +185,9 @@ extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8
     set_error("fp8_gemm_scaled_if: shape too large");
     return FP8DP_EINVAL;
   }
-  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
-    set_error("fp8_gemm_scaled_if: unknown format");
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
+      (accum != FP8DP_ACCUM_MFMA_FP8 && accum != FP8DP_ACCUM_EXACT)) {
+    set_error("fp8_gemm_scaled_if: unknown format or accumulation mode");
     return FP8DP_EINVAL;
   }
   if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
@@ -1269,60 +198,8 @@ extern "C" int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8
               "aligned");
     return FP8DP_EINVAL;
   }
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_cond_rows<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_cond_rows<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
-  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_cond_rows<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
-  return launch_cond_rows<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
-}
-
-extern "C" int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
-                                       fp8dp_format fb, int64_t M, int64_t N, int64_t K,
-                                       const float* a_scale_inv, const float* b_scale_inv,
-                                       const uint8_t* act_cache, fp8dp_cache cache,
-                                       const float* act_scale_inv, fp8dp_format fmt,
-                                       fp8dp_tensor_state* st, uint8_t* dh_out,
-                                       hipStream_t stream) {
-  if (a == nullptr || b == nullptr || a_scale_inv == nullptr || b_scale_inv == nullptr ||
-      act_cache == nullptr || act_scale_inv == nullptr || st == nullptr || dh_out == nullptr) {
-    set_error("fp8_gemm_relu2_backward: NULL pointer argument");
-    return FP8DP_EINVAL;
-  }
-  if (M < 256 || N < 128 || K < 128 || M % 256 || N % 128 || K % 128) {
-    set_error("fp8_gemm_relu2_backward: M must be a positive multiple of 256, N and K of 128 "
-              "(got %lld, %lld, %lld)", (long long)M, (long long)N, (long long)K);
-    return FP8DP_EINVAL;
-  }
-  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
-      (M / 256) * (N / 128) > (int64_t)0x7FFFFFFF) {
-    set_error("fp8_gemm_relu2_backward: shape too large");
-    return FP8DP_EINVAL;
-  }
-  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
-      (fmt != FP8DP_E4M3 && fmt != FP8DP_E5M2) ||
-      (cache != FP8DP_CACHE_E4M3 && cache != FP8DP_CACHE_E5M2 && cache != FP8DP_CACHE_BF16)) {
-    set_error("fp8_gemm_relu2_backward: unknown format or cache kind");
-    return FP8DP_EINVAL;
-  }
-  if (fa != FP8DP_E5M2 || fb != FP8DP_E4M3 || cache == FP8DP_CACHE_BF16) {
-    set_error("fp8_gemm_relu2_backward: provided for E5M2 gradients x E4M3 weights with an FP8 "
-              "activation cache (the FP8 recipe's dgrad)");
-    return FP8DP_EUNSUPPORTED;
-  }
-  if (!aligned16(a) || !aligned16(b) || !aligned16(act_cache) || !aligned16(dh_out) ||
-      !aligned16(st) || (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
-      (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u) ||
-      (reinterpret_cast<uintptr_t>(act_scale_inv) & 3u)) {
-    set_error("fp8_gemm_relu2_backward: operands, cache, output and state must be 16-byte "
-              "aligned, scales 4-byte aligned");
-    return FP8DP_EINVAL;
-  }
-  const Relu2Bwd bwd{act_cache, act_scale_inv, dh_out, &st->scale, st->acc};
-  if (cache == FP8DP_CACHE_E4M3)
-    return fmt == FP8DP_E5M2 ? launch_bwd_tile<0, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream)
-                             : launch_bwd_tile<0, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream);
-  return fmt == FP8DP_E5M2 ? launch_bwd_tile<1, 1>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream)
-                           : launch_bwd_tile<1, 0>(a, b, M, N, K, a_scale_inv, b_scale_inv, bwd, stream);
+  return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
+    return launch_cond_rows<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
+        a, b, M, N, K, a_scale_inv, b_scale_inv, y, run_flag, stream);
+  });
 }

@@ -98,17 +98,19 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"activation" in L.fp8dp_last_error()
     rc = L.gemm_bf16_quantize_fused(16, 24, 256, 128, 64, 1, 0, 16, None, None, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
-    # fp8_gemm_scaled_splitk(a, fa, b, fb, M, N, K, splits, sa, sb, ws, y, stream)
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 0, 16, 16, 16, 16, None)
+    # fp8_gemm_scaled_splitk(a, fa, b, fb, M, N, K, splits, accum, sa, sb, ws, y, stream)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 0, 1, 16, 16, 16, 16, None)
     assert rc == -1 and b"splits" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 128, 2, 16, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 128, 2, 1, 16, 16, 16, 16, None)
     assert rc == -1 and b"128 * splits" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 200, 1, 16, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 200, 1, 1, 16, 16, 16, 16, None)
     assert rc == -1 and b"of 128" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, None, 16, None)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 1, 16, 16, None, 16, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 16, 16, 24, 16, None)
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 1, 16, 16, 24, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 7, 16, 16, 16, 16, None)
+    assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 96, 32, None)
     assert rc == -1 and b"64" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 64, 16, None)
@@ -182,14 +184,16 @@ def test_recompute_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"non-NULL" in L.fp8dp_last_error()
     rc = L.quantize_recompute(16, 4, 8, 0, 0, 24, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, None, None)
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 1, 16, 16, 16, None, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 0, 128, 128, 16, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 0, 128, 128, 1, 16, 16, 16, 16, None)
     assert rc == -1 and b"M must be positive" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 128, 100, 128, 16, 16, 16, 16, None)
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 128, 100, 128, 1, 16, 16, 16, 16, None)
     assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 18, None)
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 1, 16, 16, 16, 18, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_if(16, 0, 16, 0, 256, 128, 128, 2, 16, 16, 16, 16, None)
+    assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
 
 
 def test_relu2_backward_argument_checks_reject_without_launching(L):
@@ -204,19 +208,48 @@ def test_relu2_backward_argument_checks_reject_without_launching(L):
 
 
 def test_fused_dgrad_argument_checks_reject_without_launching(L):
-    # fp8_gemm_relu2_backward(a, fa, b, fb, M, N, K, sa, sb, cache, kind, sc, fmt, st, out, stream)
-    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, None, 0, 16, 1, 16, 16,
-                                   None)
+    # fp8_gemm_relu2_backward(a, fa, b, fb, M, N, K, accum, sa, sb, cache, kind, sc, fmt, st,
+    #                         out, stream)
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 1, 16, 16, None, 0, 16, 1, 16, 16, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 128, 128, 128, 16, 16, 16, 0, 16, 1, 16, 16,
-                                   None)
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 128, 128, 128, 1, 16, 16, 16, 0, 16, 1, 16, 16, None)
     assert rc == -1 and b"256" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_relu2_backward(16, 0, 16, 0, 256, 128, 128, 16, 16, 16, 0, 16, 1, 16, 16,
-                                   None)
+    rc = L.fp8_gemm_relu2_backward(16, 0, 16, 0, 256, 128, 128, 1, 16, 16, 16, 0, 16, 1, 16, 16, None)
     assert rc == -2
-    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, 16, 2, 16, 1, 16, 16,
-                                   None)
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 1, 16, 16, 16, 2, 16, 1, 16, 16, None)
     assert rc == -2
-    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 16, 16, 24, 0, 16, 1, 16, 16,
-                                   None)
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 1, 16, 16, 24, 0, 16, 1, 16, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_relu2_backward(16, 1, 16, 0, 256, 128, 128, 4, 16, 16, 16, 0, 16, 1, 16, 16,
+                                   None)
+    assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
+
+
+def test_binding_checks_element_sizes(L):
+    # a main tensor whose element size differs from what the kernel reads or
+    # writes is refused before anything is launched (a uint8 y would be
+    # written 2 bytes per element past its end)
+    import torch
+    a8 = torch.zeros(256, 512, dtype=torch.uint8)
+    w8 = torch.zeros(128, 512, dtype=torch.uint8)
+    one = torch.ones(1)
+    with pytest.raises(sq.Fp8dpError, match="y: expected 2-byte"):
+        sq.fp8_gemm_scaled(a8, 0, w8, 0, sq.PER_TENSOR, one, one,
+                           torch.zeros(256, 128, dtype=torch.uint8))
+    with pytest.raises(sq.Fp8dpError, match="a: expected 8-bit"):
+        sq.fp8_gemm_scaled(a8.float(), 0, w8, 0, sq.PER_TENSOR, one, one,
+                           torch.zeros(256, 128, dtype=torch.bfloat16))
+    with pytest.raises(sq.Fp8dpError, match="b: expected 8-bit"):
+        sq.fp8_gemm_scaled_if(a8, 0, w8.to(torch.int16), 0, one, one,
+                              torch.zeros(256, 128, dtype=torch.bfloat16), one)
+    with pytest.raises(sq.Fp8dpError, match="y: expected 2-byte"):
+        sq.fp8_gemm_scaled_splitk(a8, 0, w8, 0, 2, one, one, torch.zeros(2 * 256 * 128),
+                                  torch.zeros(256, 128, dtype=torch.float32))
+    with pytest.raises(sq.Fp8dpError, match="h: expected 2-byte"):
+        sq.quantize_fused(torch.zeros(4, 256), sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, None)
+    with pytest.raises(sq.Fp8dpError, match="bf16_out: expected 2-byte"):
+        sq.quantize_fused(torch.zeros(4, 256, dtype=torch.bfloat16), sq.ACT_RELU2, sq.E4M3,
+                          sq.PER_TENSOR, None, torch.zeros(4, 256, dtype=torch.uint8))
+    with pytest.raises(sq.Fp8dpError, match="fp8_out: expected 8-bit"):
+        sq.quantize_fused(torch.zeros(4, 256, dtype=torch.bfloat16), sq.ACT_RELU2, sq.E4M3,
+                          sq.PER_TENSOR, None, None, torch.zeros(4, 256, dtype=torch.float16))

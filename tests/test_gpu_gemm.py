@@ -3,16 +3,20 @@
 Acceptance bound per output element, from the benchmark spec of the path:
     |y - ref| <= 2^-8 |ref| + 1e-5 * sum_k |a_k b_k|
 with ref and the absolute sum in float64 over the dequantized codes ("FP8
-training: what it is and how it works", Step 3; "FP8 Training & Inference",
+training: what it is and how it works", Step 3: FP8 inputs are acceptable
+only when the sum is kept in a wide format; "FP8 Training & Inference",
 Per-Tensor Scaling).  BF16 output rounding alone is at most 2^-9 relative.
 
-Two accumulation modes are tested on every case:
-* ACCUM_EXACT (FP16 widening, FP32-accurate sums) must meet that bound on
-  every element, adversarial inputs included;
-* ACCUM_MFMA_FP8 (the FP8 matrix instructions, which truncate products in
-  groups of 8 -- see gpu_util.fp8_mfma_allowance) must meet that bound plus
-  the truncation allowance derived from the measured instruction arithmetic.
-  How often the plain bound is exceeded is asserted per workload.
+Two accumulation modes:
+* ACCUM_EXACT (codes widened to FP16, FP16 matrix instructions summing at
+  FP32; the default and the benchmarked path) must meet that bound on every
+  element of every case, adversarial inputs included.
+* ACCUM_MFMA_FP8 (the FP8 matrix instructions, which truncate small products
+  in groups of 8 -- see gpu_util.fp8_mfma_allowance) is checked against the
+  same plain bound.  Where elements leave it, the truncation rule must
+  account for each of them (a diagnostic: any other error, e.g. a wrong
+  index, still fails), and the case is reported as an expected failure with
+  the count: the mode does not meet the contract on such data.
 
 The GEMM's inputs are the oracle's own quantization of the seeded workloads,
 uploaded, so no oracle input comes from the device path.  Full outputs at the
@@ -30,6 +34,7 @@ from gpu_util import (DEV, fp8_mfma_allowance, oracle_gemm_rows, oracle_quantize
 
 pytestmark = pytest.mark.gpu
 EXACT, FP8 = sq.ACCUM_EXACT, sq.ACCUM_MFMA_FP8
+BOTH = pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
 
 
 def _dev_f32(x):
@@ -45,23 +50,29 @@ def _gemm(a8, fa, w8, fb, mode, sa_inv, sb_inv, accum):
     return y.float().cpu().numpy()
 
 
-def _check(y, ref, absref, what, allow=None, max_plain_violation_frac=0.0):
-    """Exact mode: the plain bound.  FP8 mode: the bound plus the allowance, and
-    at most a fraction `max_plain_violation_frac` of elements outside the plain bound."""
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
-    err = np.abs(np.asarray(y, np.float64) - ref)
-    plain_bad = err > bound
-    if allow is None:
-        bad = plain_bad
-    else:
-        bad = err > bound + allow
-        frac = plain_bad.mean()
-        assert frac <= max_plain_violation_frac, f"{what}: {frac:.2e} of elements exceed the plain bound"
+def _fail_on(bad, y, ref, what):
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} outside bound, e.g. "
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the bound, e.g. "
                              + str([(tuple(map(int, i)), float(y[tuple(i)]), float(ref[tuple(i)]))
                                     for i in idx]))
+
+
+def _check(y, ref, absref, what, accum=EXACT, allowance=None):
+    """Every element within the plain bound.  In FP8 mode, elements outside it
+    must be covered by the truncation allowance (allowance() computes it), and
+    the case is then an expected failure of that mode."""
+    y = np.asarray(y, np.float64)
+    bad = ~within_bound(y, ref, absref)
+    if accum == EXACT or not bad.any():
+        _fail_on(bad, y, ref, what)
+        return
+    if allowance is not None:
+        bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
+        _fail_on(np.abs(y - ref) > bound + allowance(), y, ref,
+                 f"{what} (beyond the FP8 instructions' truncation)")
+    pytest.xfail(f"{what}: {int(bad.sum())} of {bad.size} outputs outside the plain bound -- "
+                 "the FP8 matrix instructions truncate small products (exact mode meets it)")
 
 
 def _tensor_case(name, t=0):
@@ -78,19 +89,19 @@ def _tensor_case(name, t=0):
     return w, r.fp8, st.scale, st.scale_inv, q_w, s_w, si_w
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
-def test_tiny_gemm_all_outputs(accum):
-    w, a8, s_a, si_a, w8, s_w, si_w = _tensor_case("tiny", t=2)
+@BOTH
+@pytest.mark.parametrize("t", [0, 1, 2, 3])
+def test_tiny_gemm_all_outputs(t, accum):
+    # every output of every delayed-scaling step of the tiny workload
+    w, a8, s_a, si_a, w8, s_w, si_w = _tensor_case("tiny", t=t)
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, si_a, si_w, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, s_a, s_w)
-    allow = None
-    if accum == FP8:
-        allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, range(w.M))
-    _check(y, ref, absref, "tiny", allow, max_plain_violation_frac=1e-3)
+    _check(y, ref, absref, f"tiny step {t}", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, range(w.M)))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
-@pytest.mark.parametrize("name,nrows", [("gpt2", 256), ("large", 16)])
+@BOTH
+@pytest.mark.parametrize("name,nrows", [("gpt2", 512), ("large", 48)])
 def test_per_tensor_gemm_full_size_sampled_rows(name, nrows, accum):
     w, a8, s_a, si_a, w8, s_w, si_w = _tensor_case(name)
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, si_a, si_w, accum)
@@ -98,14 +109,12 @@ def test_per_tensor_gemm_full_size_sampled_rows(name, nrows, accum):
     rows = np.sort(rng.choice(w.M, size=nrows, replace=False))
     rows[0], rows[-1] = 0, w.M - 1
     ref, absref = oracle_gemm_rows(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, s_a, s_w, rows)
-    allow = None
-    if accum == FP8:
-        allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, rows)
-    _check(y[rows], ref, absref, name, allow, max_plain_violation_frac=1e-3)
     assert np.isfinite(y).all()
+    _check(y[rows], ref, absref, name, accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, rows))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
 def test_fine_grained_block_scaled_gemm_sampled_rows(accum):
     w = workloads.get("fine")
     h = w.h0()
@@ -118,20 +127,20 @@ def test_fine_grained_block_scaled_gemm_sampled_rows(accum):
                        torch.from_numpy(si_w).to(DEV), y, accum)
     yv = y.float().cpu().numpy()
     rng = np.random.default_rng(8)
-    rows = np.sort(rng.choice(w.M, size=64, replace=False))
+    rows = np.sort(rng.choice(w.M, size=128, replace=False))
+    rows[0], rows[-1] = 0, w.M - 1
     ref, absref = oracle_gemm_rows(r.fp8, O.E4M3, q_w, O.E4M3, O.PER_GROUP128, s_a, s_w, rows)
-    allow = None
-    if accum == FP8:
-        allow = fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, s_a, s_w, rows)
-    _check(yv[rows], ref, absref, "fine", allow, max_plain_violation_frac=1e-3)
     assert np.isfinite(yv).all()
+    _check(yv[rows], ref, absref, "fine", accum,
+           lambda: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, s_a, s_w, rows))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
 def test_gpt2_per_group_gemm_full_size_sampled_rows(accum):
     # the benchmark's per-group launch: the GPT-2 activation (relu2) cast with
     # per-128 group scales, the weight with 128 x 128 block scales; in FP8
-    # mode on a 256-CU GPU this shape runs the 256 x 192 per-group tiles
+    # mode on a 256-CU GPU this shape runs the 256 x 192 per-group tiles, in
+    # exact mode the 256 x 128 ones
     w = workloads.get("gpt2")
     r = oracle_quantize(w.h0(), O.ACT_RELU2, O.E4M3, O.PER_GROUP128, want_bf16=False)
     q_w, si_w, s_w = O.quantize_weight_blocks(w.weight(), O.E4M3, with_scale=True)
@@ -141,18 +150,16 @@ def test_gpt2_per_group_gemm_full_size_sampled_rows(accum):
                        torch.from_numpy(si_w).to(DEV), y, accum)
     yv = y.float().cpu().numpy()
     rng = np.random.default_rng(9)
-    rows = np.sort(rng.choice(w.M, size=128, replace=False))
+    rows = np.sort(rng.choice(w.M, size=256, replace=False))
     rows[0], rows[-1] = 0, w.M - 1
     ref, absref = oracle_gemm_rows(r.fp8, O.E4M3, q_w, O.E4M3, O.PER_GROUP128, r.group_scale,
                                    s_w, rows)
-    allow = None
-    if accum == FP8:
-        allow = fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, r.group_scale, s_w, rows)
-    _check(yv[rows], ref, absref, "gpt2 per-group", allow, max_plain_violation_frac=1e-3)
     assert np.isfinite(yv).all()
+    _check(yv[rows], ref, absref, "gpt2 per-group", accum,
+           lambda: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, r.group_scale, s_w, rows))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
 @pytest.mark.parametrize("K", [128, 256, 1024, 4096, 16384])
 def test_random_full_range_codes_over_long_k(K, accum):
     # every finite code equally likely: products span ~2^36, the hardest case
@@ -166,20 +173,21 @@ def test_random_full_range_codes_over_long_k(K, accum):
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 1.0 / 64, 1.0 / 32, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 64.0, 32.0)
     if accum == EXACT:
-        _check(y, ref, absref, f"K={K}")
         # FP32-accurate accumulation: beyond the BF16 output rounding (at most
         # 2^-8 relative) the error stays far inside the 1e-5 term
         assert np.all(np.abs(y - ref) <= (2.0 ** -8) * np.abs(ref) + 1e-6 * absref)
-    else:
-        allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 64.0, 32.0, range(M))
-        _check(y, ref, absref, f"K={K}", allow, max_plain_violation_frac=0.05)
+    _check(y, ref, absref, f"K={K}", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 64.0, 32.0, range(M)))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
+@pytest.mark.parametrize("M,N,K", [(256, 384, 640), (512, 768, 512)])
 @pytest.mark.parametrize("fa,fb", [(0, 1), (1, 0), (1, 1)])
-def test_operand_format_combinations(fa, fb, accum):
-    rng = np.random.default_rng(10 + fa * 2 + fb)
-    M, N, K = 256, 384, 640
+def test_operand_format_combinations(fa, fb, M, N, K, accum):
+    # 256 x 384: small-tile per-group kernel (K % 512 != 0), 256 x 128 /
+    # 256 x 192 large tiles per tensor; 512 x 768 x 512: the large-tile
+    # per-group kernel
+    rng = np.random.default_rng(10 + fa * 2 + fb + M)
     ta = np.flatnonzero(np.isfinite(O.fp8_decode_table(fa)))
     tb = np.flatnonzero(np.isfinite(O.fp8_decode_table(fb)))
     a8 = rng.choice(ta, size=(M, K)).astype(np.uint8)
@@ -192,21 +200,21 @@ def test_operand_format_combinations(fa, fb, accum):
             sb = (2.0 ** rng.integers(-6, 6, (N // 128, K // 128))).astype(np.float32)
         y = _gemm(a8, fa, w8, fb, mode, 1 / sa, 1 / sb, accum)
         ref, absref = O.gemm_f64(a8, fa, w8, fb, mode, sa, sb)
-        allow = None
-        if accum == FP8:
-            allow = fp8_mfma_allowance(a8, fa, w8, fb, mode, sa, sb, range(M))
-        _check(y, ref, absref, f"fa={fa} fb={fb} mode={mode}", allow, max_plain_violation_frac=0.1)
+        _check(y, ref, absref, f"fa={fa} fb={fb} mode={mode}", accum,
+               lambda: fp8_mfma_allowance(a8, fa, w8, fb, mode, sa, sb, range(M)))
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
 @pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
-def test_identity_weight_returns_every_code_exactly(fmt, accum):
+@pytest.mark.parametrize("M", [384, 512])
+def test_identity_weight_returns_every_code_exactly(fmt, M, accum):
     # a scaled identity weight: every product group holds one nonzero product,
     # so both modes must reproduce each decoded input code exactly
     K = 256
     t = O.fp8_decode_table(fmt)
     fin = np.flatnonzero(np.isfinite(t)).astype(np.uint8)
-    a8 = np.resize(fin, (384, K)).astype(np.uint8)
+    # M = 384: 256 rows on the large tiles and 128 on the small-tile kernel
+    a8 = np.resize(fin, (M, K)).astype(np.uint8)
     one = int(O.fp8_encode(np.array([1.0], np.float32), fmt)[0])
     w8 = np.zeros((K, K), dtype=np.uint8)
     np.fill_diagonal(w8, one)
@@ -215,10 +223,11 @@ def test_identity_weight_returns_every_code_exactly(fmt, accum):
     assert np.array_equal(y, exp)
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
-def test_all_max_inputs_closed_form(accum):
+@BOTH
+@pytest.mark.parametrize("M", [128, 256])
+def test_all_max_inputs_closed_form(M, accum):
     K = 4096
-    a8 = np.full((128, K), 0x7E, dtype=np.uint8)
+    a8 = np.full((M, K), 0x7E, dtype=np.uint8)
     w8 = np.full((256, K), 0xFE, dtype=np.uint8)
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 1.0 / 448, 1.0 / 448, accum)
     assert np.all(y == -float(K))
@@ -242,7 +251,7 @@ def test_fp8_instruction_truncation_and_exact_mode():
     assert np.all(y8 == 0.0)
 
 
-@pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+@BOTH
 def test_non_multiple_of_eight_tile_grid(accum):
     # 3 x 5 = 15 tiles: the XCD renumbering falls back to the identity order
     rng = np.random.default_rng(4)
@@ -253,33 +262,36 @@ def test_non_multiple_of_eight_tile_grid(accum):
     w8 = rng.choice(near, size=(N, K)).astype(np.uint8)
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.25, 0.125, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 4.0, 8.0)
-    _check(y, ref, absref, "15 tiles")
+    _check(y, ref, absref, "15 tiles", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 4.0, 8.0, range(M)))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 256), (2304, 768, 640), (4096, 4096, 256),
                                    (256, 768, 128), (512, 640, 384), (768, 384, 256),
                                    (512, 384, 1280), (1024, 512, 1152), (512, 1024, 384),
                                    (2048, 2048, 640), (256, 256, 128)])
-def test_large_tile_paths(M, N, K):
-    # per-tensor FP8 shapes that take the 256 x 192, 256 x 256 and 256 x 128
-    # workgroup tiles: tile counts below, at and above the grid renumbering's
-    # multiple of 8, and 1, 2, 3 and 9-10 stages of 128 k (the pipeline's
-    # prologue, steady state and tail)
+@BOTH
+def test_large_tile_paths(M, N, K, accum):
+    # per-tensor shapes that take the 256 x 192, 256 x 256 (FP8 mode only)
+    # and 256 x 128 workgroup tiles: tile counts below, at and above the grid
+    # renumbering's multiple of 8, and 1, 2, 3 and 9-10 stages of 128 k (the
+    # pipeline's prologue, steady state and tail)
     rng = np.random.default_rng(M + N + K)
     t = O.fp8_decode_table(O.E4M3)
     near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
     a8 = rng.choice(near, size=(M, K)).astype(np.uint8)
     w8 = rng.choice(near, size=(N, K)).astype(np.uint8)
-    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, FP8)
+    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, accum)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 64)), [M - 1]]))
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
-    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows)
-    _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
+    _check(y[rows], ref, absref, f"{M}x{N}x{K}", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows))
 
 
 @pytest.mark.parametrize("M,N,K", [(5376, 3072, 512), (33024, 384, 256), (20480, 1024, 1024),
                                    (16384, 3072, 2048)])
-def test_persistent_grid_paths(M, N, K):
+@BOTH
+def test_persistent_grid_paths(M, N, K, accum):
     # more tiles than compute units with at most 16 stages of K: the
     # persistent grid, whose workgroups run tile after tile through one
     # pipeline -- 336 tiles (some workgroups run two, some one), 258 tiles
@@ -290,12 +302,12 @@ def test_persistent_grid_paths(M, N, K):
     near = np.flatnonzero(np.isfinite(t) & (np.abs(t) >= 0.5) & (np.abs(t) <= 8))
     a8 = rng.choice(near, size=(M, K)).astype(np.uint8)
     w8 = rng.choice(near, size=(N, K)).astype(np.uint8)
-    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, FP8)
+    y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.5, 0.25, accum)
     rows = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(255, M, 256),
                                      rng.integers(0, M, 16)]))
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
-    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows)
-    _check(y[rows], ref, absref, f"{M}x{N}x{K}", allow, max_plain_violation_frac=1e-3)
+    _check(y[rows], ref, absref, f"{M}x{N}x{K}", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows))
 
 
 def _group_case(M, N, K, fa, fb):
@@ -319,17 +331,17 @@ def _group_case(M, N, K, fa, fb):
                                          (1024, 256, 640, 1, 1), (256, 128, 512, 0, 0),
                                          (768, 384, 1536, 0, 1), (512, 640, 2048, 1, 0),
                                          (2304, 256, 4096, 1, 1)])
-def test_group_scaled_shapes(M, N, K, fa, fb):
+@BOTH
+def test_group_scaled_shapes(M, N, K, fa, fb, accum):
     # per-group FP8: per-stage partial sums promoted by sa[m, g] sb[n / 128, g]
     # over 1 to 32 stages, tile counts on and off the renumbering's multiple
     # of 8, every format pair, scales that are not powers of two
     a8, w8, sa, sb = _group_case(M, N, K, fa, fb)
-    y = _gemm(a8, fa, w8, fb, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
+    y = _gemm(a8, fa, w8, fb, sq.PER_GROUP128, 1 / sa, 1 / sb, accum)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 48)), [M - 1]]))
     ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
-    allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows)
-    _check(y[rows], ref, absref, f"group {M}x{N}x{K} fa={fa} fb={fb}", allow,
-           max_plain_violation_frac=1e-3)
+    _check(y[rows], ref, absref, f"group {M}x{N}x{K} fa={fa} fb={fb}", accum,
+           lambda: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows))
 
 
 # Ragged M (a token count that does not fill a tile): the rows that fill
@@ -340,8 +352,8 @@ def test_group_scaled_shapes(M, N, K, fa, fb):
 # for bit (the same kernel computes them); every row meets the bound.
 @pytest.mark.parametrize("M", [1, 37, 128, 255, 333, 4096 + 77])
 @pytest.mark.parametrize("mode,accum", [(sq.PER_TENSOR, FP8), (sq.PER_GROUP128, FP8),
-                                        (sq.PER_TENSOR, EXACT)],
-                         ids=["tensor", "group", "tensor-exact"])
+                                        (sq.PER_TENSOR, EXACT), (sq.PER_GROUP128, EXACT)],
+                         ids=["tensor-fp8", "group-fp8", "tensor-exact", "group-exact"])
 def test_ragged_rows(M, mode, accum):
     N, K = 384, 1024
     a8, w8, sa, sb = _group_case(M, N, K, 0, 0)
@@ -358,14 +370,13 @@ def test_ragged_rows(M, mode, accum):
     rows = np.arange(M) if M <= 512 else np.unique(np.concatenate(
         [np.arange(0, M, 61), np.arange(M - 90, M)]))
     ref, absref = O.gemm_f64(a8, 0, w8, 0, mode, sa, sb, rows=rows)
-    allow = None if accum == EXACT else fp8_mfma_allowance(a8, 0, w8, 0, mode, sa, sb, rows)
-    _check(y[rows], ref, absref, f"ragged M={M} mode={mode}", allow,
-           max_plain_violation_frac=1e-3)
     Mb = M // 256 * 256
-    if Mb > 0 and accum == FP8:
+    if Mb > 0:
         sa_b = sa if mode == sq.PER_TENSOR else sa[:Mb]
         y_b = _gemm(a8[:Mb], 0, w8, 0, mode, 1 / sa_b, 1 / sb, accum)
         assert np.array_equal(y[:Mb].view(np.uint32), y_b.view(np.uint32))
+    _check(y[rows], ref, absref, f"ragged M={M} mode={mode}", accum,
+           lambda: fp8_mfma_allowance(a8, 0, w8, 0, mode, sa, sb, rows))
 
 
 # On a 256-CU GPU these shapes take the 256 x 192 per-group tiles (one round
@@ -384,19 +395,19 @@ def test_group_wide_tiles_match_narrow_tiles(M, N, K, fa, fb):
     assert diff.size == 0, f"{diff.size} outputs differ, first at {np.unravel_index(diff[0], y.shape)}"
     rows = np.unique(np.concatenate([np.arange(0, M, M // 24), [M - 1]]))
     ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
-    allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows)
-    _check(y[rows], ref, absref, f"wide group tiles {M}x{N}x{K}", allow,
-           max_plain_violation_frac=1e-3)
+    _check(y[rows], ref, absref, f"wide group tiles {M}x{N}x{K}", FP8,
+           lambda: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 2048), (256, 256, 512)])
-def test_group_scaled_kernels_agree(M, N, K):
+@BOTH
+def test_group_scaled_kernels_agree(M, N, K, accum):
     """Scale arrays 4 bytes off 16-byte alignment send a K % 512 == 0 problem
     to the 128 x 128 tile kernel instead of the ring kernel: both meet the
-    bound, and they differ at most by the FP8 instructions' truncation (the
+    bound (in FP8 mode they differ by the FP8 instructions' truncation: the
     two order a stage's k values differently inside the instruction)."""
     a8, w8, sa, sb = _group_case(M, N, K, 0, 0)
-    y = _gemm(a8, 0, w8, 0, sq.PER_GROUP128, 1 / sa, 1 / sb, FP8)
+    y = _gemm(a8, 0, w8, 0, sq.PER_GROUP128, 1 / sa, 1 / sb, accum)
 
     def off4(x):
         x = np.ascontiguousarray(x, np.float32)
@@ -408,12 +419,10 @@ def test_group_scaled_kernels_agree(M, N, K):
 
     y2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(w8), 0, sq.PER_GROUP128, off4(1 / sa),
-                       off4(1 / sb), y2, FP8)
+                       off4(1 / sb), y2, accum)
     y2 = y2.float().cpu().numpy()
     rows = np.arange(M)
     ref, absref = O.gemm_f64(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows=rows)
-    allow = fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows)
-    for got, what in ((y, "ring kernel"), (y2, "small-tile kernel")):
-        _check(got, ref, absref, what, allow, max_plain_violation_frac=1e-3)
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
-    assert np.all(np.abs(y.astype(np.float64) - y2) <= 2 * (bound + allow))
+    for got, what in ((y2, "small-tile kernel"), (y, "ring kernel")):
+        _check(got, ref, absref, what, accum,
+               lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows))
