@@ -819,7 +819,61 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   } else {
     v8i_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     uint32_t xa0[TM], xb0[TN], xa1[TM], xb1[TN];   // MX: the fragments' row exponent dwords
+    // EX (per tensor): the substep's 64 k run as 4 slices of 16 k on the
+    // FP16 instruction.  The widened operands are double-buffered: slice
+    // q + 1 (and, for the last slice, slice 0 of the substep that follows,
+    // whose codes were read at the start of the half) is widened while the
+    // MFMAs of slice q run, so no half starts with a run of converts in
+    // front of its first MFMA, and no convert overwrites an operand an MFMA
+    // in flight still reads.
+    constexpr bool EXP = EX && !PG;
+    v8h_t wa[EXP ? TM : 1], wb[EXP ? TN : 1];
+    auto widen_slice = [&](const v8i_t* fa, const v8i_t* fb, auto Q, v8h_t* oa, v8h_t* ob) {
+      constexpr int q = decltype(Q)::value;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) oa[i] = widen8<FA, q>(fa[i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) ob[j] = widen8<FB, q>(fb[j]);
+    };
+    auto mfmas_ex = [&](const v8i_t* fa, const v8i_t* fb, const v8i_t* nfa, const v8i_t* nfb) {
+      if constexpr (EXP) {
+        static_for<4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          v8h_t na[TM], nb[TN];
+          if constexpr (q < 3)
+            widen_slice(fa, fb, std::integral_constant<int, q + 1>{}, na, nb);
+          else
+            widen_slice(nfa, nfb, std::integral_constant<int, 0>{}, na, nb);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[i], wb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) wa[i] = na[i];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) wb[j] = nb[j];
+        });
+        // the half's order: its fragment reads first (their latency then
+        // runs under the MFMAs), then each MFMA followed by a share of the
+        // next slice's converts
+        constexpr int CV = (4 * (TM + TN) + TM * TN - 1) / (TM * TN);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
+        static_for<4 * TM * TN>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, CV, 0);
+        });
+        // the next half's first slice stays converted in this half: without
+        // a use here the compiler sinks its converts past the barrier, in
+        // front of the next half's first MFMA
+#pragma unroll
+        for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(wa[i]));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(wb[j]));
+      }
+    };
     load_frags(0, 0, fa0, fb0, xa0, xb0);
+    if constexpr (EXP) widen_slice(fa0, fb0, std::integral_constant<int, 0>{}, wa, wb);
     for (int kt = 0; kt < GS; ++kt) {
       if constexpr (PG) {
         // the reads of substep 0 were issued a half stage ago: wait for them
@@ -829,7 +883,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       }
       // first half: read substep 1 of stage kt, multiply substep 0
       load_frags(kt, 1, fa1, fb1, xa1, xb1);
-      mfmas(fa0, fb0, xa0, xb0, 0);
+      if constexpr (EXP) mfmas_ex(fa0, fb0, fa1, fb1);
+      else mfmas(fa0, fb0, xa0, xb0, 0);
       if constexpr (MX || PG) {
         // keep these products in the first half: without a use here the
         // compiler sinks them past the barrier (they only feed later ones)
@@ -851,7 +906,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
         if (kt + 2 == KT) issue_cache(cache_lds);
       }
       if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
-      mfmas(fa1, fb1, xa1, xb1, 1);
+      if constexpr (EXP) mfmas_ex(fa1, fb1, fa0, fb0);
+      else mfmas(fa1, fb1, xa1, xb1, 1);
       if constexpr (PER) {
         if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum
           const int t = tile_of_pass(blockIdx.x, kt / KT, gridDim.x, ntiles);
@@ -1000,7 +1056,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 template <bool EX, typename F>
 inline int with_tile_width(int64_t N, F&& f) {
   if (N % 192 == 0) return f(std::integral_constant<int, 3>{});
-  if (!EX && N % 256 == 0) return f(std::integral_constant<int, 4>{});
+  if constexpr (!EX) {
+    if (N % 256 == 0) return f(std::integral_constant<int, 4>{});
+  }
   return f(std::integral_constant<int, 2>{});
 }
 
