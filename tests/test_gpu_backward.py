@@ -9,9 +9,11 @@ The operands are the cast codes transposed by fp8_transpose (exact: the
 same bytes, moved).  Parity: transposes byte for byte against numpy's
 transpose of the same codes; GEMMs against the oracle's float64 GEMM of the
 oracle's own quantization (transposed with numpy), to the bound
-|y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| plus the FP8 instructions'
-measured truncation allowance (tests/gpu_util.fp8_mfma_allowance), with the
-fraction outside the plain bound capped.
+|y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| on every element in exact mode (the
+default).  The FP8-instruction mode is held to the same bound and reported
+as an expected failure where its truncation takes elements outside it (the
+log-normal gradient spans ~10 binades, more than the 2^13 window the FP8
+instructions keep exact within a group of 8 products).
 """
 import numpy as np
 import pytest
@@ -20,33 +22,16 @@ import torch
 import oracle as O
 import scaled_quantization_amd as sq
 import workloads
-from gpu_util import (DEV, fp8_mfma_allowance, oracle_gemm_rows, oracle_quantize, to_dev_u8,
-                      u8_np)
+from gpu_util import (DEV, check_gemm, fp8_mfma_allowance, oracle_gemm_rows, oracle_quantize,
+                      to_dev_u8, u8_np)
 
 pytestmark = pytest.mark.gpu
+EXACT, FP8 = sq.ACCUM_EXACT, sq.ACCUM_MFMA_FP8
+BOTH = pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
 
 
 def _dev_f32(x):
     return torch.from_numpy(np.atleast_1d(np.asarray(x, np.float32)).copy()).to(DEV)
-
-
-def _check(y, ref, absref, allow, what, cap=1e-3):
-    """allow None: every element within the plain bound (exact accumulation)."""
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
-    err = np.abs(np.asarray(y, np.float64) - ref)
-    if allow is None:
-        assert not (err > bound).any(), f"{what}: {int((err > bound).sum())} outside the bound"
-        return
-    bad = err > bound + allow
-    assert not bad.any(), f"{what}: {int(bad.sum())} outside bound + allowance"
-    assert (err > bound).mean() <= cap, f"{what}: {(err > bound).mean():.2e} outside the plain bound"
-
-
-# The gradient has log-normal magnitudes (sigma 3, ~10 binades): its
-# products span far more than the 2^13 window the FP8 instructions keep exact
-# within a group of 8, so more outputs leave the plain bound than on the
-# forward workloads (measured 0.1-0.4%); they stay inside bound + allowance.
-GRAD_CAP = 0.02
 
 
 # ------------------------------------------------------------------ transpose
@@ -67,8 +52,9 @@ def _codes(rng, shape, fmt, lo=0.25, hi=16.0):
     return rng.choice(ok, size=shape).astype(np.uint8)
 
 
+@BOTH
 @pytest.mark.parametrize("M,N,K", [(256, 768, 1024), (512, 640, 512), (768, 256, 2048)])
-def test_splitk_one_split_equals_gemm_and_is_deterministic(M, N, K):
+def test_splitk_one_split_equals_gemm_and_is_deterministic(M, N, K, accum):
     rng = np.random.default_rng(M * N + K)
     a8, w8 = _codes(rng, (M, K), 1), _codes(rng, (N, K), 0)
     a, w = to_dev_u8(a8), to_dev_u8(w8)
@@ -76,32 +62,53 @@ def test_splitk_one_split_equals_gemm_and_is_deterministic(M, N, K):
     y1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     y2 = torch.empty_like(y1)
     y3 = torch.empty_like(y1)
-    sq.fp8_gemm_scaled(a, 1, w, 0, sq.PER_TENSOR, sa, sb, y1)
+    sq.fp8_gemm_scaled(a, 1, w, 0, sq.PER_TENSOR, sa, sb, y1, accum)
     ws = torch.empty(4 * M * N, dtype=torch.float32, device=DEV)
-    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 1, sa, sb, ws, y2)
+    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 1, sa, sb, ws, y2, accum)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 4, sa, sb, ws, y2)
-    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 4, sa, sb, ws, y3)
+    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 4, sa, sb, ws, y2, accum)
+    sq.fp8_gemm_scaled_splitk(a, 1, w, 0, 4, sa, sb, ws, y3, accum)
     assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
 
 
 # the last three: splits that do not divide K / 128 (uneven stage ranges,
 # down to one stage per split)
+@BOTH
 @pytest.mark.parametrize("M,N,K,splits,fa,fb", [(256, 384, 1024, 2, 0, 0), (768, 3072, 4096, 4, 1, 0),
                                                 (512, 512, 4096, 8, 1, 1), (256, 128, 256, 2, 0, 1),
                                                 (256, 384, 640, 3, 0, 0), (768, 3072, 4096, 5, 1, 0),
                                                 (256, 256, 896, 7, 1, 1)])
-def test_splitk_vs_oracle(M, N, K, splits, fa, fb):
+def test_splitk_vs_oracle(M, N, K, splits, fa, fb, accum):
     rng = np.random.default_rng(3 * M + N + K + splits)
     a8, w8 = _codes(rng, (M, K), fa), _codes(rng, (N, K), fb)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(splits * M * N, dtype=torch.float32, device=DEV)
     sq.fp8_gemm_scaled_splitk(to_dev_u8(a8), fa, to_dev_u8(w8), fb, splits, _dev_f32(0.5),
-                              _dev_f32(0.25), ws, y)
+                              _dev_f32(0.25), ws, y, accum)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 24)), [M - 1]]))
     ref, absref = oracle_gemm_rows(a8, fa, w8, fb, O.PER_TENSOR, 2.0, 4.0, rows)
-    allow = fp8_mfma_allowance(a8, fa, w8, fb, O.PER_TENSOR, 2.0, 4.0, rows)
-    _check(y.float().cpu().numpy()[rows], ref, absref, allow, f"{M}x{N}x{K}/{splits}")
+    check_gemm(y.float().cpu().numpy()[rows], ref, absref, f"{M}x{N}x{K}/{splits}",
+               accum == EXACT,
+               lambda sel: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_TENSOR, 2.0, 4.0, rows[sel]))
+
+
+@pytest.mark.parametrize("K", [1024, 16384])
+def test_splitk_exact_full_range_codes(K):
+    # every finite code equally likely (products over ~2^36): the exact mode
+    # meets the bound on every element of every split count
+    rng = np.random.default_rng(K + 5)
+    M, N = 256, 384
+    ta = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E5M2)))
+    tb = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E4M3)))
+    a8 = rng.choice(ta, size=(M, K)).astype(np.uint8)
+    w8 = rng.choice(tb, size=(N, K)).astype(np.uint8)
+    ref, absref = O.gemm_f64(a8, O.E5M2, w8, O.E4M3, O.PER_TENSOR, 4.0, 0.5)
+    for splits in (1, 3, 8):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty(splits * M * N, dtype=torch.float32, device=DEV)
+        sq.fp8_gemm_scaled_splitk(to_dev_u8(a8), O.E5M2, to_dev_u8(w8), O.E4M3, splits,
+                                  _dev_f32(0.25), _dev_f32(2.0), ws, y, EXACT)
+        check_gemm(y.float().cpu().numpy(), ref, absref, f"K={K}/{splits}")
 
 
 # ------------------------------------------------------------------ the GPT-2 backward pass
@@ -119,7 +126,8 @@ def gpt2_codes():
     return r.fp8, 11.0, q_w, s_w, rd.fp8, s_dy
 
 
-def test_gpt2_dgrad(gpt2_codes):
+@BOTH
+def test_gpt2_dgrad(gpt2_codes, accum):
     a8, s_a, w8, s_w, dy8, s_dy = gpt2_codes
     M, N = dy8.shape           # 16384 x 768
     K = w8.shape[1]            # 3072
@@ -128,22 +136,20 @@ def test_gpt2_dgrad(gpt2_codes):
     assert np.array_equal(u8_np(w8t_d), w8.T)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
     sq.fp8_gemm_scaled(to_dev_u8(dy8), O.E5M2, w8t_d, O.E4M3, sq.PER_TENSOR,
-                       _dev_f32(1.0 / np.float32(s_dy)), _dev_f32(1.0 / np.float32(s_w)), dx)
+                       _dev_f32(1.0 / np.float32(s_dy)), _dev_f32(1.0 / np.float32(s_w)), dx,
+                       accum)
     rng = np.random.default_rng(41)
-    rows = np.sort(rng.choice(M, size=24, replace=False))
+    rows = np.sort(rng.choice(M, size=256, replace=False))
+    rows[0], rows[-1] = 0, M - 1
     w8t = np.ascontiguousarray(w8.T)
     ref, absref = oracle_gemm_rows(dy8, O.E5M2, w8t, O.E4M3, O.PER_TENSOR, s_dy, s_w, rows)
-    allow = fp8_mfma_allowance(dy8, O.E5M2, w8t, O.E4M3, O.PER_TENSOR, s_dy, s_w, rows)
-    _check(dx.float().cpu().numpy()[rows], ref, absref, allow, "dgrad", GRAD_CAP)
-    # exact accumulation meets the plain bound on every element
-    sq.fp8_gemm_scaled(to_dev_u8(dy8), O.E5M2, w8t_d, O.E4M3, sq.PER_TENSOR,
-                       _dev_f32(1.0 / np.float32(s_dy)), _dev_f32(1.0 / np.float32(s_w)), dx,
-                       sq.ACCUM_EXACT)
-    _check(dx.float().cpu().numpy()[rows], ref, absref, None, "dgrad exact")
+    check_gemm(dx.float().cpu().numpy()[rows], ref, absref, "dgrad", accum == EXACT,
+               lambda sel: fp8_mfma_allowance(dy8, O.E5M2, w8t, O.E4M3, O.PER_TENSOR, s_dy, s_w, rows[sel]))
 
 
+@BOTH
 @pytest.mark.parametrize("splits", [4, 5, 8])
-def test_gpt2_wgrad(gpt2_codes, splits):
+def test_gpt2_wgrad(gpt2_codes, splits, accum):
     a8, s_a, w8, s_w, dy8, s_dy = gpt2_codes
     M, K = a8.shape            # 16384 x 3072
     N = dy8.shape[1]           # 768
@@ -154,10 +160,14 @@ def test_gpt2_wgrad(gpt2_codes, splits):
     dw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(splits * N * K, dtype=torch.float32, device=DEV)
     sq.fp8_gemm_scaled_splitk(dyt, O.E5M2, at, O.E4M3, splits, _dev_f32(1.0 / np.float32(s_dy)),
-                              _dev_f32(1.0 / np.float32(s_a)), ws, dw)
+                              _dev_f32(1.0 / np.float32(s_a)), ws, dw, accum)
     dyt_h, at_h = np.ascontiguousarray(dy8.T), np.ascontiguousarray(a8.T)
     assert np.array_equal(u8_np(dyt), dyt_h)
-    rows = np.array([0, 101, 383, 512, 767])
+    # 128 of the 768 weight-gradient rows: every 6th, the last, seeded others
+    rng = np.random.default_rng(splits)
+    rows = np.unique(np.concatenate([np.arange(0, N, 6), [N - 1],
+                                     rng.integers(0, N, 8)]))[:136]
+    assert rows.size >= 128
     ref, absref = oracle_gemm_rows(dyt_h, O.E5M2, at_h, O.E4M3, O.PER_TENSOR, s_dy, s_a, rows)
-    allow = fp8_mfma_allowance(dyt_h, O.E5M2, at_h, O.E4M3, O.PER_TENSOR, s_dy, s_a, rows)
-    _check(dw.float().cpu().numpy()[rows], ref, absref, allow, f"wgrad/{splits}", GRAD_CAP)
+    check_gemm(dw.float().cpu().numpy()[rows], ref, absref, f"wgrad/{splits}", accum == EXACT,
+               lambda sel: fp8_mfma_allowance(dyt_h, O.E5M2, at_h, O.E4M3, O.PER_TENSOR, s_dy, s_a, rows[sel]))

@@ -29,8 +29,8 @@ import torch
 import oracle as O
 import scaled_quantization_amd as sq
 import workloads
-from gpu_util import (DEV, fp8_mfma_allowance, oracle_gemm_rows, oracle_quantize, to_dev_u8,
-                      within_bound)
+from gpu_util import (DEV, check_gemm, fp8_mfma_allowance, oracle_gemm_rows, oracle_quantize,
+                      to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 EXACT, FP8 = sq.ACCUM_EXACT, sq.ACCUM_MFMA_FP8
@@ -50,29 +50,8 @@ def _gemm(a8, fa, w8, fb, mode, sa_inv, sb_inv, accum):
     return y.float().cpu().numpy()
 
 
-def _fail_on(bad, y, ref, what):
-    if bad.any():
-        idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the bound, e.g. "
-                             + str([(tuple(map(int, i)), float(y[tuple(i)]), float(ref[tuple(i)]))
-                                    for i in idx]))
-
-
 def _check(y, ref, absref, what, accum=EXACT, allowance=None):
-    """Every element within the plain bound.  In FP8 mode, elements outside it
-    must be covered by the truncation allowance (allowance() computes it), and
-    the case is then an expected failure of that mode."""
-    y = np.asarray(y, np.float64)
-    bad = ~within_bound(y, ref, absref)
-    if accum == EXACT or not bad.any():
-        _fail_on(bad, y, ref, what)
-        return
-    if allowance is not None:
-        bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
-        _fail_on(np.abs(y - ref) > bound + allowance(), y, ref,
-                 f"{what} (beyond the FP8 instructions' truncation)")
-    pytest.xfail(f"{what}: {int(bad.sum())} of {bad.size} outputs outside the plain bound -- "
-                 "the FP8 matrix instructions truncate small products (exact mode meets it)")
+    check_gemm(y, ref, absref, what, accum == EXACT, allowance)
 
 
 def _tensor_case(name, t=0):
@@ -97,7 +76,7 @@ def test_tiny_gemm_all_outputs(t, accum):
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, si_a, si_w, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, s_a, s_w)
     _check(y, ref, absref, f"tiny step {t}", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, range(w.M)))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, sel))
 
 
 @BOTH
@@ -111,7 +90,7 @@ def test_per_tensor_gemm_full_size_sampled_rows(name, nrows, accum):
     ref, absref = oracle_gemm_rows(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, s_a, s_w, rows)
     assert np.isfinite(y).all()
     _check(y[rows], ref, absref, name, accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, rows))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, s_a, s_w, rows[sel]))
 
 
 @BOTH
@@ -132,7 +111,7 @@ def test_fine_grained_block_scaled_gemm_sampled_rows(accum):
     ref, absref = oracle_gemm_rows(r.fp8, O.E4M3, q_w, O.E4M3, O.PER_GROUP128, s_a, s_w, rows)
     assert np.isfinite(yv).all()
     _check(yv[rows], ref, absref, "fine", accum,
-           lambda: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, s_a, s_w, rows))
+           lambda sel: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, s_a, s_w, rows[sel]))
 
 
 @BOTH
@@ -156,7 +135,7 @@ def test_gpt2_per_group_gemm_full_size_sampled_rows(accum):
                                    s_w, rows)
     assert np.isfinite(yv).all()
     _check(yv[rows], ref, absref, "gpt2 per-group", accum,
-           lambda: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, r.group_scale, s_w, rows))
+           lambda sel: fp8_mfma_allowance(r.fp8, 0, q_w, 0, O.PER_GROUP128, r.group_scale, s_w, rows[sel]))
 
 
 @BOTH
@@ -177,7 +156,7 @@ def test_random_full_range_codes_over_long_k(K, accum):
         # 2^-8 relative) the error stays far inside the 1e-5 term
         assert np.all(np.abs(y - ref) <= (2.0 ** -8) * np.abs(ref) + 1e-6 * absref)
     _check(y, ref, absref, f"K={K}", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 64.0, 32.0, range(M)))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 64.0, 32.0, sel))
 
 
 @BOTH
@@ -201,7 +180,7 @@ def test_operand_format_combinations(fa, fb, M, N, K, accum):
         y = _gemm(a8, fa, w8, fb, mode, 1 / sa, 1 / sb, accum)
         ref, absref = O.gemm_f64(a8, fa, w8, fb, mode, sa, sb)
         _check(y, ref, absref, f"fa={fa} fb={fb} mode={mode}", accum,
-               lambda: fp8_mfma_allowance(a8, fa, w8, fb, mode, sa, sb, range(M)))
+               lambda sel: fp8_mfma_allowance(a8, fa, w8, fb, mode, sa, sb, sel))
 
 
 @BOTH
@@ -263,7 +242,7 @@ def test_non_multiple_of_eight_tile_grid(accum):
     y = _gemm(a8, 0, w8, 0, sq.PER_TENSOR, 0.25, 0.125, accum)
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 4.0, 8.0)
     _check(y, ref, absref, "15 tiles", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 4.0, 8.0, range(M)))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 4.0, 8.0, sel))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 256), (2304, 768, 640), (4096, 4096, 256),
@@ -285,7 +264,7 @@ def test_large_tile_paths(M, N, K, accum):
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 64)), [M - 1]]))
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
     _check(y[rows], ref, absref, f"{M}x{N}x{K}", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows[sel]))
 
 
 @pytest.mark.parametrize("M,N,K", [(5376, 3072, 512), (33024, 384, 256), (20480, 1024, 1024),
@@ -307,7 +286,7 @@ def test_persistent_grid_paths(M, N, K, accum):
                                      rng.integers(0, M, 16)]))
     ref, absref = O.gemm_f64(a8, O.E4M3, w8, O.E4M3, O.PER_TENSOR, 2.0, 4.0, rows=rows)
     _check(y[rows], ref, absref, f"{M}x{N}x{K}", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_TENSOR, 2.0, 4.0, rows[sel]))
 
 
 def _group_case(M, N, K, fa, fb):
@@ -341,7 +320,7 @@ def test_group_scaled_shapes(M, N, K, fa, fb, accum):
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 48)), [M - 1]]))
     ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
     _check(y[rows], ref, absref, f"group {M}x{N}x{K} fa={fa} fb={fb}", accum,
-           lambda: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows))
+           lambda sel: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows[sel]))
 
 
 # Ragged M (a token count that does not fill a tile): the rows that fill
@@ -376,7 +355,7 @@ def test_ragged_rows(M, mode, accum):
         y_b = _gemm(a8[:Mb], 0, w8, 0, mode, 1 / sa_b, 1 / sb, accum)
         assert np.array_equal(y[:Mb].view(np.uint32), y_b.view(np.uint32))
     _check(y[rows], ref, absref, f"ragged M={M} mode={mode}", accum,
-           lambda: fp8_mfma_allowance(a8, 0, w8, 0, mode, sa, sb, rows))
+           lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, mode, sa, sb, rows[sel]))
 
 
 # On a 256-CU GPU these shapes take the 256 x 192 per-group tiles (one round
@@ -396,7 +375,7 @@ def test_group_wide_tiles_match_narrow_tiles(M, N, K, fa, fb):
     rows = np.unique(np.concatenate([np.arange(0, M, M // 24), [M - 1]]))
     ref, absref = O.gemm_f64(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows=rows)
     _check(y[rows], ref, absref, f"wide group tiles {M}x{N}x{K}", FP8,
-           lambda: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows))
+           lambda sel: fp8_mfma_allowance(a8, fa, w8, fb, O.PER_GROUP128, sa, sb, rows[sel]))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 2048), (256, 256, 512)])
@@ -425,4 +404,4 @@ def test_group_scaled_kernels_agree(M, N, K, accum):
     ref, absref = O.gemm_f64(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows=rows)
     for got, what in ((y2, "small-tile kernel"), (y, "ring kernel")):
         _check(got, ref, absref, what, accum,
-               lambda: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows))
+               lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows[sel]))

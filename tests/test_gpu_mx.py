@@ -18,7 +18,7 @@ import torch
 import oracle as O
 import scaled_quantization_amd as sq
 import workloads
-from gpu_util import (DEV, THREADS, bf16_np, fp8_mfma_allowance_mx, to_dev_bf16, to_dev_u8,
+from gpu_util import (DEV, THREADS, bf16_np, check_gemm, fp8_mfma_allowance_mx, to_dev_bf16, to_dev_u8,
                       u8_np)
 
 pytestmark = pytest.mark.gpu
@@ -150,12 +150,11 @@ def test_quantize_mx_errors():
 
 
 # ------------------------------------------------------------------ GEMM
-def _check(y, ref, absref, allow, what, cap=1e-3):
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
-    err = np.abs(np.asarray(y, np.float64) - ref)
-    bad = err > bound + allow
-    assert not bad.any(), f"{what}: {int(bad.sum())} outside bound + allowance"
-    assert (err > bound).mean() <= cap, f"{what}: {(err > bound).mean():.2e} outside the plain bound"
+def _check(y, ref, absref, allowance, what):
+    """The plain bound on every element; elements the microscaled FP8
+    instruction's truncation takes outside it make the case an expected
+    failure (after the allowance accounts for each of them)."""
+    check_gemm(y, ref, absref, what, False, allowance)
 
 
 def _gemm_case(rng, M, N, K, fa, fb, lo=-12, hi=12):
@@ -182,8 +181,8 @@ def test_gemm_mx_vs_oracle(M, N, K, fa, fb):
     y = _gemm_mx_dev(a8, fa, ea, b8, fb, eb)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 24)), [M - 1]]))
     ref, absref = O.gemm_mx_f64(a8, fa, ea, b8, fb, eb, rows)
-    allow = fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, rows)
-    _check(y[rows], ref, absref, allow, f"{M}x{N}x{K}")
+    _check(y[rows], ref, absref,
+           lambda sel: fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, rows[sel]), f"{M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 384, 1536), (256, 256, 512)])
@@ -209,8 +208,8 @@ def test_gemm_mx_exponent_copy_paths_agree(M, N, K):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     rows = np.unique(np.concatenate([np.arange(0, M, 16), [M - 1]]))
     ref, absref = O.gemm_mx_f64(a8, 0, ea, b8, 0, eb, rows)
-    allow = fp8_mfma_allowance_mx(a8, 0, ea, b8, 0, eb, rows)
-    _check(y.float().cpu().numpy()[rows], ref, absref, allow, f"{M}x{N}x{K}")
+    _check(y.float().cpu().numpy()[rows], ref, absref,
+           lambda sel: fp8_mfma_allowance_mx(a8, 0, ea, b8, 0, eb, rows[sel]), f"{M}x{N}x{K}")
 
 
 def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
@@ -230,7 +229,8 @@ def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
         y2 = torch.empty_like(y)
         sa = torch.tensor([2.0 ** i], dtype=torch.float32, device=DEV)
         sb = torch.tensor([2.0 ** j], dtype=torch.float32, device=DEV)
-        sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(b8), 0, sq.PER_TENSOR, sa, sb, y2)
+        sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(b8), 0, sq.PER_TENSOR, sa, sb, y2,
+                           sq.ACCUM_MFMA_FP8)
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (i, j)
 
 
@@ -253,8 +253,9 @@ def test_gemm_mx_gpt2_down_projection():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     sq.fp8_gemm_mx(qa, sq.E4M3, ea, qb, sq.E4M3, eb, y)
     ref, absref = O.gemm_mx_f64(ra.fp8, O.E4M3, ra.scale, rb.fp8, O.E4M3, rb.scale)
-    allow = fp8_mfma_allowance_mx(ra.fp8, 0, ra.scale, rb.fp8, 0, rb.scale, np.arange(24))
-    _check(y.float().cpu().numpy()[rows], ref, absref, allow, "gpt2 mx")
+    _check(y.float().cpu().numpy()[rows], ref, absref,
+           lambda sel: fp8_mfma_allowance_mx(ra.fp8, 0, ra.scale, rb.fp8, 0, rb.scale, sel),
+           "gpt2 mx")
 
 
 def test_gemm_mx_errors():

@@ -98,3 +98,60 @@ def test_gradient_cast_codes_amax_and_saturation():
         mags = (r.bf16 & 0x7FFF).astype(np.uint32) << 16
         assert r.amax_bits == int(mags.max())
     assert r.sat > 0      # the largest scale saturates some elements
+
+
+def _f32_order(dA_bits, dec, si, order):
+    """dH in binary32, one nearest-even operation at a time, in a given order,
+    evaluated with numpy float32 (an implementation separate from the oracle's
+    C): 'oracle' is the stated reading a = dec * si; r = sqrt(a); g = (2 r) dA.
+    (The doubling is exact, so where it sits does not matter.)"""
+    with np.errstate(invalid="ignore", over="ignore"):
+        dA = R.f32_from_bf16(dA_bits)
+        dec = np.asarray(dec, np.float32)
+        si = np.float32(si)
+        if order == "oracle":
+            return (np.float32(2.0) * np.sqrt(dec * si)) * dA
+        if order == "divide":                 # a = dec / s instead of dec * (1/s)
+            return (np.float32(2.0) * np.sqrt(dec / (np.float32(1.0) / si))) * dA
+        if order == "split_sqrt":             # r = sqrt(dec) sqrt(si)
+            return (np.float32(2.0) * (np.sqrt(dec) * np.sqrt(si))) * dA
+        if order == "scale_last":             # g = 2 sqrt(dec) dA, then times sqrt(si)
+            return ((np.float32(2.0) * np.sqrt(dec)) * dA) * np.sqrt(si)
+    raise ValueError(order)
+
+
+@pytest.mark.parametrize("cache_fmt", [O.E4M3, O.E5M2])
+def test_operation_order_at_the_ulp(cache_fmt):
+    """The BF16 dH of an FP8 cache bit for bit against the numpy float32
+    formulation of the same order, for 1024 inverse scales that are not
+    powers of two, each with every positive finite code x every BF16 dA in
+    [1, 2): on a random subset, and on every input whose binary32 result lies
+    within two ulps of a BF16 rounding midpoint (where a one-ulp change of the
+    binary32 value flips the stored BF16 value; elsewhere the final BF16
+    rounding hides it).  Each of three plausible reorderings differs from the
+    oracle on some of those, so the comparison fixes the order, not just the
+    value within the formats' error."""
+    rng = np.random.default_rng(7 + cache_fmt)
+    table = R.torch_decode_table(cache_fmt).astype(np.float32)
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[np.isfinite(table[codes]) & (table[codes] > 0)]
+    mant = np.arange(127 << 7, 128 << 7, dtype=np.uint16)          # BF16 values in [1, 2)
+    c = np.repeat(codes, mant.size)
+    dA = np.tile(mant, codes.size)
+    dec = table[c]
+    hits = {"divide": 0, "split_sqrt": 0, "scale_last": 0}
+    near_total = 0
+    for si in rng.uniform(1e-3, 0.9, 1024).astype(np.float32):
+        g = _f32_order(dA, dec, si, "oracle")
+        low = (g.view(np.uint32) & 0xFFFF).astype(np.int64)
+        pick = np.concatenate([np.flatnonzero(np.abs(low - 0x8000) <= 2),
+                               rng.integers(0, c.size, 8)])
+        near_total += pick.size - 8
+        r = O.relu2_backward(dA[pick], c[pick], cache_fmt, float(si), O.E5M2, 1.0)
+        want = R.torch_bf16(g[pick])
+        assert np.array_equal(r.bf16, want), si
+        for order in hits:
+            other = R.torch_bf16(_f32_order(dA[pick], dec[pick], si, order))
+            hits[order] += int((other != want).sum())
+    assert near_total > 500, near_total
+    assert all(v > 0 for v in hits.values()), hits
