@@ -1,16 +1,29 @@
 """Benchmark of the FP8 down-projection hot path on one GPU.
 
 One step = one pass of the whole path over one batch of the GPT-2-scale
-workload (H [16384 x 3072] BF16, 8 sequences x 2048 tokens):
+workload (H [16384 x 3072] BF16, 8 sequences x 2048 tokens), four kernels:
   1. quantize_fused: squared-ReLU, BF16 copy, E4M3 cast with the delayed
-     scale, running amax and saturation count (one kernel);
+     scale, running amax and saturation count;
   2. fp8_gemm_scaled: Y [16384 x 768] = A8 [16384 x 3072] x W8^T, FP32
-     accumulation, BF16 output, per-tensor scales in the epilogue;
-  3. amax_history_update for the activation state;
-  4. quantize_fused on the output gradient dY [16384 x 768] to E5M2 (delayed);
-  5. amax_history_update for the gradient state.
+     accumulation, BF16 output, per-tensor scales (the activation's
+     scale_inv, the inverse of the scale the codes were cast with) in the
+     epilogue;
+  3. amax_history_update of the activation's state (history, next scale,
+     overflow flag);
+  4. quantize_fused_update on the output gradient dY [16384 x 768] to E5M2
+     (delayed), whose last workgroup also closes the gradient's step.
+Each cast takes the faster of its two measured forms: one launch that also
+closes the step costs each workgroup a wait for its atomics, more than the
+separate update's launch on the large activation and less on the small
+gradient (both forms are timed and reported).
 Each step reads its own pre-generated input H_t (16 drifting steps, cycled),
 so the working set does not stay in the last-level cache.
+
+The GEMM of the step sums exactly (ACCUM_EXACT: the FP8 codes widened to
+FP16 in registers, the FP16 matrix instructions, FP32 accumulation), the mode
+that meets |err| <= 2^-8 |ref| + 1e-5 sum|ab| on every output; the FP8
+matrix instructions' mode (ACCUM_MFMA_FP8, faster, outside that bound on
+some outputs) is timed beside it with its measured out-of-bound fractions.
 
 Prints ONE JSON line.  `ms_per_step` is the time of --steps whole steps
 between two events.  `value` is the fused quantizer's throughput: algorithmic
@@ -37,6 +50,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 BURST_WARM_MS = 8.0           # GPU time of a kernel's own launches before its timed bursts
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense FP16 MFMA (the exact GEMM's instruction)
 METRIC = "fused FP8 quantize GB/s (% HBM peak); FP8 down-proj GEMM TFLOPS (% peak)"
 
 
@@ -51,8 +65,8 @@ def parse():
     p.add_argument("--no-large", action="store_true",
                    help="skip the large-configuration leg (H 65536 x 16384) and the "
                         "fine-grained one (H 65536 x 4096, per-128 groups)")
-    p.add_argument("--only", choices=("quantize", "gemm", "copy", "quantize_mx", "gemm_mx",
-                                      "relu2_bwd", "gemm_pg"), default=None,
+    p.add_argument("--only", choices=("quantize", "quantize_update", "gemm", "gemm_fp8", "copy", "quantize_mx",
+                                      "gemm_mx", "relu2_bwd", "gemm_pg"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
                         "inputs (for hardware counter runs), then exit")
     return p.parse_args()
@@ -115,14 +129,23 @@ def main():
 
     def gemm(i):
         sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
-                           st_a.field_ptr("scale_inv"), wsc, Y)
+                           st_a.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT)
+
+    def gemm_fp8(i):
+        sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                           st_a.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_MFMA_FP8)
+
+    def update_a(i):
+        sq.amax_history_update(st_a)
+
+    def dy_cast(i):
+        sq.quantize_fused_update(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2, st_g, None, DY8)
 
     def step(i):
         quant(i)
         gemm(i)
-        sq.amax_history_update(st_a)
-        sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, DY8)
-        sq.amax_history_update(st_g)
+        update_a(i)
+        dy_cast(i)
 
     for i in range(args.warmup):
         step(i)
@@ -182,15 +205,23 @@ def main():
 
     q_mean = burst(quant, "quantize_fused")
     g_mean = burst(gemm, "fp8_gemm_scaled")
-    dy_mean = burst(lambda i: sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2,
-                                                sq.PER_TENSOR, st_g, None, DY8))
-    up_mean = burst(lambda i: sq.amax_history_update(st_a))
+    g8_mean = burst(gemm_fp8, "fp8_gemm_scaled_mfma_fp8")
+    dy_mean = burst(dy_cast)
+    up_mean = burst(update_a)
+    # the other form of each cast, for comparison (the pair as the step runs it)
+    q_fused_upd = burst(lambda i: sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3,
+                                                           st_a, A16[i % n_out], A8[i % n_out]))
+    q_pair = burst(lambda i: (quant(i), update_a(i)))
+    dy_pair = burst(lambda i: (sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2,
+                                                 sq.PER_TENSOR, st_g, None, DY8),
+                               sq.amax_history_update(st_g)))
 
     elems = M * K
     q_bytes = elems * w.quant_bytes_per_elem()
     q_gbs = q_bytes / (q_mean * 1e-3) / 1e9
     flops = w.gemm_flops()
     g_tflops = flops / (g_mean * 1e-3) / 1e12
+    g8_tflops = flops / (g8_mean * 1e-3) / 1e12
     dy_bytes = M * N * 3.0
 
     out = {
@@ -209,7 +240,7 @@ def main():
                 "N(0,0.02) weight, log-normal sigma=3 gradient)",
         "config": {"workload": f"{args.workload}: H[{M}x{K}] bf16 -> relu2 -> bf16 copy + e4m3 "
                                f"(delayed, margin {w.margin}); GEMM Y[{M}x{N}] = A8 x W8[{N}x{K}]^T "
-                               f"bf16 out; dY[{M}x{N}] -> e5m2 (delayed)",
+                               f"bf16 out (exact accumulation); dY[{M}x{N}] -> e5m2 (delayed)",
                    "M": M, "K": K, "N": N, "global_batch": 8, "seq_len": 2048,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -217,19 +248,35 @@ def main():
                      "traffic": measured_traffic("quantize_fused_gpt2", "quantize.hip")},
         "kernels": {
             "quantize_fused": {"ms": round(q_mean, 5), "GB/s": round(q_gbs, 1),
-                               "bytes_per_launch": q_bytes},
+                               "bytes_per_launch": q_bytes,
+                               "with_amax_history_update_ms": round(q_pair, 5),
+                               "quantize_fused_update_ms": round(q_fused_upd, 5)},
             "fp8_gemm_scaled": {"ms": round(g_mean, 5), "TFLOP/s": round(g_tflops, 1),
+                                "accum": "exact: FP8 codes widened to FP16, FP16 MFMA, FP32 sums",
+                                "meets_bound_on_every_output": True,
+                                "frac_of_fp16_mfma_peak": round(g_tflops / FP16_PEAK_TFLOPS, 4),
                                 "frac_of_fp8_peak": round(g_tflops / FP8_PEAK_TFLOPS, 4),
                                 "flops_per_launch": flops},
-            "quantize_fused_dy_e5m2": {"ms": round(dy_mean, 5),
-                                       "GB/s": round(dy_bytes / (dy_mean * 1e-3) / 1e9, 1),
-                                       "bytes_per_launch": dy_bytes},
+            "quantize_fused_update_dy_e5m2": {"ms": round(dy_mean, 5),
+                                              "GB/s": round(dy_bytes / (dy_mean * 1e-3) / 1e9, 1),
+                                              "bytes_per_launch": dy_bytes,
+                                              "quantize_fused_then_update_ms": round(dy_pair, 5)},
             "amax_history_update": {"ms": round(up_mean, 5)},
         },
         "gemm_roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
-                          "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(g_tflops / FP8_PEAK_TFLOPS, 4),
+                          "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(g_tflops / FP16_PEAK_TFLOPS, 4),
+                          "peak_note": "FP16 MFMA, the instruction the exact GEMM runs; the FP8 "
+                                       "target is 0.6 of 5000 TFLOP/s",
+                          "frac_of_fp8_peak": round(g_tflops / FP8_PEAK_TFLOPS, 4),
                           "traffic": measured_traffic("fp8_gemm_scaled_gpt2", "gemm.hip")},
+        "gemm_fp8_mfma_mode": {
+            "ms": round(g8_mean, 5), "TFLOP/s": round(g8_tflops, 1),
+            "frac_of_fp8_peak": round(g8_tflops / FP8_PEAK_TFLOPS, 4),
+            "accum": "FP8 MFMA (truncates small products in groups of 8)",
+            "meets_bound_on_every_output": False,
+            "outside_bound_fraction": None,
+            "traffic": measured_traffic("fp8_gemm_scaled_mfma_fp8_gpt2", "gemm.hip")},
         "burst_ms": bursts,
         "burst_warmup_ms": BURST_WARM_MS,
         "last_step": {"scale": st_read["scale"], "amax": st_read["amax_last"],
@@ -240,7 +287,6 @@ def main():
     if not args.no_naive:
         out["naive_three_pass"] = naive(sq, torch, H, A16[0], A8[0], n_in, args, dev, q_bytes,
                                         elems, q_mean)
-    out["gemm_exact_accumulation"] = gemm_exact(sq, torch, A8[0], w8, st_a, wsc, Y, args, flops)
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
     out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
@@ -256,7 +302,8 @@ def main():
         out["large_config"] = large_config(sq, torch, dev, args)
         out["fine_grained_config"] = fine_grained(sq, torch, dev, args)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"], oob = cpu_baseline(w, sq, torch, dev)
+        out["gemm_fp8_mfma_mode"]["outside_bound_fraction"] = oob
     print(json.dumps(out), flush=True)
 
 
@@ -302,16 +349,21 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
             sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, wg8, sq.E4M3, sq.PER_GROUP128,
                                GS[i % n_out], wgs, Y)
         elif args.only == "gemm_mx":
-            sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], wm8, sq.E4M3, we, Y)
+            sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], wm8, sq.E4M3, we, Y,
+                           sq.ACCUM_EXACT)
         elif args.only == "relu2_bwd":
             sq.relu2_backward_quantize(dA, A8[i % n_out], sq.CACHE_E4M3,
                                        st_a.field_ptr("scale_inv"), sq.E5M2, st_h, dH8[i % 2])
         elif args.only == "quantize":
             sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a,
                               A16[i % n_out], A8[i % n_out])
-        elif args.only == "gemm":
+        elif args.only == "quantize_update":
+            sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3, st_a, A16[i % n_out],
+                                     A8[i % n_out])
+        elif args.only in ("gemm", "gemm_fp8"):
             sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
-                               st_a.field_ptr("scale_inv"), wsc, Y)
+                               st_a.field_ptr("scale_inv"), wsc, Y,
+                               sq.ACCUM_EXACT if args.only == "gemm" else sq.ACCUM_MFMA_FP8)
         else:
             copy_buffers(torch, dev)
             sq.fp8dp_bench_copy(*_COPY[i % 2])
@@ -507,17 +559,24 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
     q = timed(lambda i: sq.quantize_mx(H[i % n_in], sq.ACT_RELU2, sq.E4M3, A8[i % n_out],
                                        E[i % n_out], A16[i % n_out]))
     qw = timed(lambda i: sq.quantize_mx(wt, sq.ACT_IDENTITY, sq.E4M3, w8, we))
-    g = timed(lambda i: sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], w8, sq.E4M3, we, Y))
+    g = timed(lambda i: sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], w8, sq.E4M3, we, Y,
+                                       sq.ACCUM_EXACT))
+    g8 = timed(lambda i: sq.fp8_gemm_mx(A8[i % n_out], sq.E4M3, E[i % n_out], w8, sq.E4M3, we, Y,
+                                        sq.ACCUM_MFMA_FP8))
     q_bytes = M * K * (2 + 2 + 1) + M * K // 32
     flops = w.gemm_flops()
-    tf = flops / (g * 1e-3) / 1e12
+    tf, tf8 = flops / (g * 1e-3) / 1e12, flops / (g8 * 1e-3) / 1e12
     return {"quantize_mx": {"ms": round(q, 5), "GB/s": round(q_bytes / (q * 1e-3) / 1e9, 1),
                             "bytes_per_launch": q_bytes,
                             "vs_per_tensor_quantize": round(q_tensor_ms / q, 3)},
             "quantize_mx_weight_ms": round(qw, 5),
-            "fp8_gemm_mx": {"ms": round(g, 5), "TFLOP/s": round(tf, 1),
+            "fp8_gemm_mx": {"accum": "exact (block exponents folded into the FP16 widening)",
+                            "ms": round(g, 5), "TFLOP/s": round(tf, 1),
+                            "frac_of_fp16_mfma_peak": round(tf / FP16_PEAK_TFLOPS, 4),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
-                            "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)}}
+                            "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)},
+            "fp8_gemm_mx_mfma_fp8": {"ms": round(g8, 5), "TFLOP/s": round(tf8, 1),
+                                     "frac_of_fp8_peak": round(tf8 / FP8_PEAK_TFLOPS, 4)}}
 
 
 def per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
@@ -611,34 +670,52 @@ def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):
 
 
 def graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8, st_a, st_g, args, eager_ms):
-    """The same step captured once in a HIP graph and replayed (no per-kernel
-    host launch work): one graph per input/output buffer set, replayed in the
-    step's rotation."""
+    """The same step captured in HIP graphs and replayed (no per-kernel host
+    launch work): a graph of one step per input/output buffer set, replayed in
+    the step's rotation, and one graph of all n steps of the rotation (one
+    graph launch per n steps).  A replay is not faster than the eager stream
+    here: the eager launches are queued far ahead of the GPU (the host is not
+    the bottleneck), and the graph's kernel nodes are dispatched with a
+    dependency barrier between consecutive nodes."""
     n = min(len(H), len(A8), len(DY))
+
+    def one(i):
+        sq.quantize_fused(H[i], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, A16[i], A8[i])
+        sq.fp8_gemm_scaled(A8[i], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                           st_a.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT)
+        sq.amax_history_update(st_a)
+        sq.quantize_fused_update(DY[i], sq.ACT_IDENTITY, sq.E5M2, st_g, None, DY8)
+
     graphs = []
     torch.cuda.synchronize()
     for i in range(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            sq.quantize_fused(H[i], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, A16[i], A8[i])
-            sq.fp8_gemm_scaled(A8[i], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
-                               st_a.field_ptr("scale_inv"), wsc, Y)
-            sq.amax_history_update(st_a)
-            sq.quantize_fused(DY[i], sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, DY8)
-            sq.amax_history_update(st_g)
+            one(i)
         graphs.append(g)
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for i in range(n):
+            one(i)
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        graphs[i % n].replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(args.steps):
-        graphs[i % n].replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
-    return {"ms_per_step": round(ms, 5), "eager_ms_per_step": round(eager_ms, 5)}
+
+    def timed(replay, reps):
+        for i in range(max(args.warmup, 1)):
+            replay(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            replay(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    ms = timed(lambda i: graphs[i % n].replay(), args.steps) / args.steps
+    reps_all = max(1, args.steps // n)
+    ms_all = timed(lambda i: g_all.replay(), reps_all) / (reps_all * n)
+    return {"ms_per_step": round(ms, 5), "one_graph_of_all_steps_ms_per_step": round(ms_all, 5),
+            "eager_ms_per_step": round(eager_ms, 5)}
 
 
 def recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args, step_ms):
@@ -700,25 +777,6 @@ def recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args, step_ms):
             "overflow_flags_idle_hot": [flag_idle, st_hot.read()["overflow"]]}
 
 
-def gemm_exact(sq, torch, a8, w8, st, wsc, Y, args, flops):
-    """The same GEMM with FP16-widened operands (FP32-accurate accumulation)."""
-    stream = torch.cuda.current_stream()
-    call = lambda: sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
-                                      st.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(args.steps):
-        call()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
-    tf = flops / (ms * 1e-3) / 1e12
-    return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1), "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
-
-
 def burst_median(torch, stream, fn, per_burst):
     """ms per launch of fn: BURST_WARM_MS of its own launches first, then 5
     bursts of per_burst launches between two events; the median burst."""
@@ -744,33 +802,38 @@ def burst_median(torch, stream, fn, per_burst):
     return sorted(per)[2]
 
 
+def _upload_bf16(torch, bits, dev):
+    """uint16 BF16 patterns (host) -> a BF16 device tensor."""
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
 def large_config(sq, torch, dev, args):
     """The large layer's forward and gradient casts and its GEMM at full size:
     H[65536 x 16384] -> relu2 -> BF16 copy + E4M3 (delayed, margin 1.25),
-    dY[65536 x 4096] -> E5M2 (delayed), Y = A8 x W8[4096 x 16384]^T.  Inputs
-    come from torch's seeded device generator with the configuration's
-    distributions (H ~ N(0,1); W ~ N(0, 0.02); dY signed log-normal, sigma 3);
-    each kernel is timed like the step's (8 ms of its own launches first, then
-    5 bursts; the median burst's mean)."""
-    M, K, N = 65536, 16384, 4096
+    dY[65536 x 4096] -> E5M2 (delayed), Y = A8 x W8[4096 x 16384]^T (exact
+    accumulation; the FP8-instruction mode beside it).  Inputs are the large
+    workload's seeded bytes (workloads.py: H ~ N(0,1), W ~ N(0, 0.02), dY signed
+    log-normal sigma 3), the bytes the parity tests check; each kernel is timed
+    like the step's (8 ms of its own launches first, then 5 bursts; the median
+    burst's mean), after one step that sets the delayed scales."""
+    import workloads
+    w = workloads.get("large")
+    M, K, N = w.M, w.K, w.N
     stream = torch.cuda.current_stream()
-    g = torch.Generator(device=dev)
-    g.manual_seed(20240)
-    H = torch.randn((M, K), generator=g, device=dev, dtype=torch.bfloat16)
+    H = _upload_bf16(torch, w.h0(), dev)
     A16 = torch.empty_like(H)
     A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    W = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    W = _upload_bf16(torch, w.weight(), dev)
     W8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
     wsc = torch.empty(2, dtype=torch.float32, device=dev)   # [1/s, s]
     sq.quantize_weight(W, sq.E4M3, sq.PER_TENSOR, W8, wsc)
     del W
-    DY = (torch.exp(3.0 * torch.randn((M, N), generator=g, device=dev, dtype=torch.float32))
-          * torch.sign(torch.randn((M, N), generator=g, device=dev, dtype=torch.float32))
-          ).to(torch.bfloat16)
+    DY = _upload_bf16(torch, w.dy(), dev)
     DY8 = torch.empty((M, N), dtype=torch.uint8, device=dev)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    st_a = sq.TensorState(sq.E4M3, 16, 1.25, 1.0, device=dev)
-    st_g = sq.TensorState(sq.E5M2, 16, 1.25, 1.0, device=dev)
+    st_a = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
+    st_g = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
     sq.quantize_fused(H, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, None, None)
     sq.amax_history_update(st_a)
     sq.quantize_fused(DY, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, None)
@@ -780,17 +843,24 @@ def large_config(sq, torch, dev, args):
     q = timed(lambda: sq.quantize_fused(H, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, A16, A8),
               16)
     gm = timed(lambda: sq.fp8_gemm_scaled(A8, sq.E4M3, W8, sq.E4M3, sq.PER_TENSOR,
-                                          st_a.field_ptr("scale_inv"), wsc, Y), 4)
+                                          st_a.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT), 4)
+    g8 = timed(lambda: sq.fp8_gemm_scaled(A8, sq.E4M3, W8, sq.E4M3, sq.PER_TENSOR,
+                                          st_a.field_ptr("scale_inv"), wsc, Y,
+                                          sq.ACCUM_MFMA_FP8), 4)
     dy = timed(lambda: sq.quantize_fused(DY, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None,
                                          DY8), 16)
     qb, dyb, fl = M * K * 5, M * N * 3, 2 * M * N * K
+    tf = lambda ms: fl / (ms * 1e-3) / 1e12
     out = {"shape": f"H[{M}x{K}] relu2 -> bf16 copy + e4m3; Y[{M}x{N}] = A8 x W8[{N}x{K}]^T; "
                     f"dY[{M}x{N}] -> e5m2",
+           "data": "workloads.py large (seed 4): the parity tests' bytes",
            "quantize_fused": {"ms": round(q, 4), "GB/s": round(qb / (q * 1e-3) / 1e9, 1),
                               "frac_of_hbm_peak": round(qb / (q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-           "fp8_gemm_scaled": {"ms": round(gm, 4), "TFLOP/s": round(fl / (gm * 1e-3) / 1e12, 1),
-                               "frac_of_fp8_peak": round(fl / (gm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-                                                         4)},
+           "fp8_gemm_scaled": {"ms": round(gm, 4), "TFLOP/s": round(tf(gm), 1), "accum": "exact",
+                               "frac_of_fp16_mfma_peak": round(tf(gm) / FP16_PEAK_TFLOPS, 4),
+                               "frac_of_fp8_peak": round(tf(gm) / FP8_PEAK_TFLOPS, 4)},
+           "fp8_gemm_scaled_mfma_fp8": {"ms": round(g8, 4), "TFLOP/s": round(tf(g8), 1),
+                                        "frac_of_fp8_peak": round(tf(g8) / FP8_PEAK_TFLOPS, 4)},
            "quantize_fused_dy_e5m2": {"ms": round(dy, 4),
                                       "GB/s": round(dyb / (dy * 1e-3) / 1e9, 1),
                                       "frac_of_hbm_peak": round(dyb / (dy * 1e-3) / 1e9
@@ -801,26 +871,23 @@ def large_config(sq, torch, dev, args):
 
 
 def fine_grained(sq, torch, dev, args):
-    """The fine-grained configuration at full size: H[65536 x 4096] with
-    Student-t (nu = 3) values (z / sqrt(chi2_3 / 3) from torch's seeded device
-    generator) cast with current per-128-group scales (identity, E4M3 codes
-    and one FP32 inverse scale per 1 x 128 group, no BF16 copy); W[1024 x 4096]
-    ~ N(0, 0.02) cast with 128 x 128 block scales; the per-group GEMM
-    Y[65536 x 1024] = A8 x W8^T promoting every 128-wide partial sum by
-    sa[m, g] sb[n / 128, g].  Timed like the large configuration's kernels."""
-    M, K, N = 65536, 4096, 1024
+    """The fine-grained configuration at full size: H[65536 x 4096] of
+    Student-t (nu = 3) values cast with current per-128-group scales
+    (identity, E4M3 codes and one FP32 inverse scale per 1 x 128 group, no
+    BF16 copy); W[1024 x 4096] ~ N(0, 0.02) cast with 128 x 128 block scales;
+    the per-group GEMM Y[65536 x 1024] = A8 x W8^T promoting every 128-wide
+    partial sum by sa[m, g] sb[n / 128, g] (exact accumulation; the
+    FP8-instruction mode beside it).  Inputs are the fine-grained workload's
+    seeded bytes (workloads.py, seed 3).  Timed like the large
+    configuration's kernels."""
+    import workloads
+    w = workloads.get("fine")
+    M, K, N = w.M, w.K, w.N
     stream = torch.cuda.current_stream()
-    g = torch.Generator(device=dev)
-    g.manual_seed(30303)
-    z = torch.randn((M, K), generator=g, device=dev)
-    chi2 = torch.zeros_like(z)
-    for _ in range(3):
-        chi2 += torch.randn((M, K), generator=g, device=dev) ** 2
-    H = (z / torch.sqrt(chi2 / 3.0)).to(torch.bfloat16)
-    del z, chi2
+    H = _upload_bf16(torch, w.h0(), dev)
     A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
     GS = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
-    W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    W = _upload_bf16(torch, w.weight(), dev)
     W8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
     ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
     sq.quantize_weight(W, sq.E4M3, sq.PER_GROUP128, W8, ws)
@@ -828,17 +895,25 @@ def fine_grained(sq, torch, dev, args):
     q = burst_median(torch, stream, lambda: sq.quantize_fused(
         H, sq.ACT_IDENTITY, sq.E4M3, sq.PER_GROUP128, None, None, A8, GS), 16)
     gm = burst_median(torch, stream, lambda: sq.fp8_gemm_scaled(
-        A8, sq.E4M3, W8, sq.E4M3, sq.PER_GROUP128, GS, ws, Y), 4)
+        A8, sq.E4M3, W8, sq.E4M3, sq.PER_GROUP128, GS, ws, Y, sq.ACCUM_EXACT), 4)
+    g8 = burst_median(torch, stream, lambda: sq.fp8_gemm_scaled(
+        A8, sq.E4M3, W8, sq.E4M3, sq.PER_GROUP128, GS, ws, Y, sq.ACCUM_MFMA_FP8), 4)
     qb, fl = M * K * 3 + M * (K // 128) * 4, 2 * M * N * K
+    tf = lambda ms: fl / (ms * 1e-3) / 1e12
     out = {"shape": f"H[{M}x{K}] student-t -> e4m3 + per-128 group scales; "
                     f"Y[{M}x{N}] = A8 x W8[{N}x{K}]^T with 128 x 128 weight blocks",
+           "data": "workloads.py fine (seed 3): the parity tests' bytes",
            "quantize_fused_per_group": {
                "ms": round(q, 4), "GB/s": round(qb / (q * 1e-3) / 1e9, 1),
                "bytes_per_launch": qb,
                "frac_of_hbm_peak": round(qb / (q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
            "fp8_gemm_scaled_per_group": {
-               "ms": round(gm, 4), "TFLOP/s": round(fl / (gm * 1e-3) / 1e12, 1),
-               "frac_of_fp8_peak": round(fl / (gm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}}
+               "ms": round(gm, 4), "TFLOP/s": round(tf(gm), 1), "accum": "exact",
+               "frac_of_fp16_mfma_peak": round(tf(gm) / FP16_PEAK_TFLOPS, 4),
+               "frac_of_fp8_peak": round(tf(gm) / FP8_PEAK_TFLOPS, 4)},
+           "fp8_gemm_scaled_per_group_mfma_fp8": {
+               "ms": round(g8, 4), "TFLOP/s": round(tf(g8), 1),
+               "frac_of_fp8_peak": round(tf(g8) / FP8_PEAK_TFLOPS, 4)}}
     del H, A8, GS, W, W8, Y
     torch.cuda.empty_cache()
     return out
@@ -910,28 +985,141 @@ def measured_traffic(name, source):
         return None
 
 
-def cpu_baseline(w):
-    """The oracle, untuned and single-threaded, on a bounded sample of the workload."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_rows(O, a8, fa, b8, fb, mode, sa, sb, rows):
+    """oracle.gemm_f64 over row chunks on several host threads (the oracle
+    call releases the interpreter lock); the same values as one call."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = np.array_split(np.asarray(rows, np.int64), min(16, len(rows)))
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(lambda rr: O.gemm_f64(a8, fa, b8, fb, mode, sa, sb, rows=rr), chunks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def _outside_bound(sq, torch, dev, a8, b8, mode, sa_inv, sb_inv, ref, absref):
+    """Fraction of outputs outside |y - ref| <= 2^-8 |ref| + 1e-5 sum|ab| for
+    each accumulation mode, the GEMM run on the GPU over the given rows of A
+    (a multiple of 256, so the large-tile kernels the workloads use run them)."""
+    import numpy as np
+    M, K = a8.shape
+    N = b8.shape[0]
+    a = torch.from_numpy(np.ascontiguousarray(a8)).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(b8)).to(dev)
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(np.atleast_1d(
+        np.asarray(x, np.float32)))).to(dev)
+    res = {}
+    for name, accum in (("exact", sq.ACCUM_EXACT), ("mfma_fp8", sq.ACCUM_MFMA_FP8)):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sq.fp8_gemm_scaled(a, 0, b, 0, mode, f32(sa_inv), f32(sb_inv), y, accum)
+        yv = y.float().cpu().numpy().astype(np.float64)
+        bad = np.abs(yv - ref) > (2.0 ** -8) * np.abs(ref) + 1e-5 * absref
+        res[name] = (int(bad.sum()), int(bad.size))
+    return res
+
+
+def cpu_baseline(w, sq, torch, dev):
+    """The oracle, untuned and single-threaded, timed on a bounded sample of
+    the step's own bytes (the first step's input H_0, all rows, at the scale
+    the first timed step uses; the GEMM over 512 of its rows).  Then, with the
+    oracle as reference (not timed), the fraction of outputs each GEMM
+    accumulation mode puts outside the bound on each workload's data: tiny
+    (all four steps, every output), GPT-2 (512 rows of the steady second
+    step), large (256 rows; per-tensor scale from those rows' amax) and
+    fine-grained (256 rows, per-128 groups: the same codes as the full
+    tensor's rows).  Returns (baseline, fractions)."""
     import numpy as np
     import oracle as O
+    import workloads
 
-    rows = 16384
-    h = w.h_step(0)[:rows] if w.name == "tiny" else w.h0(0, rows)
+    h = w.h_step(0)
+    ost = O.State(O.E4M3, w.hist_len, w.margin, w.initial_amax)
+    s0 = ost.scale
     t0 = time.perf_counter()
-    r = O.quantize(h, O.ACT_RELU2, O.E4M3, O.PER_TENSOR, 358.4)
+    r = O.quantize(h, O.ACT_RELU2, O.E4M3, O.PER_TENSOR, s0)
     tq = time.perf_counter() - t0
     elems = h.size
     q_gbs = elems * w.quant_bytes_per_elem() / tq / 1e9
     grows = 512
-    wq, s_w, _ = O.quantize_weight_tensor(w.weight(), O.E4M3)
+    wq, s_w, si_w = O.quantize_weight_tensor(w.weight(), O.E4M3)
     t0 = time.perf_counter()
-    O.gemm_f64(r.fp8, O.E4M3, wq, O.E4M3, O.PER_TENSOR, 358.4, s_w, rows=list(range(grows)))
+    O.gemm_f64(r.fp8, O.E4M3, wq, O.E4M3, O.PER_TENSOR, s0, s_w, rows=list(range(grows)))
     tg = time.perf_counter() - t0
     g_gflops = 2.0 * grows * w.N * w.K / tg / 1e9
-    return {"value": round(q_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle_quantize over {rows} x {w.K} rows of H (relu2, e4m3) in {tq:.2f} s; "
-                      f"oracle_gemm_f64 over {grows} rows x {w.N} cols x K={w.K} in {tg:.2f} s",
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    base = {"value": round(q_gbs, 4), "unit": "GB/s", "cores": 1, "threads": 1,
+            "host_cores": os.cpu_count(), "host_cores_available": affinity,
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"oracle_quantize over the step's first input H_0 [{h.shape[0]} x {w.K}] "
+                      f"(relu2, e4m3, scale {s0}) in {tq:.2f} s on 1 thread; oracle_gemm_f64 "
+                      f"over {grows} of its rows x {w.N} cols x K={w.K} in {tg:.2f} s",
             "gemm_GFLOPs": round(g_gflops, 3)}
+
+    frac = {}
+
+    def record(name, counts):
+        frac[name] = {m: {"outside": c[0], "of": c[1], "fraction": round(c[0] / c[1], 6)}
+                      for m, c in counts.items()}
+
+    # tiny: every output of all four delayed steps
+    tw = workloads.get("tiny")
+    twq, ts_w, tsi_w = O.quantize_weight_tensor(tw.weight(), O.E4M3)
+    tst = O.State(O.E4M3, tw.hist_len, tw.margin, tw.initial_amax)
+    tot = {}
+    for t in range(tw.steps):
+        tr = O.quantize(tw.h_step(t), O.ACT_RELU2, O.E4M3, O.PER_TENSOR, tst.scale,
+                        want_bf16=False)
+        ref, absref = O.gemm_f64(tr.fp8, O.E4M3, twq, O.E4M3, O.PER_TENSOR, tst.scale, ts_w)
+        c = _outside_bound(sq, torch, dev, tr.fp8, twq, sq.PER_TENSOR,
+                           np.float32(1.0) / np.float32(tst.scale), tsi_w, ref, absref)
+        for k, v in c.items():
+            tot[k] = (tot.get(k, (0, 0))[0] + v[0], tot.get(k, (0, 0))[1] + v[1])
+        tst.accumulate(tr.amax_bits, tr.sat)
+        tst.update()
+    record("tiny", tot)
+    # GPT-2: 512 rows of the second step, cast with the delayed scale from step 0
+    ost.accumulate(r.amax_bits, r.sat)
+    ost.update()
+    rows = np.arange(512)
+    r1 = O.quantize(w.h_step(1)[rows], O.ACT_RELU2, O.E4M3, O.PER_TENSOR, ost.scale,
+                    want_bf16=False)
+    ref, absref = _oracle_rows(O, r1.fp8, O.E4M3, wq, O.E4M3, O.PER_TENSOR, ost.scale, s_w, rows)
+    record("gpt2", _outside_bound(sq, torch, dev, r1.fp8, wq, sq.PER_TENSOR,
+                                  np.float32(1.0) / np.float32(ost.scale), si_w, ref, absref))
+    # large: 256 rows; the scale from those rows' amax with the workload's margin
+    lw = workloads.get("large")
+    lh = lw.h0(0, 256)
+    la = O.quantize(lh, O.ACT_RELU2, O.E4M3, O.PER_TENSOR, 1.0, want_bf16=False,
+                    want_fp8=False)
+    ls = float(O.scale_from_amax(la.amax, lw.margin, O.E4M3)[0][0])
+    lr = O.quantize(lh, O.ACT_RELU2, O.E4M3, O.PER_TENSOR, ls, want_bf16=False)
+    lwq, ls_w, lsi_w = O.quantize_weight_tensor(lw.weight(), O.E4M3)
+    rows = np.arange(256)
+    ref, absref = _oracle_rows(O, lr.fp8, O.E4M3, lwq, O.E4M3, O.PER_TENSOR, ls, ls_w, rows)
+    record("large", _outside_bound(sq, torch, dev, lr.fp8, lwq, sq.PER_TENSOR,
+                                   np.float32(1.0) / np.float32(ls), lsi_w, ref, absref))
+    # fine-grained: 256 rows, per-128 groups and 128 x 128 weight blocks
+    fw = workloads.get("fine")
+    fr = O.quantize(fw.h0(0, 256), O.ACT_IDENTITY, O.E4M3, O.PER_GROUP128, want_bf16=False)
+    fwq, fsi_w, fs_w = O.quantize_weight_blocks(fw.weight(), O.E4M3, with_scale=True)
+    ref, absref = _oracle_rows(O, fr.fp8, O.E4M3, fwq, O.E4M3, O.PER_GROUP128, fr.group_scale,
+                               fs_w, rows)
+    record("fine_per_group", _outside_bound(sq, torch, dev, fr.fp8, fwq, sq.PER_GROUP128,
+                                            fr.group_scale_inv, fsi_w, ref, absref))
+    return base, frac
 
 
 if __name__ == "__main__":

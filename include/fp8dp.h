@@ -85,7 +85,7 @@ typedef enum { FP8DP_ACCUM_MFMA_FP8 = 0, FP8DP_ACCUM_EXACT = 1 } fp8dp_accum;
    one atomic add per thread block; amax_history_update reduces the slots. */
 typedef struct fp8dp_acc_slot {
   uint32_t amax;      /* binary32 bits of the running max |b| (unsigned compare) */
-  uint32_t reserved0;
+  uint32_t ticket;    /* quantize_fused_update: workgroups folded into this slot so far */
   uint64_t sat;       /* running count of saturating elements */
   uint8_t reserved[48];
 } fp8dp_acc_slot;
@@ -107,7 +107,8 @@ typedef struct fp8dp_tensor_state {
   uint32_t steps;         /* steps consumed so far                                */
   int32_t fmt;            /* fp8dp_format the state was initialised for           */
   float history[FP8DP_MAX_HIST];
-  uint8_t reserved[80];   /* pads the header to 192 bytes: acc starts on a 64-byte line */
+  uint32_t ticket;        /* quantize_fused_update: slots whose workgroups have all folded */
+  uint8_t reserved[76];   /* pads the header to 192 bytes: acc starts on a 64-byte line */
   fp8dp_acc_slot acc[FP8DP_ACC_SLOTS];   /* running accumulators of the current step */
 } fp8dp_tensor_state;
 
@@ -159,6 +160,22 @@ int quantize_fused(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
  *   overflow = sat_last > 0; amax_last = amax_t; slots cleared; steps += 1.
  * Errors: EINVAL for a NULL or misaligned st. */
 int amax_history_update(fp8dp_tensor_state* st, hipStream_t stream);
+
+/* quantize_fused in PER_TENSOR mode followed by amax_history_update, in one
+ * launch: the workgroup that folds its (amax, count) last -- counted with one
+ * atomic per workgroup on the slot's ticket and one per slot on st->ticket --
+ * closes the step ("Paradigma ...": the scale for the next step comes from
+ * this step's amax; delayed scaling removes the wait for it).  Outputs and
+ * the state after the call are bit for bit those of the two calls in
+ * sequence; a GEMM on this step's codes then takes &st->scale_inv_used (the
+ * inverse of the scale the codes were cast with).  The call ends the step:
+ * amax and counts folded by earlier quantize_fused calls of the same step are
+ * included.  Tickets are left at zero for the next call; calls that overlap
+ * on one state race.
+ * Errors: as quantize_fused in PER_TENSOR mode (st is required). */
+int quantize_fused_update(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                          fp8dp_format fmt, fp8dp_tensor_state* st, uint16_t* bf16_out,
+                          uint8_t* fp8_out, hipStream_t stream);
 
 /* Scaled FP8 x FP8 GEMM with FP32 accumulation and BF16 output ("FP8
  * training ...", Step 3; "FP8 Training & Inference", Per-Tensor Scaling):
@@ -318,14 +335,23 @@ int quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act, fp
  * of quantize_mx on each operand), y [M x N] BF16:
  *   y = bf16_rne( sum_j 2^(a_scale[m, j] - 127) 2^(b_scale[n, j] - 127)
  *                       sum_{k in block j} dec(a[m, k]) dec(b[n, k]) )
- * with FP32 accumulation; the block scales are applied by the matrix
- * instructions themselves (gfx950 microscaled MFMA), one per 32-value block.
+ * with FP32 accumulation, one scale pair per 32-value block.
+ * accum = ACCUM_EXACT: each row's block exponents are folded into the FP16
+ *   widening of its codes, relative to the row's largest exponent (exact while
+ *   a tile's rows span at most 22 binades, E4M3, or 8, E5M2, which a scan of
+ *   the tile's exponents checks); a tile past that takes a fallback that sums
+ *   each block on its own and adds it scaled by its two exponents (exact for
+ *   any exponents, slower).  FP16 products, FP32 sums: |err| <= 2^-8 |ref| +
+ *   1e-5 sum|ab| on every output.
+ * accum = ACCUM_MFMA_FP8: the block scales are applied by gfx950's microscaled
+ *   FP8 matrix instructions, which truncate small products as the unscaled
+ *   ones do (see fp8dp_accum).
  * Errors: EINVAL for NULL pointers, M not a positive multiple of 256, N or K
  * not of 128, a, b or y not 16-byte aligned, exponent arrays not 4-byte
- * aligned, or a bad format. */
+ * aligned, or a bad format or accum. */
 int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale, const uint8_t* b,
                 fp8dp_format fb, const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
-                uint16_t* y, hipStream_t stream);
+                fp8dp_accum accum, uint16_t* y, hipStream_t stream);
 
 /* Weight cast with current scaling ("FP8 training ...", Step 4: the 8-bit
  * copies are cast from the master weights at every step; Trade-offs: 128 x

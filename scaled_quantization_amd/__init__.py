@@ -7,7 +7,8 @@ and the current HIP stream, and turns nonzero return codes into exceptions.
 It raises if the library has not been built; there is no CPU fallback.
 
 Entry points (same names as the C ABI):
-    fp8dp_state_init, quantize_fused, amax_history_update, fp8_gemm_scaled,
+    fp8dp_state_init, quantize_fused, amax_history_update, quantize_fused_update,
+    fp8_gemm_scaled,
     quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
     fp8_transpose, and the comparison / diagnostic calls fp8dp_bench_*,
     fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit, fp8dp_set_codec.
@@ -43,6 +44,7 @@ _SIGS = {
     "fp8dp_state_init": ([_vp, _i32, _i32, _f32, _f32, _vp], ctypes.c_int),
     "quantize_fused": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "amax_history_update": ([_vp, _vp], ctypes.c_int),
+    "quantize_fused_update": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_scaled": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                          _vp], ctypes.c_int),
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
@@ -57,7 +59,8 @@ _SIGS = {
     "fp8_gemm_scaled_if": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
                             _vp], ctypes.c_int),
     "quantize_mx": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
-    "fp8_gemm_mx": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_mx": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp],
+                    ctypes.c_int),
     "gemm_bf16_quantize_fused": ([_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                   _vp], ctypes.c_int),
     "fp8dp_last_error": ([], ctypes.c_char_p),
@@ -128,7 +131,8 @@ def _p(t: Ptr) -> Optional[int]:
 # Field offsets of fp8dp_tensor_state (include/fp8dp.h).
 _HDR = struct.Struct("<fffIQffiiIi16f")          # 112 bytes of header fields
 _SLOT = struct.Struct("<IIQ48x")                 # 64-byte accumulator slot
-_OFF = {"scale": 0, "scale_inv": 4, "scale_inv_used": 8, "overflow": 12, "acc": 192}
+_OFF = {"scale": 0, "scale_inv": 4, "scale_inv_used": 8, "overflow": 12, "ticket": 112,
+        "acc": 192}
 
 
 class TensorState:
@@ -154,13 +158,16 @@ class TensorState:
         d = dict(scale=f[0], scale_inv=f[1], scale_inv_used=f[2], overflow=f[3], sat_last=f[4],
                  amax_last=f[5], margin=f[6], hist_len=f[7], hist_pos=f[8], steps=f[9],
                  fmt=f[10], history=list(f[11:11 + MAX_HIST]))
-        amax_acc, sat_acc = 0, 0
+        amax_acc, sat_acc, tickets = 0, 0, 0
         for i in range(ACC_SLOTS):
-            a, _, s = _SLOT.unpack_from(raw, _OFF["acc"] + 64 * i)
+            a, t, s = _SLOT.unpack_from(raw, _OFF["acc"] + 64 * i)
             amax_acc = max(amax_acc, a)
             sat_acc += s
+            tickets += t
         d["amax_acc"] = amax_acc
         d["sat_acc"] = sat_acc
+        d["ticket"] = struct.unpack_from("<I", raw, _OFF["ticket"])[0]
+        d["slot_tickets"] = tickets
         return d
 
     def raw(self) -> bytes:
@@ -235,6 +242,19 @@ def quantize_fused(h: torch.Tensor, act: int, fmt: int, mode: int, st=None,
 
 def amax_history_update(st, stream=None) -> None:
     _check(lib().amax_history_update(_state_ptr(st), _stream(stream)), "amax_history_update")
+
+
+def quantize_fused_update(h: torch.Tensor, act: int, fmt: int, st, bf16_out: Ptr = None,
+                          fp8_out: Ptr = None, stream=None) -> None:
+    """quantize_fused (PER_TENSOR) followed by amax_history_update, in one launch."""
+    _elem(h, (2,), "quantize_fused_update: h")
+    _elem(bf16_out, (2,), "quantize_fused_update: bf16_out")
+    _codes(fp8_out, "quantize_fused_update: fp8_out")
+    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    _room(bf16_out, rows * cols * 2, "quantize_fused_update: bf16_out")
+    _room(fp8_out, rows * cols, "quantize_fused_update: fp8_out")
+    _check(lib().quantize_fused_update(_p(h), rows, cols, act, fmt, _state_ptr(st), _p(bf16_out),
+                                       _p(fp8_out), _stream(stream)), "quantize_fused_update")
 
 
 def fp8_gemm_scaled(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, mode: int,
@@ -338,16 +358,16 @@ def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,
 
 
 def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor, fb: int,
-                b_scale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+                b_scale: torch.Tensor, y: torch.Tensor, accum: int = ACCUM_EXACT,
+                stream=None) -> None:
     """MXFP8 GEMM y [M, N] = a [M, K] b [N, K]^T with E8M0 block exponents
-    a_scale [M, K/32] and b_scale [N, K/32]."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or tuple(y.shape) != (M, N) or a_scale.numel() * 32 != M * K or \
-            b_scale.numel() * 32 != N * K:
-        raise Fp8dpError("fp8_gemm_mx: shape mismatch")
-    _check(lib().fp8_gemm_mx(_p(a), fa, _p(a_scale), _p(b), fb, _p(b_scale), M, N, K, _p(y),
-                             _stream(stream)), "fp8_gemm_mx")
+    a_scale [M, K/32] and b_scale [N, K/32] (uint8); accum as for fp8_gemm_scaled."""
+    M, N, K = _gemm_operands("fp8_gemm_mx", a, b, y)
+    for name, e, rows in (("a_scale", a_scale, M), ("b_scale", b_scale, N)):
+        if e.element_size() != 1 or e.numel() * 32 != rows * K:
+            raise Fp8dpError(f"fp8_gemm_mx: {name} needs {rows * K // 32} uint8 exponents")
+    _check(lib().fp8_gemm_mx(_p(a), fa, _p(a_scale), _p(b), fb, _p(b_scale), M, N, K, accum,
+                             _p(y), _stream(stream)), "fp8_gemm_mx")
 
 
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,

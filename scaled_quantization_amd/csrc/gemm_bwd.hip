@@ -93,43 +93,62 @@ static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int6
 
 using namespace fp8dp;
 
-extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
-                                      fp8dp_format fb, int64_t M, int64_t N, int64_t K,
-                                      int32_t splits, fp8dp_accum accum, const float* a_scale_inv,
-                                      const float* b_scale_inv, float* workspace, uint16_t* y,
-                                      hipStream_t stream) {
-  if (a == nullptr || b == nullptr || y == nullptr || workspace == nullptr ||
-      a_scale_inv == nullptr || b_scale_inv == nullptr) {
-    set_error("fp8_gemm_scaled_splitk: NULL pointer argument");
+// Argument checks shared by fp8_gemm_scaled_splitk and its no-allocation form.
+static int check_splitk(const char* name, const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                        fp8dp_format fb, int64_t M, int64_t N, int64_t K, int32_t splits,
+                        fp8dp_accum accum, const float* a_scale_inv, const float* b_scale_inv,
+                        uint16_t* y) {
+  if (a == nullptr || b == nullptr || y == nullptr || a_scale_inv == nullptr ||
+      b_scale_inv == nullptr) {
+    set_error("%s: NULL pointer argument", name);
     return FP8DP_EINVAL;
   }
   if (splits < 1 || splits > 64) {
-    set_error("fp8_gemm_scaled_splitk: splits must be in 1..64 (got %d)", (int)splits);
+    set_error("%s: splits must be in 1..64 (got %d)", name, (int)splits);
     return FP8DP_EINVAL;
   }
   if (M < 256 || N < 128 || K < 128 * (int64_t)splits || M % 256 || N % 128 || K % 128) {
-    set_error("fp8_gemm_scaled_splitk: M must be a positive multiple of 256, N and K of 128, "
-              "K at least 128 * splits (got %lld, %lld, %lld, splits %d)", (long long)M,
+    set_error("%s: M must be a positive multiple of 256, N and K of 128, "
+              "K at least 128 * splits (got %lld, %lld, %lld, splits %d)", name, (long long)M,
               (long long)N, (long long)K, (int)splits);
     return FP8DP_EINVAL;
   }
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30 ||
       (M / 256) * (N / 128) * splits > (int64_t)0x7FFFFFFF) {
-    set_error("fp8_gemm_scaled_splitk: shape too large");
+    set_error("%s: shape too large", name);
     return FP8DP_EINVAL;
   }
   if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
       (accum != FP8DP_ACCUM_MFMA_FP8 && accum != FP8DP_ACCUM_EXACT)) {
-    set_error("fp8_gemm_scaled_splitk: unknown format or accumulation mode");
+    set_error("%s: unknown format or accumulation mode", name);
     return FP8DP_EINVAL;
   }
-  if (!aligned16(a) || !aligned16(b) || !aligned16(y) || !aligned16(workspace) ||
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
       (reinterpret_cast<uintptr_t>(a_scale_inv) & 3u) ||
       (reinterpret_cast<uintptr_t>(b_scale_inv) & 3u)) {
+    set_error("%s: operands and workspace must be 16-byte aligned, scales 4-byte aligned", name);
+    return FP8DP_EINVAL;
+  }
+  return FP8DP_OK;
+}
+
+extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                                      fp8dp_format fb, int64_t M, int64_t N, int64_t K,
+                                      int32_t splits, fp8dp_accum accum, const float* a_scale_inv,
+                                      const float* b_scale_inv, float* workspace, uint16_t* y,
+                                      hipStream_t stream) {
+  if (workspace == nullptr) {
+    set_error("fp8_gemm_scaled_splitk: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(workspace)) {
     set_error("fp8_gemm_scaled_splitk: operands and workspace must be 16-byte aligned, scales "
               "4-byte aligned");
     return FP8DP_EINVAL;
   }
+  const int rc = check_splitk("fp8_gemm_scaled_splitk", a, fa, b, fb, M, N, K, splits, accum,
+                              a_scale_inv, b_scale_inv, y);
+  if (rc != FP8DP_OK) return rc;
   return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
     return launch_split_tile<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
         a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);

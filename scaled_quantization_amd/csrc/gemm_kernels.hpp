@@ -88,6 +88,38 @@ __device__ __forceinline__ v8h_t widen8(const v8i_t& x) {
   }
 }
 
+// The same 8 codes times a power of two `scale` (2^-22 .. 2^7), widened with
+// the hardware convert: exact whenever the scaled values are FP16 values,
+// which the microscaled exact GEMM checks before it uses this.
+template <int F, int Q>
+__device__ __forceinline__ v8h_t widen8s(const v8i_t& x, float scale) {
+  const uint32_t d0 = (uint32_t)x[2 * Q], d1 = (uint32_t)x[2 * Q + 1];
+  v2h_t p0, p1, p2, p3;
+  if constexpr (F == 1) {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(d0, scale, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(d0, scale, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(d1, scale, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(d1, scale, true);
+  } else {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, scale, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, scale, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, scale, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, scale, true);
+  }
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6,
+                                 7);
+}
+
+// Microscaled exact accumulation: each operand row's block exponents are
+// folded into its FP16 widening relative to the row's largest one, value *
+// 2^(e_block - e_rowmax + kMxFoldBias).  The largest block then reaches
+// 448 * 2^7 = 57344 (E4M3) or 57344 (E5M2), below FP16's 65504, and a block
+// stays exact down to e_rowmax - kMxSpan: the smallest subnormal code (2^-9
+// E4M3, 2^-16 E5M2) lands on FP16's grid (2^-24).
+template <int F> constexpr int kMxFoldBias = F == 0 ? 7 : 0;
+template <int F> constexpr int kMxSpan = F == 0 ? 22 : 8;
+
 constexpr int kBM = 128, kBN = 128;
 constexpr int kGemmThreads = 256;
 
@@ -361,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
                                                      Relu2Bwd bwd = {}) {
   static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
   static_assert(BC < 0 || !(MX || SPLIT), "the backward epilogue follows the per-tensor GEMM");
-  static_assert(!(EX && MX), "exact accumulation of microscaled operands is not provided here");
+  static_assert(!(EX && MX) || TN == 2, "exact microscaled accumulation: 256 x 128 tiles");
   if constexpr (COND) {
     if (*run_flag == 0) return;
   }
@@ -384,7 +416,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   constexpr int XSZ = XR ? 8192 : 0;                        // 512 rows x 16 bytes (4 stages)
   constexpr int LA = BM / 64, LB = BN / 64;                 // tile copies per wave per stage
   constexpr int NCOPY = LA + LB + (MX && !XR ? 1 : 0);      // copies of a stage with no exponents
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT + 2 * XSZ];
+  constexpr int RSZ = MX && EX ? 512 : 0;                    // rows' largest block exponents
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT + 2 * XSZ + RSZ];
 
   const int tiles_n = N / BN;
   const int ntiles = (M / BM) * tiles_n;
@@ -645,6 +678,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     }
   };
 
+  // MX && EX: each operand row's largest block exponent, from a scan of the
+  // tile's exponent rows (thread t < 256: A row m0 + t; 256 + c: B row n0 + c)
+  // into LDS; the tile folds exactly when every row's exponents span at most
+  // kMxSpan binades, else it takes the unfolded fallback below.
+  uint8_t* const sR = lds + 2 * SLOT + 2 * XSZ;
+  int ref_a[MX && EX ? TM : 1] = {}, ref_b[MX && EX ? TN : 1] = {};
+  bool mx_slow = false;
+  if constexpr (MX && EX) {
+    const int t = threadIdx.x, KB = K / 32;
+    const uint8_t* e = t < 256 ? ea + (size_t)(m0 + t) * KB
+                               : (t - 256 < BN ? eb + (size_t)(n0 + t - 256) * KB : nullptr);
+    uint32_t emax = 0, emin = 255;
+    if (e != nullptr) {
+      for (int k = 0; k < KB; k += 4) {
+        const uint32_t d = *reinterpret_cast<const uint32_t*>(e + k);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t v = (d >> (8 * b)) & 0xFFu;
+          emax = v > emax ? v : emax;
+          emin = v < emin ? v : emin;
+        }
+      }
+      sR[t] = (uint8_t)emax;
+    }
+    const int span = t < 256 ? kMxSpan<FA> : kMxSpan<FB>;
+    mx_slow = __syncthreads_or(e != nullptr && (int)(emax - emin) > span) != 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ref_a[i] = sR[wr + 32 * i + frow];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) ref_b[j] = sR[256 + wc + 32 * j + frow];
+  }
+
   // BC >= 0: the tile's cached codes [256 x BN], row-major, copied with the
   // 16-byte global->LDS copies into the ring slot stage KT would have used
   // (free once iteration KT-2's barrier has shown every wave done with stage
@@ -670,17 +735,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   // swapping one value with the neighbour lane (DPP quad_perm 1,0,3,2) gives
   // the even lane columns (c, c+1) of row r and the odd lane the same columns
   // of row r+1.
-  auto epi_plain = [&](int tm0, int tn0) {
+  // MX && EX: folded sums are scaled back by 2^(rowmax_a + rowmax_b - 254 -
+  // fold biases) per element (exact, ldexp); unfolded ones (the tile's exact
+  // fallback) carry their block scales already
+  auto epi_plain = [&](int tm0, int tn0, bool folded = true) {
     const float f = MX ? 1.0f : sa[0] * sb[0];
     const bool odd = lane & 1;
     const int colp = (lane & 31) & ~1;
+    auto val = [&](int i, int j, int r) -> float {
+      if constexpr (MX && EX) {
+        if (!folded) return acc[i][j][r];
+        const int row = wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        return __builtin_ldexpf(acc[i][j][r], (int)sR[row] + ref_b[j] - 254 - kMxFoldBias<FA> -
+                                                  kMxFoldBias<FB>);
+      } else {
+        return acc[i][j][r] * f;
+      }
+    };
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float v0 = acc[i][j][r] * f, v1 = acc[i][j][r + 1] * f;
+          const float v0 = val(i, j, r), v1 = val(i, j, r + 1);
           const float give = odd ? v0 : v1;
           const float got = __builtin_bit_cast(
               float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF,
@@ -692,6 +770,63 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
           *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = packed;
         }
   };
+
+  if constexpr (MX && EX) {
+    if (mx_slow) {
+      // Unfolded fallback, exact for any exponents: each wave sums every
+      // 32-wide block in FP32 on its own (two FP16 instructions on the
+      // widened codes, read straight from memory) and adds it to the
+      // accumulator scaled by 2^(e_a + e_b - 254) -- the promotion per block
+      // of the per-group path with microscaling's block size.
+      const int KB = K / 32;
+      for (int blk = 0; blk < KB; ++blk) {
+        v16f_t part[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const size_t k0 = (size_t)blk * 32 + 16 * sl + 8 * fhalf;
+          v8h_t ha[TM], hb[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const uint2 u = *reinterpret_cast<const uint2*>(A + (size_t)(m0 + wr + 32 * i + frow) * K + k0);
+            const v8i_t x = {(int)u.x, (int)u.y, 0, 0, 0, 0, 0, 0};
+            ha[i] = widen8<FA, 0>(x);
+          }
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const uint2 u = *reinterpret_cast<const uint2*>(B + (size_t)(n0 + wc + 32 * j + frow) * K + k0);
+            const v8i_t x = {(int)u.x, (int)u.y, 0, 0, 0, 0, 0, 0};
+            hb[j] = widen8<FB, 0>(x);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb[j], part[i][j], 0, 0, 0);
+        }
+        int e_b[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) e_b[j] = eb[(size_t)(n0 + wc + 32 * j + frow) * KB + blk];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wr + 32 * i + (r >> 2) * 8 + fhalf * 4 + (r & 3);
+            const int e_a = ea[(size_t)row * KB + blk];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j][r] += __builtin_ldexpf(part[i][j][r], e_a + e_b[j] - 254);
+          }
+      }
+      epi_plain(m0, n0, false);
+      return;
+    }
+  }
 
   // prologue: stages 0 and 1 in flight, stage 0 landed and published
   issue(0);
@@ -828,22 +963,43 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     // in flight still reads.
     constexpr bool EXP = EX && !PG;
     v8h_t wa[EXP ? TM : 1], wb[EXP ? TN : 1];
-    auto widen_slice = [&](const v8i_t* fa, const v8i_t* fb, auto Q, v8h_t* oa, v8h_t* ob) {
+    // MX: slice q of substep h holds block 2 h + q / 2 of the stage (the
+    // lane's bytes 0-15 are the first block's, 16-31 the second's); its codes
+    // are widened times 2^(e_block - e_rowmax + kMxFoldBias), e_block from
+    // the row's stage dword
+    auto widen_slice = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa,
+                           const uint32_t* xb, int h, auto Q, v8h_t* oa, v8h_t* ob) {
       constexpr int q = decltype(Q)::value;
+      if constexpr (MX) {
+        const int sh = 8 * (2 * h + q / 2);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) oa[i] = widen8<FA, q>(fa[i]);
+        for (int i = 0; i < TM; ++i) {
+          const int e = (int)((xa[i] >> sh) & 0xFFu) - ref_a[i] + kMxFoldBias<FA> + 127;
+          oa[i] = widen8s<FA, q>(fa[i], __uint_as_float((uint32_t)e << 23));
+        }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) ob[j] = widen8<FB, q>(fb[j]);
+        for (int j = 0; j < TN; ++j) {
+          const int e = (int)((xb[j] >> sh) & 0xFFu) - ref_b[j] + kMxFoldBias<FB> + 127;
+          ob[j] = widen8s<FB, q>(fb[j], __uint_as_float((uint32_t)e << 23));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) oa[i] = widen8<FA, q>(fa[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) ob[j] = widen8<FB, q>(fb[j]);
+      }
     };
-    auto mfmas_ex = [&](const v8i_t* fa, const v8i_t* fb, const v8i_t* nfa, const v8i_t* nfb) {
+    auto mfmas_ex = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa, const uint32_t* xb,
+                        int h, const v8i_t* nfa, const v8i_t* nfb, const uint32_t* nxa,
+                        const uint32_t* nxb, int nh) {
       if constexpr (EXP) {
         static_for<4>([&](auto Q) {
           constexpr int q = decltype(Q)::value;
           v8h_t na[TM], nb[TN];
           if constexpr (q < 3)
-            widen_slice(fa, fb, std::integral_constant<int, q + 1>{}, na, nb);
+            widen_slice(fa, fb, xa, xb, h, std::integral_constant<int, q + 1>{}, na, nb);
           else
-            widen_slice(nfa, nfb, std::integral_constant<int, 0>{}, na, nb);
+            widen_slice(nfa, nfb, nxa, nxb, nh, std::integral_constant<int, 0>{}, na, nb);
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -873,7 +1029,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       }
     };
     load_frags(0, 0, fa0, fb0, xa0, xb0);
-    if constexpr (EXP) widen_slice(fa0, fb0, std::integral_constant<int, 0>{}, wa, wb);
+    if constexpr (EXP) widen_slice(fa0, fb0, xa0, xb0, 0, std::integral_constant<int, 0>{}, wa, wb);
     for (int kt = 0; kt < GS; ++kt) {
       if constexpr (PG) {
         // the reads of substep 0 were issued a half stage ago: wait for them
@@ -883,7 +1039,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       }
       // first half: read substep 1 of stage kt, multiply substep 0
       load_frags(kt, 1, fa1, fb1, xa1, xb1);
-      if constexpr (EXP) mfmas_ex(fa0, fb0, fa1, fb1);
+      if constexpr (EXP) mfmas_ex(fa0, fb0, xa0, xb0, 0, fa1, fb1, xa1, xb1, 1);
       else mfmas(fa0, fb0, xa0, xb0, 0);
       if constexpr (MX || PG) {
         // keep these products in the first half: without a use here the
@@ -906,7 +1062,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
         if (kt + 2 == KT) issue_cache(cache_lds);
       }
       if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
-      if constexpr (EXP) mfmas_ex(fa1, fb1, fa0, fb0);
+      if constexpr (EXP) mfmas_ex(fa1, fb1, xa1, xb1, 1, fa0, fb0, xa0, xb0, 0);
       else mfmas(fa1, fb1, xa1, xb1, 1);
       if constexpr (PER) {
         if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum

@@ -6,27 +6,31 @@
 
 namespace fp8dp {
 
-template <int FA, int FB, int TN>
+template <int FA, int FB, int TN, bool EX>
 static int launch_mx(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const dim3 grid((unsigned)((M / 256) * (N / (64 * TN))));
   if (K % 512 == 0 && aligned16(ea) && aligned16(eb))
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true, false, -1, 1, 4>), grid, dim3(512), 0,
-                       stream, a, b, (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea,
-                       eb);
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true, false, -1, 1, 4, false, false, EX>),
+                       grid, dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       y, nullptr, 1, ea, eb);
   else
-    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true>), grid, dim3(512), 0, stream, a, b,
-                       (int)M, (int)N, (int)K, nullptr, nullptr, y, nullptr, 1, ea, eb);
+    hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, false, true, false, -1, 1, 1, false, false, EX>),
+                       grid, dim3(512), 0, stream, a, b, (int)M, (int)N, (int)K, nullptr, nullptr,
+                       y, nullptr, 1, ea, eb);
   return check_launch("fp8_gemm_mx");
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool EX>
 static int launch_mx_tile(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
                           const uint8_t* eb, int64_t M, int64_t N, int64_t K, uint16_t* y,
                           hipStream_t stream) {
-  // no 256-wide tile here: with the exponent registers it would spill
-  if (N % 192 == 0) return launch_mx<FA, FB, 3>(a, ea, b, eb, M, N, K, y, stream);
-  return launch_mx<FA, FB, 2>(a, ea, b, eb, M, N, K, y, stream);
+  // no 256-wide tile here: with the exponent registers it would spill; exact
+  // accumulation takes 256 x 128 (its fold references and fallback)
+  if constexpr (!EX) {
+    if (N % 192 == 0) return launch_mx<FA, FB, 3, EX>(a, ea, b, eb, M, N, K, y, stream);
+  }
+  return launch_mx<FA, FB, 2, EX>(a, ea, b, eb, M, N, K, y, stream);
 }
 
 }  // namespace fp8dp
@@ -35,7 +39,8 @@ using namespace fp8dp;
 
 extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale,
                            const uint8_t* b, fp8dp_format fb, const uint8_t* b_scale, int64_t M,
-                           int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+                           int64_t N, int64_t K, fp8dp_accum accum, uint16_t* y,
+                           hipStream_t stream) {
   if (a == nullptr || b == nullptr || y == nullptr || a_scale == nullptr || b_scale == nullptr) {
     set_error("fp8_gemm_mx: NULL pointer argument");
     return FP8DP_EINVAL;
@@ -50,8 +55,9 @@ extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_s
     set_error("fp8_gemm_mx: shape too large");
     return FP8DP_EINVAL;
   }
-  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2)) {
-    set_error("fp8_gemm_mx: unknown format");
+  if ((fa != FP8DP_E4M3 && fa != FP8DP_E5M2) || (fb != FP8DP_E4M3 && fb != FP8DP_E5M2) ||
+      (accum != FP8DP_ACCUM_MFMA_FP8 && accum != FP8DP_ACCUM_EXACT)) {
+    set_error("fp8_gemm_mx: unknown format or accumulation mode");
     return FP8DP_EINVAL;
   }
   if (!aligned16(a) || !aligned16(b) || !aligned16(y) ||
@@ -59,11 +65,8 @@ extern "C" int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_s
     set_error("fp8_gemm_mx: operands must be 16-byte aligned, block exponents 4-byte aligned");
     return FP8DP_EINVAL;
   }
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E4M3)
-    return launch_mx_tile<0, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  if (fa == FP8DP_E4M3 && fb == FP8DP_E5M2)
-    return launch_mx_tile<0, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  if (fa == FP8DP_E5M2 && fb == FP8DP_E4M3)
-    return launch_mx_tile<1, 0>(a, a_scale, b, b_scale, M, N, K, y, stream);
-  return launch_mx_tile<1, 1>(a, a_scale, b, b_scale, M, N, K, y, stream);
+  return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
+    return launch_mx_tile<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
+        a, a_scale, b, b_scale, M, N, K, y, stream);
+  });
 }

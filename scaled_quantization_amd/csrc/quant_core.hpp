@@ -144,4 +144,112 @@ __device__ __forceinline__ void block_fold(uint32_t amax16, uint32_t sat, fp8dp_
   block_fold_in<NT>(amax16, sat, slots, sm);
 }
 
+// Closes a step of delayed scaling; run by one wave (lane l reduces
+// accumulator slot l and holds history entry l).  Every load is issued
+// before any use; the ring after this step's write -- entry pos replaced by
+// the step's amax -- is reduced in registers.  The slots are read with
+// device-scope atomic loads: in the fused form other workgroups of the same
+// launch wrote them moments before (with atomics, at the device's L2).
+__device__ __forceinline__ void state_update_wave(fp8dp_tensor_state* st) {
+  const int l = threadIdx.x & 63;
+  uint32_t m = __hip_atomic_load(&st->acc[l].amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t c = __hip_atomic_load(&st->acc[l].sat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float h = l < FP8DP_MAX_HIST ? st->history[l] : 0.0f;
+  const int len = st->hist_len;
+  const int pos = st->hist_pos;
+  const float margin = st->margin;
+  const int fmt = st->fmt;
+  const float sinv = st->scale_inv;
+  const uint32_t steps = st->steps;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t om = __shfl_xor(m, off);
+    m = om > m ? om : m;
+    const uint32_t clo = __shfl_xor((uint32_t)c, off);
+    const uint32_t chi = __shfl_xor((uint32_t)(c >> 32), off);
+    c += ((uint64_t)chi << 32) | clo;
+  }
+  const float amax_t = __uint_as_float(m);
+  uint32_t hm = l < len ? (__float_as_uint(l == pos ? amax_t : h) & 0x7FFFFFFFu) : 0u;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(hm, off);
+    hm = o > hm ? o : hm;
+  }
+  st->acc[l].amax = 0;
+  st->acc[l].sat = 0;
+  st->acc[l].ticket = 0;
+  if (l == 0) {
+    st->history[pos] = amax_t;
+    st->hist_pos = (pos + 1 == len) ? 0 : pos + 1;
+    st->scale_inv_used = sinv;
+    const float s = scale_rule(__uint_as_float(hm), margin, fmt == 0 ? 448.0f : 57344.0f);
+    st->scale = s;
+    st->scale_inv = recip_rn(s);
+    st->sat_last = c;
+    st->overflow = c > 0 ? 1u : 0u;
+    st->amax_last = amax_t;
+    st->steps = steps + 1;
+    st->ticket = 0;
+  }
+}
+
+// The block reduction of block_fold_in, then the step's end in the workgroup
+// that folds last.  After the block reduction only wave 0 stays.  Thread 0
+// adds its workgroup's (amax, count) to its slot with atomics it waits for
+// (so they have been performed at the device's point of coherence), then
+// counts the workgroup on the slot's ticket; the workgroup that completes a
+// slot -- the slot takes workgroups b with b % 64 == j -- counts the slot on
+// st->ticket; the one that completes the last slot runs state_update_wave,
+// whose device-scope loads see every slot's final values.  Atomics only, no
+// fence: a device-scope release would write back this XCD's L2 in every
+// workgroup (measured 22x slower), and the accumulators are never written
+// any other way.  No workgroup waits for another.  sm: 2 NT / 64 words of LDS.
+template <int NT>
+__device__ __forceinline__ void block_fold_update(uint32_t amax16, uint32_t sat,
+                                                  fp8dp_tensor_state* st, uint32_t* sm) {
+  uint32_t* s_max = sm;
+  uint32_t* s_sat = sm + NT / 64;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t om = __shfl_xor(amax16, off);
+    amax16 = om > amax16 ? om : amax16;
+    sat += __shfl_xor(sat, off);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_max[w] = amax16;
+    s_sat[w] = sat;
+  }
+  __syncthreads();
+  // waves 1.. leave here instead of waiting for thread 0's round trips
+  if (threadIdx.x >= 64) return;
+  uint32_t last = 0;
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    uint64_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      m = s_max[i] > m ? s_max[i] : m;
+      c += s_sat[i];
+    }
+    const uint32_t G = gridDim.x, j = blockIdx.x % FP8DP_ACC_SLOTS;
+    fp8dp_acc_slot* slot = st->acc + j;
+    // both atomics in flight together; the ticket is issued only once the
+    // memory counter shows them performed (vmcnt counts atomics and stores)
+    if (m) __hip_atomic_fetch_max(&slot->amax, m << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c) __hip_atomic_fetch_add(&slot->sat, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    const uint32_t nj = G / FP8DP_ACC_SLOTS + (j < G % FP8DP_ACC_SLOTS ? 1u : 0u);
+    const uint32_t nslots = G < FP8DP_ACC_SLOTS ? G : FP8DP_ACC_SLOTS;
+    if (__hip_atomic_fetch_add(&slot->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        nj - 1)
+      last = __hip_atomic_fetch_add(&st->ticket, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == nslots - 1 ? 1u : 0u;
+  }
+  if (__shfl(last, 0)) state_update_wave(st);
+}
+
 }  // namespace fp8dp

@@ -50,10 +50,13 @@ constexpr int kBlocksPerCURead = 32;   // reads > writes
 // routine.  scale_ptr: the multiplier (read once); slots: accumulators or
 // nullptr.  FORM: kFormOne / kFormPair (the grid covers every vector, one or
 // two per thread, loaded first thing, no loop) or kFormLoop (grid-stride).
-template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW, int FORM = kFormLoop>
+// UPD: the launch also closes the step (block_fold_update): slots are st->acc.
+template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool HW, int FORM = kFormLoop,
+          bool UPD = false>
 __global__ __launch_bounds__(kThreads) void k_quant_tensor(
     const uint4* __restrict__ h, uint4* __restrict__ bout, uint2* __restrict__ qout, int64_t n8,
-    int tail, const float* __restrict__ scale_ptr, fp8dp_acc_slot* __restrict__ slots) {
+    int tail, const float* __restrict__ scale_ptr, fp8dp_acc_slot* __restrict__ slots,
+    fp8dp_tensor_state* st = nullptr) {
   const float s = CAST ? *scale_ptr : 1.0f;
   uint32_t amax16 = 0, sat = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -100,7 +103,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(
       if constexpr (AMAX) amax16 = a16 > amax16 ? a16 : amax16;
     }
   }
-  if (slots != nullptr && (AMAX || CAST)) block_fold<kThreads>(AMAX ? amax16 : 0u, CAST ? sat : 0u, slots);
+  if constexpr (UPD) {
+    __shared__ uint32_t sm[2 * (kThreads / 64)];
+    block_fold_update<kThreads>(amax16, sat, st, sm);
+  } else if (slots != nullptr && (AMAX || CAST)) {
+    block_fold<kThreads>(AMAX ? amax16 : 0u, CAST ? sat : 0u, slots);
+  }
 }
 
 // ------------------------------------------------------------------ per group
@@ -283,7 +291,7 @@ __global__ void k_state_init(fp8dp_tensor_state* st, int fmt, int hist_len, floa
                              float initial_amax) {
   const int l = threadIdx.x;  // 64 threads
   st->acc[l].amax = 0;
-  st->acc[l].reserved0 = 0;
+  st->acc[l].ticket = 0;
   st->acc[l].sat = 0;
   if (l < FP8DP_MAX_HIST) st->history[l] = (l < hist_len) ? initial_amax : 0.0f;
   if (l == 0) {
@@ -300,54 +308,12 @@ __global__ void k_state_init(fp8dp_tensor_state* st, int fmt, int hist_len, floa
     st->hist_pos = 0;
     st->steps = 0;
     st->fmt = fmt;
+    st->ticket = 0;
   }
 }
 
-// One wave: lane l reduces accumulator slot l and holds history entry l.
-// Every load is issued before any use (one memory round trip instead of a
-// chain of dependent ones); the ring after this step's write -- entry pos
-// replaced by the step's amax -- is reduced in registers.
-__global__ void k_history_update(fp8dp_tensor_state* st) {
-  const int l = threadIdx.x;  // 64 threads
-  uint32_t m = st->acc[l].amax;
-  uint64_t c = st->acc[l].sat;
-  const float h = l < FP8DP_MAX_HIST ? st->history[l] : 0.0f;
-  const int len = st->hist_len;
-  const int pos = st->hist_pos;
-  const float margin = st->margin;
-  const int fmt = st->fmt;
-  const float sinv = st->scale_inv;
-  const uint32_t steps = st->steps;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t om = __shfl_xor(m, off);
-    m = om > m ? om : m;
-    const uint32_t clo = __shfl_xor((uint32_t)c, off);
-    const uint32_t chi = __shfl_xor((uint32_t)(c >> 32), off);
-    c += ((uint64_t)chi << 32) | clo;
-  }
-  const float amax_t = __uint_as_float(m);
-  uint32_t hm = l < len ? (__float_as_uint(l == pos ? amax_t : h) & 0x7FFFFFFFu) : 0u;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(hm, off);
-    hm = o > hm ? o : hm;
-  }
-  st->acc[l].amax = 0;
-  st->acc[l].sat = 0;
-  if (l == 0) {
-    st->history[pos] = amax_t;
-    st->hist_pos = (pos + 1 == len) ? 0 : pos + 1;
-    st->scale_inv_used = sinv;
-    const float s = scale_rule(__uint_as_float(hm), margin, fmt == 0 ? 448.0f : 57344.0f);
-    st->scale = s;
-    st->scale_inv = recip_rn(s);
-    st->sat_last = c;
-    st->overflow = c > 0 ? 1u : 0u;
-    st->amax_last = amax_t;
-    st->steps = steps + 1;
-  }
-}
+// One wave closes the step (state_update_wave, quant_core.hpp).
+__global__ void k_history_update(fp8dp_tensor_state* st) { state_update_wave(st); }
 
 // ------------------------------------------------------------------ weights
 __global__ void k_w_zero(float* scale_out) { scale_out[1] = 0.0f; }
@@ -515,9 +481,10 @@ __global__ __launch_bounds__(kThreads) void k_copy(const uint4* __restrict__ src
 }
 
 // ------------------------------------------------------------------ dispatch
-template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST>
+template <int FMT, int ACT, bool WBF16, bool AMAX, bool CAST, bool UPD = false>
 static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout,
-                         const float* scale_ptr, fp8dp_acc_slot* slots, hipStream_t stream) {
+                         const float* scale_ptr, fp8dp_acc_slot* slots, hipStream_t stream,
+                         fp8dp_tensor_state* st = nullptr) {
   const int64_t n8 = n / 8;
   const int tail = (int)(n % 8);
   const LaunchShape ls = launch_shape(n8, kThreads, WBF16, kBlocksPerCURead);
@@ -525,10 +492,10 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
                             ? grid_for(n8 > 0 ? n8 : 1, kThreads, WBF16 ? kBlocksPerCU : kBlocksPerCURead)
                             : ls.grid;
 #define FP8DP_LAUNCH_T(F)                                                                     \
-  hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true, F>), dim3(grid),      \
+  hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, true, F, UPD>), dim3(grid), \
                      dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),            \
                      reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail, \
-                     scale_ptr, slots)
+                     scale_ptr, slots, st)
   if (codec() == 0 && ls.form == kFormOne)
     FP8DP_LAUNCH_T(kFormOne);
   else if (codec() == 0 && ls.form == kFormPair)
@@ -536,12 +503,26 @@ static int launch_tensor(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* 
   else if (codec() == 0)
     FP8DP_LAUNCH_T(kFormLoop);
   else
-    hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, false>), dim3(grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
+    hipLaunchKernelGGL((k_quant_tensor<FMT, ACT, WBF16, AMAX, CAST, false, kFormLoop, UPD>),
+                       dim3(grid), dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(h),
                        reinterpret_cast<uint4*>(bout), reinterpret_cast<uint2*>(qout), n8, tail,
-                       scale_ptr, slots);
+                       scale_ptr, slots, st);
 #undef FP8DP_LAUNCH_T
   return check_launch("quantize");
+}
+
+// quantize_fused_update: the same launches with the step's end in the last workgroup
+template <int FMT, int ACT>
+static int dispatch_tensor_update(const uint16_t* h, int64_t n, uint16_t* bout, uint8_t* qout,
+                                  fp8dp_tensor_state* st, hipStream_t stream) {
+  const float* sp = &st->scale;
+  if (bout && qout)
+    return launch_tensor<FMT, ACT, true, true, true, true>(h, n, bout, qout, sp, st->acc, stream, st);
+  if (bout)
+    return launch_tensor<FMT, ACT, true, true, false, true>(h, n, bout, qout, sp, st->acc, stream, st);
+  if (qout)
+    return launch_tensor<FMT, ACT, false, true, true, true>(h, n, bout, qout, sp, st->acc, stream, st);
+  return launch_tensor<FMT, ACT, false, true, false, true>(h, n, bout, qout, sp, st->acc, stream, st);
 }
 
 template <int FMT, int ACT>
@@ -746,6 +727,29 @@ extern "C" int quantize_fused(const uint16_t* h, int64_t rows, int64_t cols, fp8
   return act == FP8DP_ACT_RELU2
              ? dispatch_group<1, 1>(h, n, bf16_out, fp8_out, group_scale_inv, slots, stream)
              : dispatch_group<1, 0>(h, n, bf16_out, fp8_out, group_scale_inv, slots, stream);
+}
+
+extern "C" int quantize_fused_update(const uint16_t* h, int64_t rows, int64_t cols,
+                                     fp8dp_act act, fp8dp_format fmt, fp8dp_tensor_state* st,
+                                     uint16_t* bf16_out, uint8_t* fp8_out, hipStream_t stream) {
+  if (h == nullptr || st == nullptr || rows < 1 || cols < 1) {
+    set_error("quantize_fused_update: need non-NULL input and state, rows, cols >= 1");
+    return FP8DP_EINVAL;
+  }
+  if (!valid_fmt(fmt) || !valid_act(act)) {
+    set_error("quantize_fused_update: unknown format %d or activation %d", (int)fmt, (int)act);
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(h) || !aligned16(bf16_out) || !aligned16(fp8_out) || !aligned16(st)) {
+    set_error("quantize_fused_update: tensor and state pointers must be 16-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  const int64_t n = rows * cols;
+  if (fmt == FP8DP_E4M3)
+    return act == FP8DP_ACT_RELU2 ? dispatch_tensor_update<0, 1>(h, n, bf16_out, fp8_out, st, stream)
+                                  : dispatch_tensor_update<0, 0>(h, n, bf16_out, fp8_out, st, stream);
+  return act == FP8DP_ACT_RELU2 ? dispatch_tensor_update<1, 1>(h, n, bf16_out, fp8_out, st, stream)
+                                : dispatch_tensor_update<1, 0>(h, n, bf16_out, fp8_out, st, stream);
 }
 
 extern "C" int quantize_weight(const uint16_t* w, int64_t N, int64_t K, fp8dp_format fmt,

@@ -111,49 +111,6 @@ def check_gemm(y, ref, absref, what, exact=True, allowance=None):
                  "the FP8 matrix instructions truncate small products (exact mode meets it)")
 
 
-def bf16_admissible(y_bits: np.ndarray, ref: np.ndarray, absref: np.ndarray, width: int = 8):
-    """The BF16 values a GEMM meeting the bound may store for each element:
-    every BF16 value v with |v - ref| <= 2^-8 |ref| + 1e-5 sum|ab|, found by
-    walking BF16 neighbours out from the stored value y (which must itself be
-    admissible).  Returns uint16 patterns [n, width], each row padded with
-    repeats of y; raises if an element has more than `width` candidates."""
-    y_bits = np.asarray(y_bits, np.uint16).reshape(-1)
-    ref = np.asarray(ref, np.float64).reshape(-1)
-    bound = (2.0 ** -8) * np.abs(ref) + 1e-5 * np.asarray(absref, np.float64).reshape(-1)
-
-    def val(b):
-        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-    # order-preserving key of a BF16 pattern (finite values; -0 and +0 equal)
-    def key(b):
-        b = b.astype(np.int64)
-        return np.where(b & 0x8000, -(b & 0x7FFF), b)
-
-    def from_key(k):
-        return np.where(k < 0, (-k) | 0x8000, k).astype(np.uint16)
-
-    ok = np.abs(val(y_bits) - ref) <= bound
-    assert ok.all(), f"{int((~ok).sum())} stored values outside the bound"
-    out = np.repeat(y_bits[:, None], width, axis=1)
-    k0 = key(y_bits)
-    n = 1
-    for step in (-1, 1):
-        k = k0.copy()
-        live = np.ones(y_bits.size, bool)
-        for _ in range(width):
-            k = k + step
-            cand = from_key(k)
-            inb = live & (np.abs(val(cand) - ref) <= bound)
-            live = inb
-            if not live.any():
-                break
-            if n >= width:
-                raise AssertionError("more admissible BF16 values than the candidate width")
-            out[inb, n] = cand[inb]
-            n += 1
-    return out
-
-
 def encode_range_parallel(lo: int, hi: int, fmt: int) -> np.ndarray:
     n = hi - lo
     step = (n + THREADS - 1) // THREADS

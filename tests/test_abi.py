@@ -171,11 +171,11 @@ def test_mx_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"format" in L.fp8dp_last_error()
     rc = L.quantize_mx(24, 4, 64, 0, 0, None, 16, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_mx(16, 0, 16, 16, 0, 16, 128, 128, 128, 16, None)
+    rc = L.fp8_gemm_mx(16, 0, 16, 16, 0, 16, 128, 128, 128, 1, 16, None)
     assert rc == -1 and b"256" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_mx(16, 0, 18, 16, 0, 16, 256, 128, 128, 16, None)
+    rc = L.fp8_gemm_mx(16, 0, 18, 16, 0, 16, 256, 128, 128, 1, 16, None)
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
-    rc = L.fp8_gemm_mx(16, 3, 16, 16, 0, 16, 256, 128, 128, 16, None)
+    rc = L.fp8_gemm_mx(16, 3, 16, 16, 0, 16, 256, 128, 128, 1, 16, None)
     assert rc == -1 and b"format" in L.fp8dp_last_error()
 
 

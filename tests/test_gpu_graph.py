@@ -3,7 +3,8 @@
 Every entry point enqueues kernels on the caller's stream, never allocates
 and never synchronizes, so a whole step -- quantize_fused on H, the FP8 GEMM,
 amax_history_update, the E5M2 cast of dY, its update, and the overflow
-recompute of both casts -- can be captured once and replayed.  Each replay
+recompute of both casts; or the benchmark's form with each cast closing its
+own step (quantize_fused_update) -- can be captured once and replayed.  Each replay
 is one more step of delayed scaling: the test replays the graph several
 times, with eager work and host synchronizations in between, and checks
 every replay bit for bit against the same steps run eagerly on a second set
@@ -20,17 +21,28 @@ from gpu_util import DEV, to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 
-def _step(bufs, recompute=True):
+def _step(bufs, fused=False, recompute=True):
+    """fused: the benchmark's step -- each cast closes its step itself
+    (quantize_fused_update) and the GEMM reads the used scale's inverse."""
     h, a16, a8, w8, wsc, y, dy, dy8, st_a, st_g = bufs
-    sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, a16, a8)
-    sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR, st_a.field_ptr("scale_inv"), wsc, y)
-    sq.amax_history_update(st_a)
+    if fused:
+        sq.quantize_fused_update(h, sq.ACT_RELU2, sq.E4M3, st_a, a16, a8)
+        sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                           st_a.field_ptr("scale_inv_used"), wsc, y)
+    else:
+        sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, a16, a8)
+        sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR, st_a.field_ptr("scale_inv"),
+                           wsc, y)
+        sq.amax_history_update(st_a)
     if recompute:
         sq.quantize_recompute(h, sq.ACT_RELU2, sq.E4M3, st_a, a8)
         sq.fp8_gemm_scaled_if(a8, sq.E4M3, w8, sq.E4M3, st_a.field_ptr("scale_inv"), wsc, y,
                               st_a.field_ptr("overflow"))
-    sq.quantize_fused(dy, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, dy8)
-    sq.amax_history_update(st_g)
+    if fused:
+        sq.quantize_fused_update(dy, sq.ACT_IDENTITY, sq.E5M2, st_g, None, dy8)
+    else:
+        sq.quantize_fused(dy, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None, dy8)
+        sq.amax_history_update(st_g)
     if recompute:
         sq.quantize_recompute(dy, sq.ACT_IDENTITY, sq.E5M2, st_g, dy8)
 
@@ -48,8 +60,9 @@ def _buffers(w, h, dy, wt):
             sq.TensorState(sq.E5M2, 1, w.margin, w.initial_amax)]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused_update"])
 @pytest.mark.parametrize("name", ["tiny", "gpt2"])
-def test_step_graph_replays_equal_eager_steps(name):
+def test_step_graph_replays_equal_eager_steps(name, fused):
     w = workloads.get(name)
     h = to_dev_bf16(w.h0())
     dy = to_dev_bf16(w.dy())
@@ -60,18 +73,18 @@ def test_step_graph_replays_equal_eager_steps(name):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # warm-up outside the capture (library load)
-        _step(g_bufs)
+        _step(g_bufs, fused)
     torch.cuda.current_stream().wait_stream(side)
-    _step(e_bufs)                          # the eager twin runs the same warm-up step
+    _step(e_bufs, fused)                   # the eager twin runs the same warm-up step
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _step(g_bufs)
+        _step(g_bufs, fused)
     # capture enqueues nothing: the captured step has not run yet
     torch.cuda.synchronize()
     for rep in range(4):
         graph.replay()
-        _step(e_bufs)
+        _step(e_bufs, fused)
         torch.cuda.synchronize()
         for k in (1, 2, 5, 7):             # a16, a8, y, dy8
             assert torch.equal(g_bufs[k].view(torch.uint8), e_bufs[k].view(torch.uint8)), (rep, k)

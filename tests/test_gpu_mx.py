@@ -4,12 +4,16 @@
 microscaling recipe gives each block of 32 adjacent values its own
 power-of-two scale.  quantize_mx is compared bit for bit with oracle
 quantize_mx (BF16 copy, codes, E8M0 block exponents); fp8_gemm_mx with the
-oracle's float64 MX GEMM to |y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| plus the
-FP8 instructions' truncation allowance, the fraction outside the plain bound
-capped.  Workloads: the seeded synthetic tensors of workloads.py (the GPT-2
-MLP activation and down-projection weight at full size), block magnitudes
-spread over many binades, and special blocks (zero, signed zero, subnormal,
-infinity, NaN).
+oracle's float64 MX GEMM to |y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| on every
+element in exact mode (the default), both where a tile's block exponents fold
+into the FP16 widening (rows spanning at most 22 binades, E4M3, or 8, E5M2)
+and where a tile takes the per-block fallback (wider spans; tiles of both
+kinds in one launch).  The microscaled FP8 instructions' mode is held to the
+same bound and reported as an expected failure where their truncation takes
+elements outside it.  Workloads: the seeded synthetic tensors of workloads.py
+(the GPT-2 MLP activation and down-projection weight at full size), block
+magnitudes spread over many binades, and special blocks (zero, signed zero,
+subnormal, infinity, NaN).
 """
 import numpy as np
 import pytest
@@ -150,11 +154,16 @@ def test_quantize_mx_errors():
 
 
 # ------------------------------------------------------------------ GEMM
-def _check(y, ref, absref, allowance, what):
-    """The plain bound on every element; elements the microscaled FP8
-    instruction's truncation takes outside it make the case an expected
-    failure (after the allowance accounts for each of them)."""
-    check_gemm(y, ref, absref, what, False, allowance)
+EXACT, FP8 = sq.ACCUM_EXACT, sq.ACCUM_MFMA_FP8
+BOTH = pytest.mark.parametrize("accum", [EXACT, FP8], ids=["exact", "fp8"])
+
+
+def _check(y, ref, absref, allowance, what, accum):
+    """The plain bound on every element.  Exact mode must meet it everywhere;
+    in FP8 mode, elements the microscaled instruction's truncation takes
+    outside it make the case an expected failure (after the allowance
+    accounts for each of them)."""
+    check_gemm(y, ref, absref, what, accum == EXACT, allowance)
 
 
 def _gemm_case(rng, M, N, K, fa, fb, lo=-12, hi=12):
@@ -165,36 +174,91 @@ def _gemm_case(rng, M, N, K, fa, fb, lo=-12, hi=12):
     return ra.fp8, ra.scale, rb.fp8, rb.scale
 
 
-def _gemm_mx_dev(a8, fa, ea, b8, fb, eb):
+def _gemm_mx_dev(a8, fa, ea, b8, fb, eb, accum):
     M, N = a8.shape[0], b8.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    sq.fp8_gemm_mx(to_dev_u8(a8), fa, to_dev_u8(ea), to_dev_u8(b8), fb, to_dev_u8(eb), y)
+    sq.fp8_gemm_mx(to_dev_u8(a8), fa, to_dev_u8(ea), to_dev_u8(b8), fb, to_dev_u8(eb), y, accum)
     return y.float().cpu().numpy()
 
 
-@pytest.mark.parametrize("M,N,K,fa,fb", [(256, 128, 128, 0, 0), (256, 384, 1024, 0, 0),
-                                         (512, 512, 512, 1, 0), (256, 640, 256, 0, 1),
-                                         (768, 768, 3072, 0, 0), (256, 256, 384, 1, 1)])
-def test_gemm_mx_vs_oracle(M, N, K, fa, fb):
-    rng = np.random.default_rng(M + 3 * N + 7 * K + fa + 2 * fb)
-    a8, ea, b8, eb = _gemm_case(rng, M, N, K, fa, fb)
-    y = _gemm_mx_dev(a8, fa, ea, b8, fb, eb)
+def _span(e):
+    """Largest per-row spread (max - min) of block exponent bytes."""
+    e = e.astype(np.int32)
+    return int((e.max(axis=1) - e.min(axis=1)).max())
+
+
+# block exponent spreads: lo..hi binades of the inputs; E4M3 rows of +-12
+# span more than 22 binades in some tiles (fallback) and the E5M2 ones more
+# than 8 (fallback everywhere), +-4 folds everywhere
+@BOTH
+@pytest.mark.parametrize("M,N,K,fa,fb,spread", [(256, 128, 128, 0, 0, 12), (256, 384, 1024, 0, 0, 12),
+                                                (512, 512, 512, 1, 0, 12), (256, 640, 256, 0, 1, 12),
+                                                (768, 768, 3072, 0, 0, 12), (256, 256, 384, 1, 1, 12),
+                                                (512, 384, 1024, 0, 0, 9), (256, 256, 1024, 1, 1, 3),
+                                                (256, 384, 512, 0, 1, 3)])
+def test_gemm_mx_vs_oracle(M, N, K, fa, fb, spread, accum):
+    rng = np.random.default_rng(M + 3 * N + 7 * K + fa + 2 * fb + spread)
+    a8, ea, b8, eb = _gemm_case(rng, M, N, K, fa, fb, -spread, spread)
+    y = _gemm_mx_dev(a8, fa, ea, b8, fb, eb, accum)
     rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 24)), [M - 1]]))
     ref, absref = O.gemm_mx_f64(a8, fa, ea, b8, fb, eb, rows)
     _check(y[rows], ref, absref,
-           lambda sel: fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, rows[sel]), f"{M}x{N}x{K}")
+           lambda sel: fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, rows[sel]),
+           f"{M}x{N}x{K} spread {spread}", accum)
 
 
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 1), (0, 1)])
+def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb):
+    """Rows 0-255 (the first row tile) and columns 0-127 keep their blocks
+    within the fold span; one A row of the second row tile and one B row of
+    the second column tile spread over 40 binades, so three of the four
+    256 x 128 tiles take the per-block fallback and one folds.  Every output
+    meets the plain bound."""
+    M, N, K = 512, 256, 1024
+    rng = np.random.default_rng(31 + fa + 2 * fb)
+    narrow = {0: 9, 1: 3}
+    ha = _spread(rng, M, K, -narrow[fa], narrow[fa])
+    hb = _spread(rng, N, K, -narrow[fb], narrow[fb])
+    ha[300] = _spread(rng, 1, K, -20, 20)[0]
+    hb[200] = _spread(rng, 1, K, -20, 20)[0]
+    ra = O.quantize_mx(ha, O.ACT_IDENTITY, fa, want_bf16=False)
+    rb = O.quantize_mx(hb, O.ACT_IDENTITY, fb, want_bf16=False)
+    span_a, span_b = {0: 22, 1: 8}[fa], {0: 22, 1: 8}[fb]
+    assert _span(ra.scale[:256]) <= span_a and _span(rb.scale[:128]) <= span_b
+    assert _span(ra.scale[300:301]) > span_a and _span(rb.scale[200:201]) > span_b
+    y = _gemm_mx_dev(ra.fp8, fa, ra.scale, rb.fp8, fb, rb.scale, EXACT)
+    rows = np.unique(np.concatenate([np.arange(0, M, 8), [255, 256, 300, M - 1]]))
+    ref, absref = O.gemm_mx_f64(ra.fp8, fa, ra.scale, rb.fp8, fb, rb.scale, rows)
+    check_gemm(y[rows], ref, absref, f"mixed tiles {fa}{fb}")
+
+
+def test_gemm_mx_exact_full_range_codes():
+    """Every finite code equally likely and block exponents over the whole
+    quantizer range: the fallback meets the bound on every element."""
+    rng = np.random.default_rng(77)
+    M, N, K = 256, 256, 2048
+    ta = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E4M3)))
+    tb = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E5M2)))
+    a8 = rng.choice(ta, size=(M, K)).astype(np.uint8)
+    b8 = rng.choice(tb, size=(N, K)).astype(np.uint8)
+    ea = rng.integers(127 - 40, 127 + 40, (M, K // 32)).astype(np.uint8)
+    eb = rng.integers(127 - 40, 127 + 40, (N, K // 32)).astype(np.uint8)
+    y = _gemm_mx_dev(a8, O.E4M3, ea, b8, O.E5M2, eb, EXACT)
+    ref, absref = O.gemm_mx_f64(a8, O.E4M3, ea, b8, O.E5M2, eb)
+    check_gemm(y, ref, absref, "full range")
+
+
+@BOTH
 @pytest.mark.parametrize("M,N,K", [(512, 384, 1536), (256, 256, 512)])
-def test_gemm_mx_exponent_copy_paths_agree(M, N, K):
+def test_gemm_mx_exponent_copy_paths_agree(M, N, K, accum):
     """With K a multiple of 512 and 16-byte aligned exponent arrays the kernel
     copies four stages' exponents per row at once; exponent arrays 4 bytes off
     that alignment take the per-stage copies.  Both read the same bytes, so the
     outputs are equal bit for bit, and both match the oracle."""
     rng = np.random.default_rng(K + N)
-    a8, ea, b8, eb = _gemm_case(rng, M, N, K, 0, 0)
+    a8, ea, b8, eb = _gemm_case(rng, M, N, K, 0, 0, -9, 9)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y)
+    sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y, accum)
 
     def off4(x):
         buf = torch.zeros(x.size + 16, dtype=torch.uint8, device=DEV)
@@ -204,17 +268,21 @@ def test_gemm_mx_exponent_copy_paths_agree(M, N, K):
         return v
 
     y2 = torch.empty_like(y)
-    sq.fp8_gemm_mx(to_dev_u8(a8), 0, off4(ea), to_dev_u8(b8), 0, off4(eb), y2)
+    sq.fp8_gemm_mx(to_dev_u8(a8), 0, off4(ea), to_dev_u8(b8), 0, off4(eb), y2, accum)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     rows = np.unique(np.concatenate([np.arange(0, M, 16), [M - 1]]))
     ref, absref = O.gemm_mx_f64(a8, 0, ea, b8, 0, eb, rows)
     _check(y.float().cpu().numpy()[rows], ref, absref,
-           lambda sel: fp8_mfma_allowance_mx(a8, 0, ea, b8, 0, eb, rows[sel]), f"{M}x{N}x{K}")
+           lambda sel: fp8_mfma_allowance_mx(a8, 0, ea, b8, 0, eb, rows[sel]), f"{M}x{N}x{K}",
+           accum)
 
 
-def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
+@BOTH
+def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm(accum):
     """Exponent bytes 127 + i (A) and 127 + j (B) everywhere equal per-tensor
-    scales 2^i, 2^j: the MX GEMM then matches fp8_gemm_scaled bit for bit."""
+    scales 2^i, 2^j: the MX GEMM then matches fp8_gemm_scaled in the same
+    accumulation mode bit for bit (the fold scales every product by one power
+    of two, which the epilogue takes back exactly)."""
     rng = np.random.default_rng(5)
     M, N, K = 512, 768, 1024
     t = O.fp8_decode_table(0)
@@ -225,16 +293,16 @@ def test_gemm_mx_neutral_exponents_equal_per_tensor_gemm():
         ea = np.full((M, K // 32), 127 + i, np.uint8)
         eb = np.full((N, K // 32), 127 + j, np.uint8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-        sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y)
+        sq.fp8_gemm_mx(to_dev_u8(a8), 0, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y, accum)
         y2 = torch.empty_like(y)
         sa = torch.tensor([2.0 ** i], dtype=torch.float32, device=DEV)
         sb = torch.tensor([2.0 ** j], dtype=torch.float32, device=DEV)
-        sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(b8), 0, sq.PER_TENSOR, sa, sb, y2,
-                           sq.ACCUM_MFMA_FP8)
+        sq.fp8_gemm_scaled(to_dev_u8(a8), 0, to_dev_u8(b8), 0, sq.PER_TENSOR, sa, sb, y2, accum)
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (i, j)
 
 
-def test_gemm_mx_gpt2_down_projection():
+@BOTH
+def test_gemm_mx_gpt2_down_projection(accum):
     """The GPT-2 down-projection in MXFP8: H = relu2(H0) and W cast by
     quantize_mx on the GPU, checked byte for byte against the oracle's cast,
     then the GEMM on sampled rows against the oracle."""
@@ -244,18 +312,18 @@ def test_gemm_mx_gpt2_down_projection():
     _, qa, ea = _run_mx(h, sq.ACT_RELU2, sq.E4M3, want_bf16=False)
     _, qb, eb = _run_mx(wt, sq.ACT_IDENTITY, sq.E4M3, want_bf16=False)
     rng = np.random.default_rng(17)
-    rows = np.sort(rng.choice(h.shape[0], size=24, replace=False))
+    rows = np.sort(rng.choice(h.shape[0], size=64, replace=False))
     ra = O.quantize_mx(h[rows], O.ACT_RELU2, O.E4M3, want_bf16=False)
     rb = O.quantize_mx(wt, O.ACT_IDENTITY, O.E4M3, want_bf16=False)
     assert np.array_equal(u8_np(qa)[rows], ra.fp8) and np.array_equal(u8_np(ea)[rows], ra.scale)
     assert np.array_equal(u8_np(qb), rb.fp8) and np.array_equal(u8_np(eb), rb.scale)
     M, N = h.shape[0], wt.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    sq.fp8_gemm_mx(qa, sq.E4M3, ea, qb, sq.E4M3, eb, y)
+    sq.fp8_gemm_mx(qa, sq.E4M3, ea, qb, sq.E4M3, eb, y, accum)
     ref, absref = O.gemm_mx_f64(ra.fp8, O.E4M3, ra.scale, rb.fp8, O.E4M3, rb.scale)
     _check(y.float().cpu().numpy()[rows], ref, absref,
            lambda sel: fp8_mfma_allowance_mx(ra.fp8, 0, ra.scale, rb.fp8, 0, rb.scale, sel),
-           "gpt2 mx")
+           "gpt2 mx", accum)
 
 
 def test_gemm_mx_errors():
@@ -264,8 +332,11 @@ def test_gemm_mx_errors():
     y = torch.empty((256, 256), dtype=torch.bfloat16, device=DEV)
     b = torch.zeros((256, 128), dtype=torch.uint8, device=DEV)
     rc = sq.lib().fp8_gemm_mx(a.data_ptr(), 0, e.data_ptr(), b.data_ptr(), 0, e.data_ptr(),
-                              128, 256, 128, y.data_ptr(), None)
+                              128, 256, 128, EXACT, y.data_ptr(), None)
     assert rc == -1
     rc = sq.lib().fp8_gemm_mx(a.data_ptr(), 0, e.data_ptr(), b.data_ptr(), 0, e.data_ptr() + 1,
-                              256, 256, 128, y.data_ptr(), None)
+                              256, 256, 128, EXACT, y.data_ptr(), None)
     assert rc == -1
+    rc = sq.lib().fp8_gemm_mx(a.data_ptr(), 0, e.data_ptr(), b.data_ptr(), 0, e.data_ptr(),
+                              256, 256, 128, 7, y.data_ptr(), None)
+    assert rc == -1 and b"accumulation" in sq.lib().fp8dp_last_error()

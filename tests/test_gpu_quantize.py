@@ -162,6 +162,70 @@ def test_gpt2_sixteen_delayed_steps_full_size():
     assert ost.overflow == 0 and len(set(scales[1:])) > 1
 
 
+@pytest.mark.parametrize("shape,limit", [((1, 8), 0), ((3, 1001), 0), ((64, 256), 1),
+                                         ((300, 2048), 3), ((300, 2048), 64), ((300, 2048), 100),
+                                         ((1031, 777), 0), ((16384, 3072), 0)])
+def test_fused_update_equals_quantize_then_update(shape, limit, codec):
+    """quantize_fused_update against quantize_fused followed by
+    amax_history_update: codes, BF16 copy and every field of the state equal
+    after each of 5 steps (so the tickets are back at zero for the next call),
+    for grids of 1, 3, 64, 100 workgroups and unlimited ones (a workgroup
+    count below, at and off the 64 accumulator slots, and the looping form),
+    with an earlier quantize_fused call of the same step folded in on step 2;
+    and the state sequence against the oracle's."""
+    h0 = workloads.normal(47 + shape[0], *shape)
+    prev = sq.fp8dp_set_grid_limit(limit)
+    try:
+        st_a = sq.TensorState(sq.E4M3, 4, 1.25, 0.5)
+        st_b = sq.TensorState(sq.E4M3, 4, 1.25, 0.5)
+        ost = O.State(O.E4M3, 4, 1.25, 0.5)
+        for t, f in enumerate((1.0, 3.0, 0.5, 40.0, 1.0)):
+            h = h0 if f == 1.0 else workloads.scale_bf16(h0, f)
+            hd = to_dev_bf16(h)
+            b1, q1 = torch.empty_like(hd), torch.empty(shape, dtype=torch.uint8, device=DEV)
+            b2, q2 = torch.empty_like(hd), torch.empty(shape, dtype=torch.uint8, device=DEV)
+            if t == 2:                     # an earlier call of the same step
+                extra = to_dev_bf16(workloads.scale_bf16(h0, 7.0))
+                qx = torch.empty(shape, dtype=torch.uint8, device=DEV)
+                for st in (st_a, st_b):
+                    sq.quantize_fused(extra, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st, None, qx)
+            sq.quantize_fused(hd, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, b1, q1)
+            sq.amax_history_update(st_a)
+            sq.quantize_fused_update(hd, sq.ACT_RELU2, sq.E4M3, st_b, b2, q2)
+            assert torch.equal(b1.view(torch.int16), b2.view(torch.int16)), t
+            assert torch.equal(q1, q2), t
+            da, d = st_a.read(), st_b.read()          # every field (not the padding)
+            assert da == d, (t, {k: (da[k], d[k]) for k in d if da[k] != d[k]})
+            assert d["ticket"] == 0 and d["slot_tickets"] == 0, t
+            r = oracle_quantize(h, O.ACT_RELU2, O.E4M3, O.PER_TENSOR, ost.scale)
+            assert np.array_equal(u8_np(q2), r.fp8), t
+            amax, sat = r.amax_bits, r.sat
+            if t == 2:
+                re = oracle_quantize(workloads.scale_bf16(h0, 7.0), O.ACT_RELU2, O.E4M3,
+                                     O.PER_TENSOR, ost.scale, want_bf16=False)
+                amax, sat = max(amax, re.amax_bits), sat + re.sat
+            ost.accumulate(amax, sat)
+            ost.update()
+            _compare_state(st_b, ost)
+    finally:
+        sq.fp8dp_set_grid_limit(prev)
+
+
+def test_fused_update_gradient_cast_identity_e5m2():
+    """The gradient form: identity, E5M2, no BF16 copy, ragged length."""
+    x = workloads.signed_lognormal(48, 7, 4099)
+    st_a = sq.TensorState(sq.E5M2, 1, 1.25, 1.0)
+    st_b = sq.TensorState(sq.E5M2, 1, 1.25, 1.0)
+    for t in range(3):
+        hd = to_dev_bf16(x)
+        q1 = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+        q2 = torch.empty_like(q1)
+        sq.quantize_fused(hd, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_a, None, q1)
+        sq.amax_history_update(st_a)
+        sq.quantize_fused_update(hd, sq.ACT_IDENTITY, sq.E5M2, st_b, None, q2)
+        assert torch.equal(q1, q2) and st_a.read() == st_b.read(), t
+
+
 @pytest.mark.parametrize("hist_len", [2, 4, 16])
 def test_history_window_sequence(hist_len):
     """Delayed scaling with a window of hist_len steps ("FP8 training: what it

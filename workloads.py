@@ -36,6 +36,8 @@ seed + 5000.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Callable, Dict, List
 
@@ -62,7 +64,8 @@ def _rows_chunked(stream, rows: int, cols: int, draw: Callable, row0: int = 0,
     out = np.empty((nrows, cols), dtype=np.float32)
     c0 = row0 // CHUNK_ROWS
     c1 = (row0 + nrows + CHUNK_ROWS - 1) // CHUNK_ROWS
-    for c in range(c0, c1):
+
+    def chunk(c):
         r_lo = c * CHUNK_ROWS
         r_hi = min(rows, r_lo + CHUNK_ROWS)
         rng = np.random.default_rng(stream + [c])
@@ -70,6 +73,15 @@ def _rows_chunked(stream, rows: int, cols: int, draw: Callable, row0: int = 0,
         a = max(r_lo, row0)
         b = min(r_hi, row0 + nrows)
         out[a - row0:b - row0] = block[a - r_lo:b - r_lo]
+
+    # chunks are independent streams, so drawing them on several threads
+    # gives the same bytes as drawing them in order
+    if c1 - c0 >= 8 and nrows * cols >= (1 << 24):
+        with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+            list(ex.map(chunk, range(c0, c1)))
+    else:
+        for c in range(c0, c1):
+            chunk(c)
     return out
 
 
