@@ -221,6 +221,25 @@ int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, 
                            const float* a_scale_inv, const float* b_scale_inv, float* workspace,
                            uint16_t* y, hipStream_t stream);
 
+/* fp8_gemm_scaled_splitk without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The split partials go to a device array of 16 Mi floats (64 MiB) inside
+ * the library, one per GPU, held until the process ends; its device address
+ * is resolved on the first call on each device (hipGetSymbolAddress, no
+ * allocation).  Same arguments, kernels and result as fp8_gemm_scaled_splitk
+ * (bit for bit), minus the workspace.  Nothing in the array needs clearing:
+ * each call writes every partial it reads.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (on different streams, or from
+ * several threads) race and must be serialized by the caller.
+ * Errors: those of fp8_gemm_scaled_splitk; EINVAL when splits * M * N
+ * exceeds 16 Mi floats; EHIP when no device is current or the array's
+ * address cannot be resolved. */
+int fp8_gemm_scaled_splitk_noalloc(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
+                                   fp8dp_format fb, int64_t M, int64_t N, int64_t K,
+                                   int32_t splits, fp8dp_accum accum, const float* a_scale_inv,
+                                   const float* b_scale_inv, uint16_t* y, hipStream_t stream);
+
 /* dst [cols x rows] = src [rows x cols] transposed, bytes (FP8 codes): the
  * operand layouts of the backward GEMMs (dgrad needs W^T, wgrad dY^T and
  * X^T).  The codes and their scale are unchanged.

@@ -8,10 +8,10 @@ It raises if the library has not been built; there is no CPU fallback.
 
 Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, quantize_fused_update,
-    fp8_gemm_scaled,
-    quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
-    fp8_transpose, and the comparison / diagnostic calls fp8dp_bench_*,
-    fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit, fp8dp_set_codec.
+    fp8_gemm_scaled, quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
+    fp8_gemm_scaled_splitk_noalloc, fp8_transpose, and the comparison / diagnostic
+    calls fp8dp_bench_*, fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit,
+    fp8dp_set_codec.
 """
 from __future__ import annotations
 
@@ -50,6 +50,8 @@ _SIGS = {
     "quantize_weight": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "fp8_gemm_scaled_splitk": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
                                 _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_scaled_splitk_noalloc": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32,
+                                        _vp, _vp, _vp, _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
@@ -284,6 +286,20 @@ def fp8_gemm_scaled_splitk(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, s
                                         _p(a_scale_inv),
                                         _p(b_scale_inv), _p(workspace), _p(y), _stream(stream)),
            "fp8_gemm_scaled_splitk")
+
+
+def fp8_gemm_scaled_splitk_noalloc(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int,
+                                   splits: int, a_scale_inv: Ptr, b_scale_inv: Ptr,
+                                   y: torch.Tensor, accum: int = ACCUM_EXACT,
+                                   stream=None) -> None:
+    """fp8_gemm_scaled_splitk with the library's own per-GPU scratch array
+    (splits * M * N <= 16 Mi floats) instead of a workspace: allocates nothing.
+    Calls that overlap on one GPU race."""
+    M, N, K = _gemm_operands("fp8_gemm_scaled_splitk_noalloc", a, b, y)
+    _check(lib().fp8_gemm_scaled_splitk_noalloc(_p(a), fa, _p(b), fb, M, N, K, splits, accum,
+                                                _p(a_scale_inv), _p(b_scale_inv), _p(y),
+                                                _stream(stream)),
+           "fp8_gemm_scaled_splitk_noalloc")
 
 
 def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -4,6 +4,8 @@
 // and the gradient cast in its epilogue).  The kernels are in gemm_kernels.hpp.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gemm_kernels.hpp"
 
 namespace fp8dp {
@@ -152,6 +154,65 @@ extern "C" int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const u
   return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
     return launch_split_tile<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
         a, b, M, N, K, splits, a_scale_inv, b_scale_inv, workspace, y, stream);
+  });
+}
+
+// ------------------------------------------------------------------ no-allocation form
+// The split partials of fp8_gemm_scaled_splitk_noalloc live in this array
+// (one copy per GPU, held until the process ends) instead of a caller's
+// workspace.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is resolved once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;   // 64 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+static std::mutex g_scratch_mu;
+static float* g_scratch_dev[64];   // per device; nullptr until resolved
+
+// The calling thread's current device's copy of scratch (resolved on the
+// first call on that device, with that device current).
+static int scratch_for_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("fp8_gemm_scaled_splitk_noalloc: no current HIP device (or device index >= 64)");
+    return FP8DP_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("fp8_gemm_scaled_splitk_noalloc: hipGetSymbolAddress failed: %s",
+                hipGetErrorString(e));
+      return FP8DP_EHIP;
+    }
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return FP8DP_OK;
+}
+
+extern "C" int fp8_gemm_scaled_splitk_noalloc(const uint8_t* a, fp8dp_format fa,
+                                              const uint8_t* b, fp8dp_format fb, int64_t M,
+                                              int64_t N, int64_t K, int32_t splits,
+                                              fp8dp_accum accum, const float* a_scale_inv,
+                                              const float* b_scale_inv, uint16_t* y,
+                                              hipStream_t stream) {
+  const int rc = check_splitk("fp8_gemm_scaled_splitk_noalloc", a, fa, b, fb, M, N, K, splits,
+                              accum, a_scale_inv, b_scale_inv, y);
+  if (rc != FP8DP_OK) return rc;
+  if ((int64_t)splits * M * N > kScratchFloats) {
+    set_error("fp8_gemm_scaled_splitk_noalloc: splits * M * N = %lld floats exceeds the "
+              "%lld-float (64 MiB) scratch array; use fp8_gemm_scaled_splitk with a workspace",
+              (long long)splits * M * N, (long long)kScratchFloats);
+    return FP8DP_EINVAL;
+  }
+  float* ws = nullptr;
+  const int sr = scratch_for_current_device(&ws);
+  if (sr != FP8DP_OK) return sr;
+  return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
+    return launch_split_tile<decltype(A)::value, decltype(B)::value, decltype(X)::value>(
+        a, b, M, N, K, splits, a_scale_inv, b_scale_inv, ws, y, stream);
   });
 }
 

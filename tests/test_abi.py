@@ -32,7 +32,7 @@ def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
-              "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
+              "fp8_gemm_scaled_splitk_noalloc", "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
               "fp8_gemm_scaled_if", "relu2_backward_quantize", "fp8_gemm_relu2_backward",
               "fp8dp_last_error"):
         assert n in names
@@ -111,6 +111,16 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_splitk(16, 0, 16, 1, 256, 128, 512, 2, 7, 16, 16, 16, 16, None)
     assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
+    # fp8_gemm_scaled_splitk_noalloc(a, fa, b, fb, M, N, K, splits, accum, sa, sb, y, stream):
+    # the split-K checks, then the scratch limit (16 Mi floats), all before any HIP call
+    rc = L.fp8_gemm_scaled_splitk_noalloc(16, 0, 16, 1, 256, 128, 512, 0, 1, 16, 16, 16, None)
+    assert rc == -1 and b"splits" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk_noalloc(16, 0, 16, 1, 256, 128, 512, 2, 7, 16, 16, 16, None)
+    assert rc == -1 and b"accumulation" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk_noalloc(16, 0, 16, 1, 4096, 4096, 1024, 2, 1, 16, 16, 16, None)
+    assert rc == -1 and b"scratch" in L.fp8dp_last_error()
+    rc = L.fp8_gemm_scaled_splitk_noalloc(16, 0, 16, 1, 256, 128, 512, 2, 1, 16, 16, None, None)
+    assert rc == -1 and b"NULL" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 96, 32, None)
     assert rc == -1 and b"64" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 64, 16, None)
