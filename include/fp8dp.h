@@ -115,9 +115,14 @@ typedef struct fp8dp_tensor_state {
 /* Size in bytes of fp8dp_tensor_state (for callers allocating raw bytes). */
 int64_t fp8dp_state_size(void);
 
-/* Initialise a state: history filled with initial_amax, accumulators zeroed,
-   scale = max / (initial_amax * margin) (1.0 if that is not a positive finite
-   number), scale_inv = 1/scale.  Runs as a one-thread kernel on `stream`.
+/* Initialise a state for delayed scaling ("Paradigma ...": each step casts
+   with the scale derived from the previous step's amax times a safety margin;
+   "FP8 training ...", Trade-offs and edge cases: the amax kept over a stored
+   history window).  The pages leave the first step's amax open; it is taken
+   as initial_amax here: history filled with initial_amax, accumulators
+   zeroed, scale = max / (initial_amax * margin) (1.0 if that is not a
+   positive finite number), scale_inv = 1/scale.  Runs as a one-thread kernel
+   on `stream`.
    Errors: EINVAL for st == NULL, misaligned st, bad fmt, hist_len outside
    1..FP8DP_MAX_HIST, or a margin that is not positive and finite. */
 int fp8dp_state_init(fp8dp_tensor_state* st, fp8dp_format fmt, int32_t hist_len, float margin,
