@@ -393,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
                                                      Relu2Bwd bwd = {}) {
   static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
   static_assert(BC < 0 || !(MX || SPLIT), "the backward epilogue follows the per-tensor GEMM");
-  static_assert(!(EX && MX) || TN == 2, "exact microscaled accumulation: 256 x 128 tiles");
+  static_assert(!(EX && MX) || TN <= 3, "exact microscaled accumulation: 256 x 128 or 256 x 192 tiles");
   if constexpr (COND) {
     if (*run_flag == 0) return;
   }
@@ -780,48 +780,46 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       // of the per-group path with microscaling's block size.
       const int KB = K / 32;
       for (int blk = 0; blk < KB; ++blk) {
-        v16f_t part[TM][TN];
+        v8h_t ha[2][TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const size_t k0 = (size_t)blk * 32 + 16 * sl + 8 * fhalf;
-          v8h_t ha[TM], hb[TN];
+        for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
+            const size_t k0 = (size_t)blk * 32 + 16 * sl + 8 * fhalf;
             const uint2 u = *reinterpret_cast<const uint2*>(A + (size_t)(m0 + wr + 32 * i + frow) * K + k0);
             const v8i_t x = {(int)u.x, (int)u.y, 0, 0, 0, 0, 0, 0};
-            ha[i] = widen8<FA, 0>(x);
+            ha[sl][i] = widen8<FA, 0>(x);
           }
+        // one B fragment column at a time: its TM partial sums, then their promotion
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j) {
+          v16f_t part[TM];
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) {
+            const size_t k0 = (size_t)blk * 32 + 16 * sl + 8 * fhalf;
             const uint2 u = *reinterpret_cast<const uint2*>(B + (size_t)(n0 + wc + 32 * j + frow) * K + k0);
             const v8i_t x = {(int)u.x, (int)u.y, 0, 0, 0, 0, 0, 0};
-            hb[j] = widen8<FB, 0>(x);
+            const v8h_t hb = widen8<FB, 0>(x);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+              if (sl == 0) {
+                const v16f_t zero = {};
+                part[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[0][i], hb, zero, 0, 0, 0);
+              } else {
+                part[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[1][i], hb, part[i], 0, 0, 0);
+              }
+            }
           }
+          const int e_b = eb[(size_t)(n0 + wc + 32 * j + frow) * KB + blk];
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb[j], part[i][j], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) {
+              const int row = m0 + wr + 32 * i + (r >> 2) * 8 + fhalf * 4 + (r & 3);
+              const int e_a = ea[(size_t)row * KB + blk];
+              acc[i][j][r] += __builtin_ldexpf(part[i][r], e_a + e_b - 254);
+            }
         }
-        int e_b[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) e_b[j] = eb[(size_t)(n0 + wc + 32 * j + frow) * KB + blk];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wr + 32 * i + (r >> 2) * 8 + fhalf * 4 + (r & 3);
-            const int e_a = ea[(size_t)row * KB + blk];
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j][r] += __builtin_ldexpf(part[i][j][r], e_a + e_b[j] - 254);
-          }
       }
       epi_plain(m0, n0, false);
       return;
@@ -961,7 +959,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     // MFMAs of slice q run, so no half starts with a run of converts in
     // front of its first MFMA, and no convert overwrites an operand an MFMA
     // in flight still reads.
-    constexpr bool EXP = EX && !PG;
+    // (exact MX at 256 x 192 widens each slice just before its MFMAs: the
+    // double-buffered widening's registers would spill beside the exponents)
+    constexpr bool EXP = EX && !PG && !(MX && TN == 3);
     v8h_t wa[EXP ? TM : 1], wb[EXP ? TN : 1];
     // MX: slice q of substep h holds block 2 h + q / 2 of the stage (the
     // lane's bytes 0-15 are the first block's, 16-31 the second's); its codes
@@ -988,6 +988,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
 #pragma unroll
         for (int j = 0; j < TN; ++j) ob[j] = widen8<FB, q>(fb[j]);
       }
+    };
+    auto mfmas_mx_direct = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa,
+                               const uint32_t* xb, int h) {
+      static_for<4>([&](auto Q) {
+        v8h_t ha[TM], hb[TN];
+        widen_slice(fa, fb, xa, xb, h, Q, ha, hb);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+      });
     };
     auto mfmas_ex = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa, const uint32_t* xb,
                         int h, const v8i_t* nfa, const v8i_t* nfb, const uint32_t* nxa,
@@ -1040,6 +1052,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       // first half: read substep 1 of stage kt, multiply substep 0
       load_frags(kt, 1, fa1, fb1, xa1, xb1);
       if constexpr (EXP) mfmas_ex(fa0, fb0, xa0, xb0, 0, fa1, fb1, xa1, xb1, 1);
+      else if constexpr (EX && MX) mfmas_mx_direct(fa0, fb0, xa0, xb0, 0);
       else mfmas(fa0, fb0, xa0, xb0, 0);
       if constexpr (MX || PG) {
         // keep these products in the first half: without a use here the
@@ -1063,6 +1076,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       }
       if (kt + 1 < GS) load_frags(kt + 1, 0, fa0, fb0, xa0, xb0);
       if constexpr (EXP) mfmas_ex(fa1, fb1, xa1, xb1, 1, fa0, fb0, xa0, xb0, 0);
+      else if constexpr (EX && MX) mfmas_mx_direct(fa1, fb1, xa1, xb1, 1);
       else mfmas(fa1, fb1, xa1, xb1, 1);
       if constexpr (PER) {
         if ((kt + 1) % KT == 0) {   // the last stage of a tile: its epilogue, then a fresh sum

@@ -25,11 +25,8 @@ template <int FA, int FB, bool EX>
 static int launch_mx_tile(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
                           const uint8_t* eb, int64_t M, int64_t N, int64_t K, uint16_t* y,
                           hipStream_t stream) {
-  // no 256-wide tile here: with the exponent registers it would spill; exact
-  // accumulation takes 256 x 128 (its fold references and fallback)
-  if constexpr (!EX) {
-    if (N % 192 == 0) return launch_mx<FA, FB, 3, EX>(a, ea, b, eb, M, N, K, y, stream);
-  }
+  // no 256-wide tile here: with the exponent registers it would spill
+  if (N % 192 == 0) return launch_mx<FA, FB, 3, EX>(a, ea, b, eb, M, N, K, y, stream);
   return launch_mx<FA, FB, 2, EX>(a, ea, b, eb, M, N, K, y, stream);
 }
 

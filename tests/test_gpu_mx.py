@@ -207,15 +207,16 @@ def test_gemm_mx_vs_oracle(M, N, K, fa, fb, spread, accum):
            f"{M}x{N}x{K} spread {spread}", accum)
 
 
+@pytest.mark.parametrize("N", [256, 384])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 1), (0, 1)])
-def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb):
-    """Rows 0-255 (the first row tile) and columns 0-127 keep their blocks
+def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb, N):
+    """Rows 0-255 (the first row tile) and columns 0-191 keep their blocks
     within the fold span; one A row of the second row tile and one B row of
-    the second column tile spread over 40 binades, so three of the four
-    256 x 128 tiles take the per-block fallback and one folds.  Every output
-    meets the plain bound."""
-    M, N, K = 512, 256, 1024
-    rng = np.random.default_rng(31 + fa + 2 * fb)
+    the second column tile (256 x 128 tiles at N = 256, 256 x 192 at N = 384)
+    spread over 40 binades, so three of the four tiles take the per-block
+    fallback and one folds.  Every output meets the plain bound."""
+    M, K = 512, 1024
+    rng = np.random.default_rng(31 + fa + 2 * fb + N)
     narrow = {0: 9, 1: 3}
     ha = _spread(rng, M, K, -narrow[fa], narrow[fa])
     hb = _spread(rng, N, K, -narrow[fb], narrow[fb])
@@ -224,12 +225,12 @@ def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb):
     ra = O.quantize_mx(ha, O.ACT_IDENTITY, fa, want_bf16=False)
     rb = O.quantize_mx(hb, O.ACT_IDENTITY, fb, want_bf16=False)
     span_a, span_b = {0: 22, 1: 8}[fa], {0: 22, 1: 8}[fb]
-    assert _span(ra.scale[:256]) <= span_a and _span(rb.scale[:128]) <= span_b
+    assert _span(ra.scale[:256]) <= span_a and _span(rb.scale[:192]) <= span_b
     assert _span(ra.scale[300:301]) > span_a and _span(rb.scale[200:201]) > span_b
     y = _gemm_mx_dev(ra.fp8, fa, ra.scale, rb.fp8, fb, rb.scale, EXACT)
     rows = np.unique(np.concatenate([np.arange(0, M, 8), [255, 256, 300, M - 1]]))
     ref, absref = O.gemm_mx_f64(ra.fp8, fa, ra.scale, rb.fp8, fb, rb.scale, rows)
-    check_gemm(y[rows], ref, absref, f"mixed tiles {fa}{fb}")
+    check_gemm(y[rows], ref, absref, f"mixed tiles {fa}{fb} N={N}")
 
 
 def test_gemm_mx_exact_full_range_codes():
