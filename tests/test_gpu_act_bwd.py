@@ -56,7 +56,7 @@ def _inputs(rng, n, cache):
     if cache == O.CACHE_BF16:
         return dA, a, 1.0
     s = O.scale_from_amax(float(((a.astype(np.uint32) << 16).view(np.float32)).max()), 1.25,
-                          cache)[0]
+                          cache)[0][0]
     r = O.quantize(a, O.ACT_IDENTITY, cache, O.PER_TENSOR, float(s), want_bf16=False)
     return dA, r.fp8.reshape(-1), float(np.float32(1.0) / np.float32(s))
 

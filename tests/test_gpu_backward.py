@@ -121,7 +121,7 @@ def gpt2_codes():
     q_w, s_w, _ = O.quantize_weight_tensor(w.weight(), O.E4M3)
     dy = w.dy()
     s_dy = O.scale_from_amax(float(np.abs((dy.astype(np.uint32) << 16).view(np.float32)).max()),
-                             1.0, O.E5M2)[0]
+                             1.0, O.E5M2)[0][0]
     rd = oracle_quantize(dy, O.ACT_IDENTITY, O.E5M2, O.PER_TENSOR, s_dy, want_bf16=False)
     return r.fp8, 11.0, q_w, s_w, rd.fp8, s_dy
 

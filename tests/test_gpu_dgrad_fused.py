@@ -117,7 +117,7 @@ def test_fused_gpt2_down_projection(accum):
     w8, s_w, _ = O.quantize_weight_tensor(w.weight(), O.E4M3)
     dy = w.dy()
     s_dy = O.scale_from_amax(float(np.abs((dy.astype(np.uint32) << 16).view(np.float32)).max()),
-                             1.0, O.E5M2)[0]
+                             1.0, O.E5M2)[0][0]
     rd = oracle_quantize(dy, O.ACT_IDENTITY, O.E5M2, O.PER_TENSOR, s_dy, want_bf16=False)
     w8t = np.ascontiguousarray(w8.T)                       # [3072 x 768]
     M = rd.fp8.shape[0]
