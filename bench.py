@@ -288,7 +288,8 @@ def main():
         out["naive_three_pass"] = naive(sq, torch, H, A16[0], A8[0], n_in, args, dev, q_bytes,
                                         elems, q_mean)
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
-    out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args)
+    out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args,
+                                     H, A16, DY)
     out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["per_group_128"] = per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["fp8_cached_activation"] = fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args,
@@ -463,10 +464,12 @@ def fused_up(sq, torch, np, w, A16, A8, dev, args):
             "hipblaslt_bf16_gemm_ms": None if lib_ms is None else round(lib_ms, 5)}
 
 
-def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
+def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args, H, A16, DY):
     """The FP8 recipe's two backward GEMMs of the down-projection on the step's
     codes: dA = dY W (E5M2 x E4M3, needs W8^T) and dW = dY^T A (split-K,
-    needs dY8^T and A8^T), with the transposes they need."""
+    needs dY8^T and A8^T), with the transposes they need; and the casts that
+    write the transposed codes themselves (quantize_fused_transposed) against
+    the cast followed by the transpose."""
     M, K, N = w.M, w.K, w.N
     stream = torch.cuda.current_stream()
     w8t = torch.empty((K, N), dtype=torch.uint8, device=dev)
@@ -514,6 +517,31 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args):
     sq.fp8_gemm_relu2_backward(dy8, sq.E5M2, w8t, sq.E4M3, si_g, wsc, A8[0], sq.CACHE_E4M3, si_a,
                                sq.E5M2, st_h, dh8)
     sq.amax_history_update(st_h)
+    # the casts with a transposed copy of the codes, against cast + transpose
+    st_t = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
+    st_tg = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
+    dy_d = DY[0]
+    t_qa_t = timed(lambda: sq.quantize_fused_transposed(H[0], sq.ACT_RELU2, sq.E4M3, st_t, at,
+                                                        A16[0], A8[0]))
+    t_qa = timed(lambda: sq.quantize_fused(H[0], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_t,
+                                           A16[0], A8[0]))
+    t_qg_t = timed(lambda: sq.quantize_fused_transposed(dy_d, sq.ACT_IDENTITY, sq.E5M2, st_tg,
+                                                        dyt, None, dy8))
+    t_qg = timed(lambda: sq.quantize_fused(dy_d, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_tg,
+                                           None, dy8))
+    sq.amax_history_update(st_t)
+    sq.amax_history_update(st_tg)
+    res["cast_with_transposed_codes"] = {
+        "activation": {"shape": f"H[{M}x{K}] relu2 -> bf16 copy + e4m3 + e4m3^T [{K}x{M}]",
+                       "ms": round(t_qa_t, 5),
+                       "GB/s": round(M * K * 6 / (t_qa_t * 1e-3) / 1e9, 1),
+                       "cast_then_transpose_ms": round(t_qa + t_a, 5),
+                       "speedup": round((t_qa + t_a) / t_qa_t, 3)},
+        "gradient": {"shape": f"dY[{M}x{N}] -> e5m2 + e5m2^T [{N}x{M}]",
+                     "ms": round(t_qg_t, 5),
+                     "GB/s": round(M * N * 4 / (t_qg_t * 1e-3) / 1e9, 1),
+                     "cast_then_transpose_ms": round(t_qg + t_dy, 5),
+                     "speedup": round((t_qg + t_dy) / t_qg_t, 3)}}
     t_fused = timed(lambda: sq.fp8_gemm_relu2_backward(dy8, sq.E5M2, w8t, sq.E4M3, si_g, wsc,
                                                        A8[0], sq.CACHE_E4M3, si_a, sq.E5M2,
                                                        st_h, dh8))

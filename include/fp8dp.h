@@ -245,6 +245,23 @@ int fp8_gemm_scaled_splitk_noalloc(const uint8_t* a, fp8dp_format fa, const uint
                                    int32_t splits, fp8dp_accum accum, const float* a_scale_inv,
                                    const float* b_scale_inv, uint16_t* y, hipStream_t stream);
 
+/* quantize_fused in PER_TENSOR mode (delayed scale from st, accumulators into
+ * st's slots, amax_history_update closes the step as usual) that also writes
+ * its codes transposed: fp8_t_out[c * rows + r] = code(r, c), the [cols x rows]
+ * operand layout of the weight-gradient GEMM ("FP8 Training & Inference", FP8
+ * Training Recipe: dW = dY^T X; this GEMM contracts along the contiguous
+ * dimension of both operands).  One more byte written per element replaces a
+ * separate fp8_transpose pass.  The codes, BF16 copy, amax and saturation
+ * count are quantize_fused's, bit for bit.
+ *   fp8_t_out: required, [cols x rows] bytes; bf16_out, fp8_out: optional
+ *   ([rows x cols], as in quantize_fused).
+ * Errors: EINVAL for NULL h, st or fp8_t_out, rows not a positive multiple
+ * of 64 or cols of 128, misaligned (16 bytes) pointers, a bad format or
+ * activation. */
+int quantize_fused_transposed(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                              fp8dp_format fmt, fp8dp_tensor_state* st, uint16_t* bf16_out,
+                              uint8_t* fp8_out, uint8_t* fp8_t_out, hipStream_t stream);
+
 /* dst [cols x rows] = src [rows x cols] transposed, bytes (FP8 codes): the
  * operand layouts of the backward GEMMs (dgrad needs W^T, wgrad dY^T and
  * X^T).  The codes and their scale are unchanged.

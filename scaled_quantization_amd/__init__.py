@@ -9,9 +9,9 @@ It raises if the library has not been built; there is no CPU fallback.
 Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, quantize_fused_update,
     fp8_gemm_scaled, quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
-    fp8_gemm_scaled_splitk_noalloc, fp8_transpose, and the comparison / diagnostic
-    calls fp8dp_bench_*, fp8dp_convert_f32, fp8dp_scale_rule, fp8dp_set_grid_limit,
-    fp8dp_set_codec.
+    fp8_gemm_scaled_splitk_noalloc, fp8_transpose, quantize_fused_transposed, and the
+    comparison / diagnostic calls fp8dp_bench_*, fp8dp_convert_f32, fp8dp_scale_rule,
+    fp8dp_set_grid_limit, fp8dp_set_codec.
 """
 from __future__ import annotations
 
@@ -53,6 +53,8 @@ _SIGS = {
     "fp8_gemm_scaled_splitk_noalloc": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _i32,
                                         _vp, _vp, _vp, _vp], ctypes.c_int),
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "quantize_fused_transposed": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
+                                  ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
     "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
@@ -300,6 +302,24 @@ def fp8_gemm_scaled_splitk_noalloc(a: torch.Tensor, fa: int, b: torch.Tensor, fb
                                                 _p(a_scale_inv), _p(b_scale_inv), _p(y),
                                                 _stream(stream)),
            "fp8_gemm_scaled_splitk_noalloc")
+
+
+def quantize_fused_transposed(h: torch.Tensor, act: int, fmt: int, st, fp8_t_out: torch.Tensor,
+                              bf16_out: Ptr = None, fp8_out: Ptr = None, stream=None) -> None:
+    """Per-tensor quantize_fused of h [rows, cols] that also writes the codes
+    transposed to fp8_t_out [cols, rows] (uint8)."""
+    if h.dim() != 2:
+        raise Fp8dpError("quantize_fused_transposed: h must be [rows, cols]")
+    _elem(h, (2,), "quantize_fused_transposed: h")
+    rows, cols = h.shape
+    _codes(fp8_t_out, "quantize_fused_transposed: fp8_t_out")
+    if fp8_t_out.numel() != rows * cols:
+        raise Fp8dpError("quantize_fused_transposed: fp8_t_out needs cols x rows codes")
+    _room(bf16_out, rows * cols * 2, "quantize_fused_transposed: bf16_out")
+    _room(fp8_out, rows * cols, "quantize_fused_transposed: fp8_out")
+    _check(lib().quantize_fused_transposed(_p(h), rows, cols, act, fmt, _state_ptr(st),
+                                           _p(bf16_out), _p(fp8_out), _p(fp8_t_out),
+                                           _stream(stream)), "quantize_fused_transposed")
 
 
 def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

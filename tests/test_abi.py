@@ -32,7 +32,7 @@ def test_header_declares_the_named_entry_points():
     names = declared_functions()
     for n in ("quantize_fused", "amax_history_update", "fp8_gemm_scaled", "fp8dp_state_init",
               "quantize_weight", "gemm_bf16_quantize_fused", "fp8_gemm_scaled_splitk",
-              "fp8_gemm_scaled_splitk_noalloc", "fp8_transpose", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
+              "fp8_gemm_scaled_splitk_noalloc", "fp8_transpose", "quantize_fused_transposed", "quantize_mx", "fp8_gemm_mx", "quantize_recompute",
               "fp8_gemm_scaled_if", "relu2_backward_quantize", "fp8_gemm_relu2_backward",
               "fp8dp_last_error"):
         assert n in names
@@ -121,6 +121,15 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"scratch" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled_splitk_noalloc(16, 0, 16, 1, 256, 128, 512, 2, 1, 16, 16, None, None)
     assert rc == -1 and b"NULL" in L.fp8dp_last_error()
+    # quantize_fused_transposed(h, rows, cols, act, fmt, st, bf16_out, fp8_out, fp8_t_out, stream)
+    rc = L.quantize_fused_transposed(16, 96, 128, 1, 0, 16, None, None, 16, None)
+    assert rc == -1 and b"multiple of 64" in L.fp8dp_last_error()
+    rc = L.quantize_fused_transposed(16, 128, 128, 1, 0, 16, None, None, None, None)
+    assert rc == -1 and b"non-NULL" in L.fp8dp_last_error()
+    rc = L.quantize_fused_transposed(16, 128, 128, 1, 7, 16, None, None, 16, None)
+    assert rc == -1 and b"format" in L.fp8dp_last_error()
+    rc = L.quantize_fused_transposed(16, 128, 128, 1, 0, 16, None, None, 24, None)
+    assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 96, 32, None)
     assert rc == -1 and b"64" in L.fp8dp_last_error()
     rc = L.fp8_transpose(16, 64, 64, 16, None)
