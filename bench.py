@@ -65,8 +65,9 @@ def parse():
     p.add_argument("--no-large", action="store_true",
                    help="skip the large-configuration leg (H 65536 x 16384) and the "
                         "fine-grained one (H 65536 x 4096, per-128 groups)")
-    p.add_argument("--only", choices=("quantize", "quantize_update", "gemm", "gemm_fp8", "copy", "quantize_mx",
-                                      "gemm_mx", "relu2_bwd", "gemm_pg"), default=None,
+    p.add_argument("--only", choices=("quantize", "quantize_update", "quantize_t", "gemm",
+                                      "gemm_fp8", "copy", "quantize_mx", "gemm_mx", "relu2_bwd",
+                                      "gemm_pg"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
                         "inputs (for hardware counter runs), then exit")
     return p.parse_args()
@@ -333,6 +334,8 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
         for j in range(n_out):
             sq.quantize_fused(H[j % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_GROUP128, None, None,
                               A8[j], GS[j])
+    if args.only == "quantize_t":
+        AT = [torch.empty((K, M), dtype=torch.uint8, device=dev) for _ in range(2)]
     if args.only == "relu2_bwd":
         dA = torch.from_numpy(w.da().view(np.int16)).to(dev).view(torch.bfloat16)
         dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
@@ -358,6 +361,9 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
         elif args.only == "quantize":
             sq.quantize_fused(H[i % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a,
                               A16[i % n_out], A8[i % n_out])
+        elif args.only == "quantize_t":
+            sq.quantize_fused_transposed(H[i % n_in], sq.ACT_RELU2, sq.E4M3, st_a, AT[i % 2],
+                                         A16[i % n_out], A8[i % n_out])
         elif args.only == "quantize_update":
             sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3, st_a, A16[i % n_out],
                                      A8[i % n_out])
