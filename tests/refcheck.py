@@ -27,7 +27,8 @@ def nearest_code(x: np.ndarray, fmt: int) -> np.ndarray:
     whose value is nearest is chosen; among equally near codes the one with
     an even code (last bit 0) wins.  NaN -> 0x7F | sign.
     """
-    x = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(-1)
+    with np.errstate(invalid="ignore"):    # signalling NaN payloads raise the flag when widened
+        x = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(-1)
     table = torch_decode_table(fmt)
     pos_codes = np.array([c for c in range(128) if np.isfinite(table[c])], dtype=np.int64)
     pos_vals = table[pos_codes]
