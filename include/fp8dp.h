@@ -237,9 +237,11 @@ int fp8_gemm_scaled_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* b, 
  * each call writes every partial it reads.  Every call on a GPU shares that
  * GPU's array: calls that overlap on one GPU (on different streams, or from
  * several threads) race and must be serialized by the caller.
+ * The stream must belong to the current device (the array's address is
+ * that device's).
  * Errors: those of fp8_gemm_scaled_splitk; EINVAL when splits * M * N
- * exceeds 16 Mi floats; EHIP when no device is current or the array's
- * address cannot be resolved. */
+ * exceeds 16 Mi floats or the stream belongs to another device; EHIP when
+ * no device is current or the array's address cannot be resolved. */
 int fp8_gemm_scaled_splitk_noalloc(const uint8_t* a, fp8dp_format fa, const uint8_t* b,
                                    fp8dp_format fb, int64_t M, int64_t N, int64_t K,
                                    int32_t splits, fp8dp_accum accum, const float* a_scale_inv,

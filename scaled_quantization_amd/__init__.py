@@ -324,6 +324,8 @@ def quantize_fused_transposed(h: torch.Tensor, act: int, fmt: int, st, fp8_t_out
 
 def fp8_transpose(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     """dst [cols, rows] = src [rows, cols]^T (uint8 codes)."""
+    _codes(src, "fp8_transpose: src")
+    _codes(dst, "fp8_transpose: dst")
     rows, cols = src.shape
     if tuple(dst.shape) != (cols, rows):
         raise Fp8dpError("fp8_transpose: shape mismatch")
@@ -338,9 +340,17 @@ def relu2_backward_quantize(dA: torch.Tensor, a_cache: torch.Tensor, cache: int,
                             bf16_out: Ptr = None, stream=None) -> None:
     """dH = dA * 2 sqrt(A) from the cached activation (FP8 codes + inverse scale, or
     BF16), cast to fmt with st's delayed scale (amax / saturation folded into st)."""
+    _elem(dA, (2,), "relu2_backward_quantize: dA")
+    if cache == CACHE_BF16:
+        _elem(a_cache, (2,), "relu2_backward_quantize: a_cache")
+    else:
+        _codes(a_cache, "relu2_backward_quantize: a_cache")
+    _codes(fp8_out, "relu2_backward_quantize: fp8_out")
+    _elem(bf16_out, (2,), "relu2_backward_quantize: bf16_out")
     rows, cols = (1, dA.numel()) if dA.dim() == 1 else (dA.shape[0], dA[0].numel())
     if a_cache.numel() != dA.numel() or fp8_out.numel() != dA.numel():
         raise Fp8dpError("relu2_backward_quantize: size mismatch")
+    _room(bf16_out, rows * cols * 2, "relu2_backward_quantize: bf16_out")
     _check(lib().relu2_backward_quantize(_p(dA), _p(a_cache), cache, _p(a_scale_inv), rows, cols,
                                          fmt, _state_ptr(st), _p(bf16_out), _p(fp8_out),
                                          _stream(stream)), "relu2_backward_quantize")
@@ -367,7 +377,10 @@ def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.T
                        stream=None) -> None:
     """Re-cast h with st's corrected scale when st's last update flagged an overflow
     (decided on the GPU; otherwise nothing is written)."""
+    _elem(h, (2,), "quantize_recompute: h")
+    _codes(fp8_out, "quantize_recompute: fp8_out")
     rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    _room(fp8_out, rows * cols, "quantize_recompute: fp8_out")
     _check(lib().quantize_recompute(_p(h), rows, cols, act, fmt, _state_ptr(st), _p(fp8_out),
                                     _stream(stream)), "quantize_recompute")
 
@@ -377,6 +390,9 @@ def fp8_gemm_scaled_if(a: torch.Tensor, fa: int, b: torch.Tensor, fb: int, a_sca
                        accum: int = ACCUM_EXACT, stream=None) -> None:
     """Per-tensor FP8 GEMM that runs only when the device word *run_flag is nonzero."""
     M, N, K = _gemm_operands("fp8_gemm_scaled_if", a, b, y)
+    _room(a_scale_inv, 4, "fp8_gemm_scaled_if: a_scale_inv")
+    _room(b_scale_inv, 4, "fp8_gemm_scaled_if: b_scale_inv")
+    _room(run_flag, 4, "fp8_gemm_scaled_if: run_flag")
     _check(lib().fp8_gemm_scaled_if(_p(a), fa, _p(b), fb, M, N, K, accum, _p(a_scale_inv),
                                     _p(b_scale_inv), _p(y), _p(run_flag), _stream(stream)),
            "fp8_gemm_scaled_if")
@@ -386,9 +402,14 @@ def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,
                 scale_out: torch.Tensor, bf16_out: Ptr = None, stream=None) -> None:
     """MXFP8 cast: h [rows, cols] BF16 (cols % 32 == 0) -> fp8_out [rows, cols] codes and
     scale_out [rows, cols/32] E8M0 block exponents (uint8)."""
+    _elem(h, (2,), "quantize_mx: h")
+    _codes(fp8_out, "quantize_mx: fp8_out")
+    _codes(scale_out, "quantize_mx: scale_out")
+    _elem(bf16_out, (2,), "quantize_mx: bf16_out")
     rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
     if fp8_out.numel() != rows * cols or scale_out.numel() * 32 != rows * cols:
         raise Fp8dpError("quantize_mx: output sizes do not match the input")
+    _room(bf16_out, rows * cols * 2, "quantize_mx: bf16_out")
     _check(lib().quantize_mx(_p(h), rows, cols, act, fmt, _p(bf16_out), _p(fp8_out),
                              _p(scale_out), _stream(stream)), "quantize_mx")
 
@@ -408,7 +429,14 @@ def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor
 
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,
                     stream=None) -> None:
+    """w [N, K] BF16 -> w8 [N, K] codes; scale_out: per tensor [1/s, s], per group
+    one inverse scale per 128 x 128 block."""
+    if w.dim() != 2:
+        raise Fp8dpError("quantize_weight: w must be [N, K]")
+    _elem(w, (2,), "quantize_weight: w")
+    _codes(w8, "quantize_weight: w8")
     N, K = w.shape
+    _room(w8, N * K, "quantize_weight: w8")
     if isinstance(scale_out, torch.Tensor):
         need = 2 if mode == PER_TENSOR else (N // 128) * (K // 128)
         if scale_out.dtype != torch.float32 or scale_out.numel() < need:
@@ -422,6 +450,11 @@ def gemm_bf16_quantize_fused(x: torch.Tensor, w: torch.Tensor, act: int = ACT_RE
                              fmt: int = E4M3, st=None, h_out: Ptr = None, bf16_out: Ptr = None,
                              fp8_out: Ptr = None, stream=None) -> None:
     """x [M, K] BF16, w [N, K] BF16 device tensors; outputs [M, N] (see the C header)."""
+    _elem(x, (2,), "gemm_bf16_quantize_fused: x")
+    _elem(w, (2,), "gemm_bf16_quantize_fused: w")
+    _elem(h_out, (2,), "gemm_bf16_quantize_fused: h_out")
+    _elem(bf16_out, (2,), "gemm_bf16_quantize_fused: bf16_out")
+    _codes(fp8_out, "gemm_bf16_quantize_fused: fp8_out")
     M, K = x.shape
     N = w.shape[0]
     if w.shape[1] != K:
@@ -435,32 +468,47 @@ def gemm_bf16_quantize_fused(x: torch.Tensor, w: torch.Tensor, act: int = ACT_RE
 
 
 def fp8dp_bench_act_bf16(h: torch.Tensor, act: int, out: torch.Tensor, stream=None) -> None:
+    _elem(h, (2,), "fp8dp_bench_act_bf16: h")
+    _elem(out, (2,), "fp8dp_bench_act_bf16: out")
+    _room(out, h.numel() * 2, "fp8dp_bench_act_bf16: out")
     _check(lib().fp8dp_bench_act_bf16(_p(h), h.numel(), act, _p(out), _stream(stream)),
            "fp8dp_bench_act_bf16")
 
 
 def fp8dp_bench_amax(x: torch.Tensor, st, stream=None) -> None:
+    _elem(x, (2,), "fp8dp_bench_amax: x")
     _check(lib().fp8dp_bench_amax(_p(x), x.numel(), _state_ptr(st), _stream(stream)),
            "fp8dp_bench_amax")
 
 
 def fp8dp_bench_cast(x: torch.Tensor, fmt: int, st, out: torch.Tensor, stream=None) -> None:
+    _elem(x, (2,), "fp8dp_bench_cast: x")
+    _codes(out, "fp8dp_bench_cast: out")
+    _room(out, x.numel(), "fp8dp_bench_cast: out")
     _check(lib().fp8dp_bench_cast(_p(x), x.numel(), fmt, _state_ptr(st), _p(out),
                                   _stream(stream)), "fp8dp_bench_cast")
 
 
 def fp8dp_bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
+    _room(dst, nbytes, "fp8dp_bench_copy: dst")
     _check(lib().fp8dp_bench_copy(_p(src), _p(dst), nbytes, _stream(stream)), "fp8dp_bench_copy")
 
 
 def fp8dp_convert_f32(x: torch.Tensor, target: int, out: torch.Tensor, stream=None) -> None:
+    """target 0/1: E4M3/E5M2 codes, 2: BF16, 3/4: saturation predicates (bytes),
+    5: binary32 square root (float)."""
+    _elem(x, (4,), "fp8dp_convert_f32: x")
+    _room(out, x.numel() * {2: 2, 5: 4}.get(target, 1), "fp8dp_convert_f32: out")
     _check(lib().fp8dp_convert_f32(_p(x), x.numel(), target, _p(out), _stream(stream)),
            "fp8dp_convert_f32")
 
 
 def fp8dp_scale_rule(amax: torch.Tensor, margin: float, fmt: int, scale: torch.Tensor,
                      scale_inv: Ptr = None, stream=None) -> None:
+    _elem(amax, (4,), "fp8dp_scale_rule: amax")
+    _room(scale, amax.numel() * 4, "fp8dp_scale_rule: scale")
+    _room(scale_inv, amax.numel() * 4, "fp8dp_scale_rule: scale_inv")
     _check(lib().fp8dp_scale_rule(_p(amax), amax.numel(), margin, fmt, _p(scale), _p(scale_inv),
                                   _stream(stream)), "fp8dp_scale_rule")
 

@@ -170,12 +170,20 @@ static std::mutex g_scratch_mu;
 static float* g_scratch_dev[64];   // per device; nullptr until resolved
 
 // The calling thread's current device's copy of scratch (resolved on the
-// first call on that device, with that device current).
-static int scratch_for_current_device(float** out) {
+// first call on that device, with that device current).  The kernels run on
+// the stream's device, so a stream of another device is refused: that
+// device's copy of the array is at another address.
+static int scratch_for_current_device(hipStream_t stream, float** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     set_error("fp8_gemm_scaled_splitk_noalloc: no current HIP device (or device index >= 64)");
     return FP8DP_EHIP;
+  }
+  hipDevice_t sdev = -1;
+  if (stream != nullptr && hipStreamGetDevice(stream, &sdev) == hipSuccess && sdev != dev) {
+    set_error("fp8_gemm_scaled_splitk_noalloc: the stream belongs to device %d, the current "
+              "device is %d; make the stream's device current", (int)sdev, dev);
+    return FP8DP_EINVAL;
   }
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_dev[dev] == nullptr) {
@@ -208,7 +216,7 @@ extern "C" int fp8_gemm_scaled_splitk_noalloc(const uint8_t* a, fp8dp_format fa,
     return FP8DP_EINVAL;
   }
   float* ws = nullptr;
-  const int sr = scratch_for_current_device(&ws);
+  const int sr = scratch_for_current_device(stream, &ws);
   if (sr != FP8DP_OK) return sr;
   return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
     return launch_split_tile<decltype(A)::value, decltype(B)::value, decltype(X)::value>(

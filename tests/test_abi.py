@@ -272,3 +272,52 @@ def test_binding_checks_element_sizes(L):
     with pytest.raises(sq.Fp8dpError, match="fp8_out: expected 8-bit"):
         sq.quantize_fused(torch.zeros(4, 256, dtype=torch.bfloat16), sq.ACT_RELU2, sq.E4M3,
                           sq.PER_TENSOR, None, None, torch.zeros(4, 256, dtype=torch.float16))
+
+
+def test_binding_checks_every_entry_points_tensors(L):
+    # the same refusals on the other entry points: inputs read at 2 bytes per
+    # element, outputs written past the end of a smaller buffer
+    import torch
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    with pytest.raises(sq.Fp8dpError, match="dA: expected 2-byte"):
+        sq.relu2_backward_quantize(u8(4, 256), u8(4, 256), sq.CACHE_E4M3, None, sq.E5M2, None,
+                                   u8(4, 256))
+    with pytest.raises(sq.Fp8dpError, match="a_cache: expected 2-byte"):
+        sq.relu2_backward_quantize(bf(4, 256), u8(4, 256), sq.CACHE_BF16, None, sq.E5M2, None,
+                                   u8(4, 256))
+    with pytest.raises(sq.Fp8dpError, match="bf16_out: needs"):
+        sq.relu2_backward_quantize(bf(4, 256), u8(4, 256), sq.CACHE_E4M3, None, sq.E5M2, None,
+                                   u8(4, 256), bf(4, 128))
+    with pytest.raises(sq.Fp8dpError, match="quantize_recompute: fp8_out: needs"):
+        sq.quantize_recompute(bf(4, 256), sq.ACT_RELU2, sq.E4M3, None, u8(4, 128))
+    with pytest.raises(sq.Fp8dpError, match="quantize_recompute: h: expected 2-byte"):
+        sq.quantize_recompute(u8(4, 256), sq.ACT_RELU2, sq.E4M3, None, u8(4, 256))
+    with pytest.raises(sq.Fp8dpError, match="quantize_mx: h: expected 2-byte"):
+        sq.quantize_mx(u8(4, 256), sq.ACT_RELU2, sq.E4M3, u8(4, 256), u8(4, 8))
+    with pytest.raises(sq.Fp8dpError, match="quantize_mx: bf16_out: needs"):
+        sq.quantize_mx(bf(4, 256), sq.ACT_RELU2, sq.E4M3, u8(4, 256), u8(4, 8), bf(2, 256))
+    with pytest.raises(sq.Fp8dpError, match="quantize_weight: w8: needs"):
+        sq.quantize_weight(bf(128, 256), sq.E4M3, sq.PER_TENSOR, u8(64, 256), torch.zeros(2))
+    with pytest.raises(sq.Fp8dpError, match="quantize_weight: w: expected 2-byte"):
+        sq.quantize_weight(torch.zeros(128, 256), sq.E4M3, sq.PER_TENSOR, u8(128, 256),
+                           torch.zeros(2))
+    with pytest.raises(sq.Fp8dpError, match="gemm_bf16_quantize_fused: x: expected 2-byte"):
+        sq.gemm_bf16_quantize_fused(torch.zeros(256, 128), bf(128, 128))
+    with pytest.raises(sq.Fp8dpError, match="gemm_bf16_quantize_fused: fp8_out: expected 8-bit"):
+        sq.gemm_bf16_quantize_fused(bf(256, 128), bf(128, 128), fp8_out=bf(256, 128))
+    with pytest.raises(sq.Fp8dpError, match="fp8_transpose: dst: expected 8-bit"):
+        sq.fp8_transpose(u8(64, 128), bf(128, 64))
+    with pytest.raises(sq.Fp8dpError, match="run_flag: needs"):
+        sq.fp8_gemm_scaled_if(u8(256, 512), 0, u8(128, 512), 0, torch.ones(1), torch.ones(1),
+                              bf(256, 128), u8(2))
+    with pytest.raises(sq.Fp8dpError, match="fp8dp_bench_copy: dst: needs"):
+        sq.fp8dp_bench_copy(u8(4096), u8(2048))
+    with pytest.raises(sq.Fp8dpError, match="fp8dp_bench_cast: out: needs"):
+        sq.fp8dp_bench_cast(bf(4096), sq.E4M3, None, u8(2048))
+    with pytest.raises(sq.Fp8dpError, match="fp8dp_bench_act_bf16: out: needs"):
+        sq.fp8dp_bench_act_bf16(bf(4096), sq.ACT_RELU2, bf(2048))
+    with pytest.raises(sq.Fp8dpError, match="fp8dp_convert_f32: out: needs"):
+        sq.fp8dp_convert_f32(torch.zeros(64), 5, u8(64))
+    with pytest.raises(sq.Fp8dpError, match="fp8dp_scale_rule: scale: needs"):
+        sq.fp8dp_scale_rule(torch.zeros(8), 1.0, sq.E4M3, torch.zeros(4))
