@@ -26,7 +26,9 @@ matrix instructions' mode (ACCUM_MFMA_FP8, faster, outside that bound on
 some outputs) is timed beside it with its measured out-of-bound fractions.
 
 Prints ONE JSON line.  `ms_per_step` is the time of --steps whole steps
-between two events.  `value` is the fused quantizer's throughput: algorithmic
+between two events, after --warmup steps and, while those have run for less
+than BURST_WARM_MS of GPU time, further untimed steps until the clock has
+settled (`step_clock_settle_steps`).  `value` is the fused quantizer's throughput: algorithmic
 bytes (5 per element: read 2, write 2 + 1) over its average launch duration,
 timed with HIP events on the launch stream around --steps back-to-back
 launches that rotate through the step's inputs and outputs; the GEMM's
@@ -151,6 +153,23 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Under a new sustained load the GPU's clock takes about 5 ms to settle
+    # (the same launches run 3-10% longer until then), and --warmup steps are
+    # ~1 ms (their first launches also carry one-time costs): with
+    # --warmup > 0 further untimed steps run, in timed chunks of 8, until
+    # BURST_WARM_MS of GPU time has passed, as before every burst below, so
+    # that the timed steps see the steady state of a training loop.
+    settle = 0
+    settle_ms = 0.0
+    while args.warmup > 0 and settle_ms < BURST_WARM_MS and settle < 4096:
+        w0, w1 = ev(), ev()
+        w0.record(stream)
+        for i in range(8):
+            step(args.warmup + settle + i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        settle_ms += w0.elapsed_time(w1)
+        settle += 8
 
     # ---------------------------------------------------------------- timed region: whole steps
     # Events only at the two ends: an event recorded between two kernels adds
@@ -160,7 +179,7 @@ def main():
     t_start.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(args.warmup + settle + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -280,6 +299,7 @@ def main():
             "traffic": measured_traffic("fp8_gemm_scaled_mfma_fp8_gpt2", "gemm.hip")},
         "burst_ms": bursts,
         "burst_warmup_ms": BURST_WARM_MS,
+        "step_clock_settle_steps": settle,
         "last_step": {"scale": st_read["scale"], "amax": st_read["amax_last"],
                       "saturated": st_read["sat_last"]},
         "wall_s_timed": round(wall, 3),
