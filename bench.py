@@ -65,8 +65,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-naive", action="store_true")
     p.add_argument("--no-large", action="store_true",
-                   help="skip the large-configuration leg (H 65536 x 16384) and the "
-                        "fine-grained one (H 65536 x 4096, per-128 groups)")
+                   help="skip the large-configuration leg (H 65536 x 16384), the "
+                        "fine-grained one (H 65536 x 4096, per-128 groups) and the outlier "
+                        "one (65 tensors 4096 x 4096)")
     p.add_argument("--only", choices=("quantize", "quantize_update", "quantize_t", "gemm",
                                       "gemm_fp8", "copy", "quantize_mx", "gemm_mx", "relu2_bwd",
                                       "gemm_pg"), default=None,
@@ -323,6 +324,7 @@ def main():
     if not args.no_large:
         out["large_config"] = large_config(sq, torch, dev, args)
         out["fine_grained_config"] = fine_grained(sq, torch, dev, args)
+        out["outlier_config"] = outlier_config(sq, torch, dev, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], oob = cpu_baseline(w, sq, torch, dev)
         out["gemm_fp8_mfma_mode"]["outside_bound_fraction"] = oob
@@ -971,6 +973,62 @@ def fine_grained(sq, torch, dev, args):
                "ms": round(g8, 4), "TFLOP/s": round(tf(g8), 1),
                "frac_of_fp8_peak": round(tf(g8) / FP8_PEAK_TFLOPS, 4)}}
     del H, A8, GS, W, W8, Y
+    torch.cuda.empty_cache()
+    return out
+
+
+def outlier_config(sq, torch, dev, args):
+    """The outlier stress configuration: 65 tensors X_k[4096 x 4096] ~ N(0,1),
+    each with one entry +-1e5 (X_64 = 8 X_63), cast in turn to E4M3 under one
+    delayed-scaling history (identity, margin 1.25, no BF16 copy; 3 bytes per
+    element).  Reported: per step, what the pages' outlier example predicts
+    ("FP8 training ...", Step 2 and the delayed-scaling passages) -- the share
+    of values flushed to zero by the outlier's scale on the steady steps, the
+    saturation count and overflow flag at the cold start and at the 8x jump;
+    and the cast's launch duration, timed like the large configuration's
+    kernels on X_1 .. X_8 in rotation.  Inputs: workloads.py outlier (seed 2),
+    the parity tests' bytes."""
+    import workloads
+    from concurrent.futures import ThreadPoolExecutor
+    w = workloads.get("outlier")
+    M, K = w.M, w.K
+    stream = torch.cuda.current_stream()
+    st = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    keep, flushed, sat, flags = [], [], [], []
+    with ThreadPoolExecutor(8) as ex:
+        for k, x in enumerate(ex.map(workloads.outlier_tensor, range(w.steps))):
+            h = _upload_bf16(torch, x, dev)
+            sq.quantize_fused(h, sq.ACT_IDENTITY, sq.E4M3, sq.PER_TENSOR, st, None, q)
+            sq.amax_history_update(st)
+            flushed.append(((q & 0x7F) == 0).float().mean().item())
+            d = st.read()
+            sat.append(d["sat_last"])
+            flags.append(d["overflow"])
+            if 1 <= k <= 8:
+                keep.append(h)
+    i = [0]
+
+    def one():
+        sq.quantize_fused(keep[i[0] % len(keep)], sq.ACT_IDENTITY, sq.E4M3, sq.PER_TENSOR, st,
+                          None, q)
+        i[0] += 1
+
+    ms = burst_median(torch, stream, one, max(args.steps, 16))
+    nb = M * K * 3
+    steady = sorted(flushed[1:-1])
+    out = {"shape": f"65 x X_k[{M}x{K}] identity -> e4m3 (delayed, margin 1.25), no BF16 copy",
+           "data": "workloads.py outlier (seed 2): the parity tests' bytes",
+           "quantize_fused": {"ms": round(ms, 5), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                              "bytes_per_launch": nb,
+                              "frac_of_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "flushed_fraction_steps_1_63": {"min": round(steady[0], 4),
+                                           "median": round(steady[len(steady) // 2], 4),
+                                           "max": round(steady[-1], 4)},
+           "saturated_codes": {"step_0": sat[0], "steps_1_63": sum(sat[1:-1]), "step_64": sat[-1]},
+           "overflow_flag": {"step_0": flags[0], "steps_1_63": sum(flags[1:-1]),
+                             "step_64": flags[-1]}}
+    del keep, q
     torch.cuda.empty_cache()
     return out
 
