@@ -59,6 +59,12 @@ def test_argument_checks_reject_without_launching(L):
     assert rc == -1 and b"aligned" in L.fp8dp_last_error()
     rc = L.quantize_fused(16, 4, 8, 7, 0, 0, 16, None, None, None, None)
     assert rc == -1
+    # empty inputs are refused, not launched
+    for rows, cols in ((0, 8), (4, 0), (-1, 8)):
+        rc = L.quantize_fused(16, rows, cols, 0, 0, 0, 16, None, 16, None, None)
+        assert rc == -1 and b"rows" in L.fp8dp_last_error()
+    rc = L.quantize_fused_update(16, 0, 8, 0, 0, 16, None, 16, None)
+    assert rc == -1
     rc = L.fp8_gemm_scaled(16, 0, 16, 0, 128, 128, 100, 0, 0, 16, 16, 16, None)
     assert rc == -1 and b"multiples of 128" in L.fp8dp_last_error()
     rc = L.fp8_gemm_scaled(16, 0, 16, 0, 0, 128, 128, 0, 0, 16, 16, 16, None)

@@ -405,3 +405,17 @@ def test_group_scaled_kernels_agree(M, N, K, accum):
     for got, what in ((y2, "small-tile kernel"), (y, "ring kernel")):
         _check(got, ref, absref, what, accum,
                lambda sel: fp8_mfma_allowance(a8, 0, w8, 0, O.PER_GROUP128, sa, sb, rows[sel]))
+
+
+@pytest.mark.parametrize("mode", [sq.PER_TENSOR, sq.PER_GROUP128], ids=["tensor", "group"])
+@pytest.mark.parametrize("accum", [FP8, EXACT], ids=["fp8", "exact"])
+def test_zero_operand_gives_positive_zero(mode, accum):
+    # every product is zero, so every output is the oracle's +0 (positive
+    # zero bits), whatever the scales and the other operand
+    M, N, K = 512, 384, 1024
+    a8, w8, sa, sb = _group_case(M, N, K, 0, 0)
+    a8 = np.zeros_like(a8)
+    if mode == sq.PER_TENSOR:
+        sa, sb = np.float32(0.75), np.float32(3.0)
+    y = _gemm(a8, 0, w8, 0, mode, 1 / sa, 1 / sb, accum)
+    assert not np.any(y.view(np.uint32))

@@ -455,3 +455,46 @@ def test_weight_cast_per_tensor_and_blocks(fmt, codec):
         qb, sib = O.quantize_weight_blocks(wn, fmt)
         assert np.array_equal(u8_np(w8), qb), name
         assert np.array_equal(bs.cpu().numpy().view(np.uint32), sib.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("case", ["zeros", "negative_relu2", "max_bf16", "zero_groups"])
+def test_degenerate_inputs(case, codec):
+    """The method's degenerate cases against the oracle, bytes and state:
+    an all-zero tensor and a squared ReLU of only negative values (amax 0:
+    the next scale takes the rule's fallback), every element at the largest
+    finite BF16 (every code saturates and is counted), and per-128 groups
+    that are all zero or hold a single nonzero value."""
+    rows, cols = 64, 512
+    act, fmt, mode = sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR
+    if case == "zeros":
+        h = np.zeros((rows, cols), dtype=np.uint16)
+        act, fmt = sq.ACT_IDENTITY, sq.E5M2
+    elif case == "negative_relu2":
+        h = workloads.normal(43, rows, cols) | np.uint16(0x8000)     # every value <= -0
+    elif case == "max_bf16":
+        h = np.full((rows, cols), 0x7F7F, dtype=np.uint16)
+        h[::2] |= np.uint16(0x8000)
+        act = sq.ACT_IDENTITY
+    else:
+        h = workloads.normal(44, rows, cols)
+        h[:, 0:128] = 0
+        h[:, 128:256] = 0
+        h[:, 130] = 0x4040                                           # one value: 3.0
+        mode = sq.PER_GROUP128
+    st = sq.TensorState(fmt, 1, 1.25, 3.0)
+    ost = O.State(fmt, 1, 1.25, 3.0)
+    b, q, g = _run(h, act, fmt, mode, st if mode == sq.PER_TENSOR else None)
+    r = O.quantize(h, act, fmt, mode, ost.scale if mode == sq.PER_TENSOR else 1.0)
+    assert np.array_equal(bf16_np(b), r.bf16)
+    assert np.array_equal(u8_np(q), r.fp8)
+    if mode == sq.PER_GROUP128:
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), r.group_scale_inv.view(np.uint32))
+        return
+    if case == "max_bf16":
+        assert r.sat == rows * cols
+    else:
+        assert r.amax_bits == 0 and not np.any(r.fp8 & 0x7F)
+    sq.amax_history_update(st)
+    ost.accumulate(r.amax_bits, r.sat)
+    ost.update()
+    _compare_state(st, ost)
