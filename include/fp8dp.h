@@ -268,7 +268,8 @@ int quantize_fused_transposed(const uint16_t* h, int64_t rows, int64_t cols, fp8
  * operand layouts of the backward GEMMs (dgrad needs W^T, wgrad dY^T and
  * X^T).  The codes and their scale are unchanged.
  * Errors: EINVAL for NULL or misaligned (16 bytes) pointers, src == dst, or
- * rows / cols not positive multiples of 64. */
+ * rows / cols not positive multiples of 64 (or more than 2^31 - 1 tiles of
+ * 64 x 64). */
 int fp8_transpose(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                   hipStream_t stream);
 

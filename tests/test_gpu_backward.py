@@ -36,7 +36,7 @@ def _dev_f32(x):
 
 # ------------------------------------------------------------------ transpose
 @pytest.mark.parametrize("rows,cols", [(64, 64), (128, 320), (192, 64), (768, 3072),
-                                       (16384, 768)])
+                                       (16384, 768), (64, 128), (192, 384), (16448, 192)])
 def test_transpose_exact(rows, cols):
     rng = np.random.default_rng(rows + cols)
     src = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
