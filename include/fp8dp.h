@@ -374,6 +374,25 @@ int fp8_gemm_scaled_if(const uint8_t* a, fp8dp_format fa, const uint8_t* b, fp8d
 int quantize_mx(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act, fp8dp_format fmt,
                 uint16_t* bf16_out, uint8_t* fp8_out, uint8_t* scale_out, hipStream_t stream);
 
+/* quantize_mx with the blocks of 32 running down the columns, its codes and
+ * exponents written transposed ("FP8 training: what it is and how it works",
+ * Trade-offs and edge cases, for the GEMMs that contract along the token
+ * dimension or along a weight's output features: the weight gradient
+ * dW = dY^T X takes dY and X this way, the input gradient dX = dY W takes W).
+ * h [rows x cols] BF16; block j of column c is its rows 32 j .. 32 j + 31:
+ *   b = bf16_rne(act(h)) -> bf16_out [rows x cols], row-major (may be NULL)
+ *   per block: k by quantize_mx's rule, E8M0 byte k + 127 ->
+ *     scale_t_out[c * rows/32 + j]
+ *   codes: fp8_t_out[c * rows + r] = sat_rne(b[r][c] * 2^-k)
+ * i.e. exactly quantize_mx applied to act(h) transposed.  Device pointers
+ * owned by the caller; nothing is allocated.
+ * Errors: EINVAL for NULL h / fp8_t_out / scale_t_out, rows not a positive
+ * multiple of 64 or cols of 128, h, bf16_out or fp8_t_out not 16-byte
+ * aligned, or an unknown act / fmt. */
+int quantize_mx_transposed(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                           fp8dp_format fmt, uint16_t* bf16_out, uint8_t* fp8_t_out,
+                           uint8_t* scale_t_out, hipStream_t stream);
+
 /* MXFP8 GEMM: a [M x K] codes (format fa) with E8M0 block exponents a_scale
  * [M x K/32], b [N x K] codes (format fb) with b_scale [N x K/32] (the output
  * of quantize_mx on each operand), y [M x N] BF16:

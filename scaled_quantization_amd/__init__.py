@@ -9,7 +9,8 @@ It raises if the library has not been built; there is no CPU fallback.
 Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, quantize_fused_update,
     fp8_gemm_scaled, quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
-    fp8_gemm_scaled_splitk_noalloc, fp8_transpose, quantize_fused_transposed, and the
+    fp8_gemm_scaled_splitk_noalloc, fp8_transpose, quantize_fused_transposed,
+    quantize_mx, quantize_mx_transposed, fp8_gemm_mx, and the
     comparison / diagnostic calls fp8dp_bench_*, fp8dp_convert_f32, fp8dp_scale_rule,
     fp8dp_set_grid_limit, fp8dp_set_codec.
 """
@@ -55,6 +56,7 @@ _SIGS = {
     "fp8_transpose": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "quantize_fused_transposed": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
                                   ctypes.c_int),
+    "quantize_mx_transposed": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
     "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
@@ -412,6 +414,28 @@ def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,
     _room(bf16_out, rows * cols * 2, "quantize_mx: bf16_out")
     _check(lib().quantize_mx(_p(h), rows, cols, act, fmt, _p(bf16_out), _p(fp8_out),
                              _p(scale_out), _stream(stream)), "quantize_mx")
+
+
+def quantize_mx_transposed(h: torch.Tensor, act: int, fmt: int, fp8_t_out: torch.Tensor,
+                           scale_t_out: torch.Tensor, bf16_out: Ptr = None,
+                           stream=None) -> None:
+    """MXFP8 cast of h [rows, cols] BF16 with the blocks of 32 down the columns:
+    fp8_t_out [cols, rows] codes, scale_t_out [cols, rows/32] E8M0 exponents
+    (quantize_mx of act(h) transposed); bf16_out [rows, cols] optional."""
+    if h.dim() != 2:
+        raise Fp8dpError("quantize_mx_transposed: h must be [rows, cols]")
+    _elem(h, (2,), "quantize_mx_transposed: h")
+    _codes(fp8_t_out, "quantize_mx_transposed: fp8_t_out")
+    _codes(scale_t_out, "quantize_mx_transposed: scale_t_out")
+    _elem(bf16_out, (2,), "quantize_mx_transposed: bf16_out")
+    rows, cols = h.shape
+    if fp8_t_out.numel() != rows * cols or scale_t_out.numel() * 32 != rows * cols:
+        raise Fp8dpError("quantize_mx_transposed: outputs need cols x rows codes and "
+                         "cols x rows/32 exponents")
+    _room(bf16_out, rows * cols * 2, "quantize_mx_transposed: bf16_out")
+    _check(lib().quantize_mx_transposed(_p(h), rows, cols, act, fmt, _p(bf16_out), _p(fp8_t_out),
+                                        _p(scale_t_out), _stream(stream)),
+           "quantize_mx_transposed")
 
 
 def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor, fb: int,

@@ -101,6 +101,31 @@ __device__ __forceinline__ void quant_one(uint16_t h, float s, uint16_t& b, uint
   sat += saturates<FMT>(v);
 }
 
+// ------------------------------------------------------------------ MXFP8
+// "FP8 training: what it is and how it works", Trade-offs and edge cases: the
+// microscaling recipe scales each block of 32 adjacent values by its own
+// power of two.  Block exponent k (decode scale 2^k, stored as the E8M0 byte
+// k + 127): the smallest k in [-127, 127] with |b| <= max * 2^k for every
+// element of the block.  From the block's largest BF16 magnitude pattern m
+// (sign cleared; NaN patterns order above infinity): for a normal m = 1.f 2^e
+// and max = 1.75 * 2^emax, k = e - emax, plus one when the fraction exceeds
+// 0.75 (7-bit field above 0x60); zero and subnormal BF16 values lie below
+// max * 2^-127 (k = -127); infinity and NaN admit no k (k = 127).
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(uint32_t m) {
+  constexpr int emax = FMT == 0 ? 8 : 15;
+  const int ef = (int)(m >> 7);
+  if (ef >= 0xFF) return 127;
+  if (ef == 0) return -127;
+  const int k = ef - 127 - emax + ((m & 0x7Fu) > 0x60u ? 1 : 0);
+  return k < -127 ? -127 : k;
+}
+
+// 2^-k in binary32 (k = 127 gives the subnormal 2^-127).
+__device__ __forceinline__ float mx_multiplier(int k) {
+  return __uint_as_float(k == 127 ? 0x00400000u : (uint32_t)(127 - k) << 23);
+}
+
 // Block-wide reduction of (amax16, sat) and one atomic pair into a slot.
 // NT: threads of the block (a multiple of 64); every thread must call it.
 // sm: 2 NT / 64 words of LDS scratch.  Kernels that copy global memory

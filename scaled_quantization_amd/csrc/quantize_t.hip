@@ -126,9 +126,144 @@ static int dispatch_t(const uint16_t* h, int64_t rows, int64_t cols, uint16_t* b
   return launch_t<FMT, ACT, false>(h, rows, cols, bout, qout, qt, sp, slots, stream);
 }
 
+// ------------------------------------------------------------------ MXFP8, transposed
+// quantize_mx with the blocks of 32 running down the columns, its codes and
+// exponents written transposed: code^T [cols x rows], exponent^T [cols x
+// rows / 32].  "FP8 training: what it is and how it works", Trade-offs and
+// edge cases: one power of two per 32 adjacent values; a GEMM that contracts
+// along the token dimension (the weight gradient dW = dY^T X, and the weight
+// operand of dX = dY W, contracted along the output features) needs its
+// blocks along that dimension.  The exponent rule and the cast are
+// quantize_mx's (mx_exponent, cast8).
+//
+// Kernel: 256 threads own a 64-row x 128-column tile.  Thread t loads four
+// 8-value row vectors (rows t / 16 + 16 p, columns 8 (t % 16) ..), applies the
+// activation, stores the BF16 copy if asked, and writes the values to an LDS
+// tile of 65 dwords per row.  After a barrier thread t takes the column pair
+// 2 cp, 2 cp + 1 (cp = t / 4) over the 16 rows 16 rq .. (rq = t % 4): sixteen
+// dword reads (dword (16 rq + i) 65 + cp lands in bank 16 rq + cp + i: free of
+// conflicts across a wave, as are the row writes), byte permutes that split
+// them into the two columns' 16 values, the halves' maxima swapped with the
+// neighbour lane (t ^ 1 holds the other 16 rows of the block), then per
+// column one exponent, 16 codes and one 16-byte store: 4 lanes write a
+// 64-byte run of a transposed row.
+constexpr int kMxPitchW = 65;
+
+template <int FMT, int ACT, bool WBF16, bool HW>
+__global__ __launch_bounds__(256) void k_quant_mx_t(const uint16_t* __restrict__ h,
+                                                    uint16_t* __restrict__ bout,
+                                                    uint8_t* __restrict__ qt,
+                                                    uint8_t* __restrict__ et, int64_t rows,
+                                                    int64_t cols) {
+  __shared__ uint32_t tile[kTR * kMxPitchW];
+  const int64_t tiles_c = cols / kTC;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTR;
+  const int64_t c0 = (int64_t)(blockIdx.x % tiles_c) * kTC;
+  const int t = threadIdx.x;
+  const int rr = t >> 4, cc = t & 15;
+  uint4 x[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    x[p] = load_nt(reinterpret_cast<const uint4*>(h + (r0 + rr + 16 * p) * cols + c0 + 8 * cc));
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t b[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = act_pair<ACT, HW>(b[j]);
+    if constexpr (WBF16)
+      store_nt(reinterpret_cast<uint4*>(bout + (r0 + rr + 16 * p) * cols + c0 + 8 * cc), b[0],
+               b[1], b[2], b[3]);
+    uint32_t* dst = tile + (rr + 16 * p) * kMxPitchW + 4 * cc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = b[j];
+  }
+  __syncthreads();
+
+  const int rq = t & 3, cp = t >> 2;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = tile[(16 * rq + i) * kMxPitchW + cp];
+  // column 2 cp: the low BF16 halves, rows 2 k and 2 k + 1 in dword k; column
+  // 2 cp + 1: the high halves
+  uint32_t col[2][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    col[0][k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x05040100u);
+    col[1][k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07060302u);
+  }
+  const int64_t nb = rows / 32;
+  uint32_t sat = 0;   // nothing finite saturates under the block rule; unused
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t m0 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(col[c]);
+    const uint32_t m1 = vec_absmax16<ACT == FP8DP_ACT_IDENTITY>(col[c] + 4);
+    uint32_t bm = m0 > m1 ? m0 : m1;
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bm, 0xB1, 0xF, 0xF, false);
+    bm = o > bm ? o : bm;
+    const int k = mx_exponent<FMT>(bm);
+    const float mult = mx_multiplier(k);
+    const uint2 q0 = cast8<FMT, HW>(col[c], m0, mult, sat);
+    const uint2 q1 = cast8<FMT, HW>(col[c] + 4, m1, mult, sat);
+    const int64_t dc = c0 + 2 * cp + c;
+    *reinterpret_cast<uint4*>(qt + dc * rows + r0 + 16 * rq) = make_uint4(q0.x, q0.y, q1.x, q1.y);
+    if ((rq & 1) == 0) et[dc * nb + r0 / 32 + rq / 2] = (uint8_t)(k + 127);
+  }
+}
+
+template <int FMT, int ACT, bool HW>
+static int launch_mx_t(const uint16_t* h, int64_t rows, int64_t cols, uint16_t* bout, uint8_t* qt,
+                       uint8_t* et, hipStream_t stream) {
+  const unsigned grid = (unsigned)((rows / kTR) * (cols / kTC));
+  if (bout)
+    hipLaunchKernelGGL((k_quant_mx_t<FMT, ACT, true, HW>), dim3(grid), dim3(256), 0, stream, h,
+                       bout, qt, et, rows, cols);
+  else
+    hipLaunchKernelGGL((k_quant_mx_t<FMT, ACT, false, HW>), dim3(grid), dim3(256), 0, stream, h,
+                       bout, qt, et, rows, cols);
+  return check_launch("quantize_mx_transposed");
+}
+
+template <int FMT, int ACT>
+static int dispatch_mx_t(const uint16_t* h, int64_t rows, int64_t cols, uint16_t* bout,
+                         uint8_t* qt, uint8_t* et, hipStream_t stream) {
+  if (codec() == 0) return launch_mx_t<FMT, ACT, true>(h, rows, cols, bout, qt, et, stream);
+  return launch_mx_t<FMT, ACT, false>(h, rows, cols, bout, qt, et, stream);
+}
+
 }  // namespace fp8dp
 
 using namespace fp8dp;
+
+extern "C" int quantize_mx_transposed(const uint16_t* h, int64_t rows, int64_t cols, fp8dp_act act,
+                                      fp8dp_format fmt, uint16_t* bf16_out, uint8_t* fp8_t_out,
+                                      uint8_t* scale_t_out, hipStream_t stream) {
+  if (h == nullptr || fp8_t_out == nullptr || scale_t_out == nullptr) {
+    set_error("quantize_mx_transposed: h, fp8_t_out and scale_t_out must be non-NULL");
+    return FP8DP_EINVAL;
+  }
+  if (rows < kTR || cols < kTC || rows % kTR || cols % kTC || rows > ((int64_t)1 << 31) ||
+      cols > ((int64_t)1 << 31) || (rows / kTR) * (cols / kTC) > (int64_t)0x7FFFFFFF) {
+    set_error("quantize_mx_transposed: rows must be a positive multiple of 64 and cols of 128 "
+              "(got %lld x %lld)", (long long)rows, (long long)cols);
+    return FP8DP_EINVAL;
+  }
+  if ((fmt != FP8DP_E4M3 && fmt != FP8DP_E5M2) ||
+      (act != FP8DP_ACT_IDENTITY && act != FP8DP_ACT_RELU2)) {
+    set_error("quantize_mx_transposed: unknown format %d or activation %d", (int)fmt, (int)act);
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(h) || !aligned16(bf16_out) || !aligned16(fp8_t_out)) {
+    set_error("quantize_mx_transposed: h, bf16_out and fp8_t_out must be 16-byte aligned");
+    return FP8DP_EINVAL;
+  }
+  if (fmt == FP8DP_E4M3)
+    return act == FP8DP_ACT_RELU2
+               ? dispatch_mx_t<0, 1>(h, rows, cols, bf16_out, fp8_t_out, scale_t_out, stream)
+               : dispatch_mx_t<0, 0>(h, rows, cols, bf16_out, fp8_t_out, scale_t_out, stream);
+  return act == FP8DP_ACT_RELU2
+             ? dispatch_mx_t<1, 1>(h, rows, cols, bf16_out, fp8_t_out, scale_t_out, stream)
+             : dispatch_mx_t<1, 0>(h, rows, cols, bf16_out, fp8_t_out, scale_t_out, stream);
+}
 
 extern "C" int quantize_fused_transposed(const uint16_t* h, int64_t rows, int64_t cols,
                                          fp8dp_act act, fp8dp_format fmt,
