@@ -416,6 +416,26 @@ int fp8_gemm_mx(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale, const
                 fp8dp_format fb, const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
                 fp8dp_accum accum, uint16_t* y, hipStream_t stream);
 
+/* fp8_gemm_mx with K split over `splits` workgroups per output tile, for the
+ * shapes whose output has too few tiles to fill the GPU: the MX weight
+ * gradient dW [N x K] = dY^T X contracts along the tokens ("FP8 Training &
+ * Inference", FP8 Training Recipe; blocks along the tokens from
+ * quantize_mx_transposed).  Split s sums the 128-wide K blocks
+ * floor(s KS / splits) .. floor((s + 1) KS / splits) - 1 (KS = K / 128) into
+ * FP32 partials in workspace (at least splits * M * N floats, caller-owned,
+ * 16-byte aligned), with the block scales already applied; a second kernel
+ * adds the partials in split order and rounds to BF16 (deterministic).  The
+ * accumulation modes are fp8_gemm_mx's (exact mode: each split folds the
+ * block exponents of its own range); one split gives fp8_gemm_mx's output
+ * bit for bit.
+ * Errors: those of fp8_gemm_scaled_splitk (shapes: M a positive multiple of
+ * 256, N and K of 128, K >= 128 * splits, 1 <= splits <= 64), plus NULL or
+ * misaligned (4 bytes) exponent arrays. */
+int fp8_gemm_mx_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale,
+                       const uint8_t* b, fp8dp_format fb, const uint8_t* b_scale, int64_t M,
+                       int64_t N, int64_t K, int32_t splits, fp8dp_accum accum, float* workspace,
+                       uint16_t* y, hipStream_t stream);
+
 /* Weight cast with current scaling ("FP8 training ...", Step 4: the 8-bit
  * copies are cast from the master weights at every step; Trade-offs: 128 x
  * 128 weight blocks).  w [N x K] BF16 -> w8 [N x K] codes.

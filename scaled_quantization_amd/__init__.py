@@ -10,7 +10,7 @@ Entry points (same names as the C ABI):
     fp8dp_state_init, quantize_fused, amax_history_update, quantize_fused_update,
     fp8_gemm_scaled, quantize_weight, gemm_bf16_quantize_fused, fp8_gemm_scaled_splitk,
     fp8_gemm_scaled_splitk_noalloc, fp8_transpose, quantize_fused_transposed,
-    quantize_mx, quantize_mx_transposed, fp8_gemm_mx, and the
+    quantize_mx, quantize_mx_transposed, fp8_gemm_mx, fp8_gemm_mx_splitk, and the
     comparison / diagnostic calls fp8dp_bench_*, fp8dp_convert_f32, fp8dp_scale_rule,
     fp8dp_set_grid_limit, fp8dp_set_codec.
 """
@@ -57,6 +57,8 @@ _SIGS = {
     "quantize_fused_transposed": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
                                   ctypes.c_int),
     "quantize_mx_transposed": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "fp8_gemm_mx_splitk": ([_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
+                            _vp, _vp], ctypes.c_int),
     "relu2_backward_quantize": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
                                 ctypes.c_int),
     "fp8_gemm_relu2_backward": ([_vp, _i32, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
@@ -449,6 +451,22 @@ def fp8_gemm_mx(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor
             raise Fp8dpError(f"fp8_gemm_mx: {name} needs {rows * K // 32} uint8 exponents")
     _check(lib().fp8_gemm_mx(_p(a), fa, _p(a_scale), _p(b), fb, _p(b_scale), M, N, K, accum,
                              _p(y), _stream(stream)), "fp8_gemm_mx")
+
+
+def fp8_gemm_mx_splitk(a: torch.Tensor, fa: int, a_scale: torch.Tensor, b: torch.Tensor,
+                       fb: int, b_scale: torch.Tensor, splits: int, workspace: torch.Tensor,
+                       y: torch.Tensor, accum: int = ACCUM_EXACT, stream=None) -> None:
+    """fp8_gemm_mx with K split `splits` ways; workspace: float32 device tensor of
+    at least splits * M * N elements."""
+    M, N, K = _gemm_operands("fp8_gemm_mx_splitk", a, b, y)
+    for name, e, rows in (("a_scale", a_scale, M), ("b_scale", b_scale, N)):
+        if e.element_size() != 1 or e.numel() * 32 != rows * K:
+            raise Fp8dpError(f"fp8_gemm_mx_splitk: {name} needs {rows * K // 32} uint8 exponents")
+    if workspace.dtype != torch.float32 or workspace.numel() < splits * M * N:
+        raise Fp8dpError("fp8_gemm_mx_splitk: workspace needs splits * M * N float32")
+    _check(lib().fp8_gemm_mx_splitk(_p(a), fa, _p(a_scale), _p(b), fb, _p(b_scale), M, N, K,
+                                    splits, accum, _p(workspace), _p(y), _stream(stream)),
+           "fp8_gemm_mx_splitk")
 
 
 def quantize_weight(w: torch.Tensor, fmt: int, mode: int, w8: torch.Tensor, scale_out: Ptr,

@@ -39,13 +39,14 @@ static int launch_bwd_accum(const uint8_t* a, const uint8_t* b, int64_t M, int64
   return launch_bwd_tile<BC, BF, false>(a, b, M, N, K, sa, sb, bwd, stream);
 }
 
-// y[m, n] = bf16_rne((sum over s in order of ws[s][m][n]) * sa[0] * sb[0]):
-// 8 consecutive elements per thread per iteration, grid-stride.
+// y[m, n] = bf16_rne((sum over s in order of ws[s][m][n]) * sa[0] * sb[0]), or
+// without the scale product when sa is NULL (MX partials carry their block
+// scales): 8 consecutive elements per thread per iteration, grid-stride.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits,
                                                        int64_t mn, const float* __restrict__ sa,
                                                        const float* __restrict__ sb,
                                                        uint16_t* __restrict__ y) {
-  const float f = sa[0] * sb[0];
+  const float f = sa != nullptr ? sa[0] * sb[0] : 1.0f;
   const int64_t stride = (int64_t)gridDim.x * 256 * 8;
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < mn; i += stride) {
     float v[8];
@@ -89,6 +90,19 @@ static int launch_split_tile(const uint8_t* a, const uint8_t* b, int64_t M, int6
     return launch_split<FA, FB, decltype(T)::value, EX>(a, b, M, N, K, splits, sa, sb, ws, y,
                                                          stream);
   });
+}
+
+template <int FA, int FB, int TN, bool EX>
+static int launch_mx_split(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
+                           const uint8_t* eb, int64_t M, int64_t N, int64_t K, int splits,
+                           float* ws, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL((k_gemm_big<FA, FB, TN, true, true, false, -1, 1, 1, false, false, EX>),
+                     dim3((unsigned)((M / 256) * (N / (64 * TN)) * splits)), dim3(512), 0, stream,
+                     a, b, (int)M, (int)N, (int)K, nullptr, nullptr, y, ws, splits, ea, eb);
+  if (check_launch("fp8_gemm_mx_splitk")) return FP8DP_EHIP;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3(grid_for(M * N / 8, 256, 8)), dim3(256), 0, stream, ws,
+                     splits, M * N, nullptr, nullptr, y);
+  return check_launch("fp8_gemm_mx_splitk");
 }
 
 }  // namespace fp8dp
@@ -273,4 +287,36 @@ extern "C" int fp8_gemm_relu2_backward(const uint8_t* a, fp8dp_format fa, const 
                              : launch_bwd_accum<0, 0>(a, b, M, N, K, sa, sb, bwd, accum, stream);
   return fmt == FP8DP_E5M2 ? launch_bwd_accum<1, 1>(a, b, M, N, K, sa, sb, bwd, accum, stream)
                            : launch_bwd_accum<1, 0>(a, b, M, N, K, sa, sb, bwd, accum, stream);
+}
+
+extern "C" int fp8_gemm_mx_splitk(const uint8_t* a, fp8dp_format fa, const uint8_t* a_scale,
+                                  const uint8_t* b, fp8dp_format fb, const uint8_t* b_scale,
+                                  int64_t M, int64_t N, int64_t K, int32_t splits,
+                                  fp8dp_accum accum, float* workspace, uint16_t* y,
+                                  hipStream_t stream) {
+  if (a_scale == nullptr || b_scale == nullptr || workspace == nullptr) {
+    set_error("fp8_gemm_mx_splitk: NULL pointer argument");
+    return FP8DP_EINVAL;
+  }
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(a_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(b_scale) & 3u)) {
+    set_error("fp8_gemm_mx_splitk: workspace must be 16-byte aligned, block exponents 4-byte "
+              "aligned");
+    return FP8DP_EINVAL;
+  }
+  // the same shape, format and alignment rules as fp8_gemm_scaled_splitk (the
+  // scale arguments there are checked for NULL only: pass the exponents)
+  const int rc = check_splitk("fp8_gemm_mx_splitk", a, fa, b, fb, M, N, K, splits, accum,
+                              reinterpret_cast<const float*>(a_scale),
+                              reinterpret_cast<const float*>(b_scale), y);
+  if (rc != FP8DP_OK) return rc;
+  return dispatch_formats(fa, fb, accum, [&](auto A, auto B, auto X) {
+    constexpr int FA = decltype(A)::value, FB = decltype(B)::value;
+    constexpr bool EX = decltype(X)::value;
+    if (N % 192 == 0)
+      return launch_mx_split<FA, FB, 3, EX>(a, a_scale, b, b_scale, M, N, K, splits, workspace, y,
+                                            stream);
+    return launch_mx_split<FA, FB, 2, EX>(a, a_scale, b, b_scale, M, N, K, splits, workspace, y,
+                                          stream);
+  });
 }

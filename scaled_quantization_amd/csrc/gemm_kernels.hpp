@@ -391,7 +391,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
                                                      const uint8_t* __restrict__ eb = nullptr,
                                                      const uint32_t* __restrict__ run_flag = nullptr,
                                                      Relu2Bwd bwd = {}) {
-  static_assert(!(MX && SPLIT), "microscaled split-K is not provided");
   static_assert(BC < 0 || !(MX || SPLIT), "the backward epilogue follows the per-tensor GEMM");
   static_assert(!(EX && MX) || TN <= 3, "exact microscaled accumulation: 256 x 128 or 256 x 192 tiles");
   if constexpr (COND) {
@@ -407,6 +406,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   constexpr int BM = 256, BN = 64 * TN, TM = 2;
   constexpr int ASZ = BM * kBK, TILES = (BM + BN) * kBK;   // bytes of A / of both tiles
   static_assert(XG == 1 || ((MX || PG) && XG == 4), "exponents come 1 or 4 stages per copy");
+  static_assert(!(MX && SPLIT) || XG == 1, "split-K ranges need not be whole 4-stage exponent copies");
   static_assert(!PG || ((TN == 2 || TN == 3) && XG == 4 && !MX && !SPLIT && BC < 0),
                 "per-group scales: 256 x 128 or 256 x 192 tiles, scales through the ring");
   static_assert(!PER || (!MX && !PG && !SPLIT && !COND && BC < 0),
@@ -685,13 +685,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   uint8_t* const sR = lds + 2 * SLOT + 2 * XSZ;
   int ref_a[MX && EX ? TM : 1] = {}, ref_b[MX && EX ? TN : 1] = {};
   bool mx_slow = false;
+  // the 32-wide blocks this workgroup sums: all of K, or its split's range
+  const int kb0 = (int)(kbase / 32), nkb = KT * (kBK / 32);
   if constexpr (MX && EX) {
     const int t = threadIdx.x, KB = K / 32;
-    const uint8_t* e = t < 256 ? ea + (size_t)(m0 + t) * KB
-                               : (t - 256 < BN ? eb + (size_t)(n0 + t - 256) * KB : nullptr);
+    const uint8_t* e = t < 256 ? ea + (size_t)(m0 + t) * KB + kb0
+                               : (t - 256 < BN ? eb + (size_t)(n0 + t - 256) * KB + kb0 : nullptr);
     uint32_t emax = 0, emin = 255;
     if (e != nullptr) {
-      for (int k = 0; k < KB; k += 4) {
+      for (int k = 0; k < nkb; k += 4) {
         const uint32_t d = *reinterpret_cast<const uint32_t*>(e + k);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -771,6 +773,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
         }
   };
 
+  // SPLIT: the unscaled FP32 partial sums of this split (lanes 0-31 of a
+  // store cover 32 consecutive columns); folded MX sums are scaled back first,
+  // so every split's partials are in the same units
+  auto split_store = [&]() {
+    float* out = ws + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lrow = wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          float v = acc[i][j][r];
+          if constexpr (MX && EX) {
+            if (!mx_slow)
+              v = __builtin_ldexpf(v, (int)sR[lrow] + ref_b[j] - 254 - kMxFoldBias<FA> -
+                                          kMxFoldBias<FB>);
+          }
+          out[(size_t)(m0 + lrow) * N + n0 + wc + j * 32 + (lane & 31)] = v;
+        }
+  };
+
   if constexpr (MX && EX) {
     if (mx_slow) {
       // Unfolded fallback, exact for any exponents: each wave sums every
@@ -779,7 +803,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       // accumulator scaled by 2^(e_a + e_b - 254) -- the promotion per block
       // of the per-group path with microscaling's block size.
       const int KB = K / 32;
-      for (int blk = 0; blk < KB; ++blk) {
+      for (int blk = kb0; blk < kb0 + nkb; ++blk) {
         v8h_t ha[2][TM];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
@@ -821,7 +845,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
             }
         }
       }
-      epi_plain(m0, n0, false);
+      if constexpr (SPLIT)
+        split_store();
+      else
+        epi_plain(m0, n0, false);
       return;
     }
   }
@@ -1095,17 +1122,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
   if constexpr (PER) return;
 
   if constexpr (SPLIT) {
-    // FP32 partial sums: lanes 0-31 of a store cover 32 consecutive columns
-    float* out = ws + (size_t)split * M * N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wr + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          out[(size_t)row * N + n0 + wc + j * 32 + (lane & 31)] = acc[i][j][r];
-        }
+    split_store();
     return;
   }
 

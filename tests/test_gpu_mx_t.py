@@ -156,3 +156,90 @@ def test_transposed_mx_argument_errors():
     h = torch.zeros((64, 128), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(sq.Fp8dpError, match="cols x rows"):
         sq.quantize_mx_transposed(h, sq.ACT_RELU2, sq.E4M3, qt, et)
+
+
+# ------------------------------------------------------------------ MX split-K
+def _mx_operands(rng, M, N, K, fa, fb, spread):
+    """Codes and exponents of two spread operands via the oracle's MX cast."""
+    def one(rows, fmt):
+        x = rng.standard_normal((rows, K)).astype(np.float32)
+        x *= np.exp2(rng.integers(-spread, spread + 1, (rows, K // 32, 1)).astype(np.float32)).repeat(
+            32, axis=2).reshape(rows, K)
+        h = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        r = O.quantize_mx(h, O.ACT_IDENTITY, fmt, want_bf16=False)
+        return r.fp8, r.scale
+    a8, ea = one(M, fa)
+    b8, eb = one(N, fb)
+    return a8, ea, b8, eb
+
+
+def _mx_split(a8, fa, ea, b8, fb, eb, splits, accum):
+    M, N = a8.shape[0], b8.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(splits * M * N, dtype=torch.float32, device=DEV)
+    sq.fp8_gemm_mx_splitk(to_dev_u8(a8), fa, to_dev_u8(ea), to_dev_u8(b8), fb, to_dev_u8(eb),
+                          splits, ws, y, accum)
+    return y
+
+
+@BOTH
+@pytest.mark.parametrize("N", [256, 384])
+def test_mx_splitk_one_split_equals_mx_gemm(N, accum):
+    rng = np.random.default_rng(31 + N)
+    a8, ea, b8, eb = _mx_operands(rng, 512, N, 1024, 1, 0, 6)
+    y1 = _mx_split(a8, 1, ea, b8, 0, eb, 1, accum)
+    y0 = torch.empty_like(y1)
+    sq.fp8_gemm_mx(to_dev_u8(a8), 1, to_dev_u8(ea), to_dev_u8(b8), 0, to_dev_u8(eb), y0, accum)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+
+
+# uneven split ranges, fold-only (spread 3) and fallback tiles (spread 14) in
+# exact mode, every format pair
+@BOTH
+@pytest.mark.parametrize("M,N,K,fa,fb,splits,spread", [(256, 384, 2048, 1, 0, 3, 3),
+                                                       (512, 256, 4096, 1, 0, 5, 14),
+                                                       (256, 128, 1280, 0, 0, 7, 6),
+                                                       (256, 384, 1536, 0, 1, 4, 3),
+                                                       (256, 256, 1024, 1, 1, 8, 3)])
+def test_mx_splitk_vs_oracle(M, N, K, fa, fb, splits, spread, accum):
+    rng = np.random.default_rng(M + N + K + splits + spread)
+    a8, ea, b8, eb = _mx_operands(rng, M, N, K, fa, fb, spread)
+    y = _mx_split(a8, fa, ea, b8, fb, eb, splits, accum).float().cpu().numpy()
+    ref, absref = O.gemm_mx_f64(a8, fa, ea, b8, fb, eb)
+    check_gemm(y, ref, absref, f"mx split {splits}", accum == EXACT,
+               lambda sel: fp8_mfma_allowance_mx(a8, fa, ea, b8, fb, eb, sel))
+
+
+@BOTH
+def test_mx_wgrad_gpt2(accum):
+    """dW [768 x 3072] = dY^T A in MXFP8 at the GPT-2 shape: dY^T and A^T =
+    relu2(H)^T from quantize_mx_transposed (blocks along the 16384 tokens),
+    K = 16384 split 5 ways, sampled rows against the oracle."""
+    w = workloads.get("gpt2")
+    dy, h = w.dy(), w.h0()
+    _, q_dyt, e_dyt = _run_t(dy, sq.ACT_IDENTITY, sq.E5M2, want_bf16=False)
+    _, q_at, e_at = _run_t(h, sq.ACT_RELU2, sq.E4M3, want_bf16=False)
+    N, M = q_dyt.shape
+    K = q_at.shape[0]
+    y = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(5 * N * K, dtype=torch.float32, device=DEV)
+    sq.fp8_gemm_mx_splitk(q_dyt, sq.E5M2, e_dyt, q_at, sq.E4M3, e_at, 5, ws, y, accum)
+    rows = np.sort(np.random.default_rng(37).choice(N, size=24, replace=False))
+    ra = O.quantize_mx(np.ascontiguousarray(dy.T[rows]), O.ACT_IDENTITY, O.E5M2, want_bf16=False)
+    rb = _oracle_t(h, O.ACT_RELU2, O.E4M3)
+    assert np.array_equal(u8_np(q_dyt)[rows], ra.fp8) and np.array_equal(u8_np(e_dyt)[rows], ra.scale)
+    assert np.array_equal(u8_np(q_at), rb.fp8) and np.array_equal(u8_np(e_at), rb.scale)
+    ref, absref = O.gemm_mx_f64(ra.fp8, O.E5M2, ra.scale, rb.fp8, O.E4M3, rb.scale)
+    check_gemm(y.float().cpu().numpy()[rows], ref, absref, "mx wgrad", accum == EXACT,
+               lambda sel: fp8_mfma_allowance_mx(ra.fp8, 1, ra.scale, rb.fp8, 0, rb.scale, sel))
+
+
+def test_mx_splitk_argument_errors():
+    a = torch.zeros((256, 512), dtype=torch.uint8, device=DEV)
+    e = torch.zeros((256, 16), dtype=torch.uint8, device=DEV)
+    y = torch.empty((256, 256), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(4 * 256 * 256, dtype=torch.float32, device=DEV)
+    with pytest.raises(sq.Fp8dpError, match="splits"):
+        sq.fp8_gemm_mx_splitk(a, 0, e, a, 0, e, 5, ws, y)      # K < 128 * splits
+    with pytest.raises(sq.Fp8dpError, match="workspace"):
+        sq.fp8_gemm_mx_splitk(a, 0, e, a, 0, e, 4, ws[:10], y)
