@@ -312,7 +312,7 @@ def main():
     out["fused_up_projection"] = fused_up(sq, torch, np, w, A16, A8, dev, args)
     out["backward_gemms"] = backward(sq, torch, w, A8, w8, wsc, st_a, DY8, st_g, dev, args,
                                      H, A16, DY)
-    out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
+    out["mxfp8"] = mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean, DY)
     out["per_group_128"] = per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["fp8_cached_activation"] = fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args,
                                               q_mean)
@@ -586,7 +586,7 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args, H, A16, DY):
     return res
 
 
-def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
+def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms, DY):
     """The microscaled variant of the step's forward half: quantize_mx of the
     activation (relu2, BF16 copy, E4M3 codes + one E8M0 exponent per 32
     values), quantize_mx of the weight, and the MX GEMM that applies the block
@@ -632,7 +632,62 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)},
             "fp8_gemm_mx_mfma_fp8": {"ms": round(g8, 5), "TFLOP/s": round(tf8, 1),
-                                     "frac_of_fp8_peak": round(tf8 / FP8_PEAK_TFLOPS, 4)}}
+                                     "frac_of_fp8_peak": round(tf8 / FP8_PEAK_TFLOPS, 4)},
+            "backward": mx_backward(sq, torch, w, H, A8, wt, DY, dev, args)}
+
+
+def mx_backward(sq, torch, w, H, A8, wt, DY, dev, args):
+    """The MXFP8 backward of the down-projection: the casts whose blocks run
+    down the columns (quantize_mx_transposed: relu2(H)^T and dY^T with their
+    blocks along the tokens, W^T along the output features), the input
+    gradient dA = dY W (fp8_gemm_mx, E5M2 x E4M3 on dY's row-wise MX codes and
+    W^T's) and the weight gradient dW = dY^T A (fp8_gemm_mx_splitk, K = the
+    16384 tokens), exact accumulation.  Each kernel timed like the large
+    configuration's (8 ms of its own launches, then the median of 5 bursts)."""
+    M, K, N = w.M, w.K, w.N
+    stream = torch.cuda.current_stream()
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    at, eat = u8(K, M), u8(K, M // 32)
+    dyt, edyt = u8(N, M), u8(N, M // 32)
+    dy8, edy = u8(M, N), u8(M, N // 32)
+    wt8, ewt = u8(K, N), u8(K, N // 32)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    i = [0]
+
+    def rot(fn):
+        def f():
+            fn(i[0])
+            i[0] += 1
+        return f
+
+    timed = lambda fn, per: burst_median(torch, stream, fn, per)
+    ca = timed(rot(lambda j: sq.quantize_mx_transposed(H[j % len(H)], sq.ACT_RELU2, sq.E4M3, at,
+                                                      eat)), 16)
+    cg = timed(rot(lambda j: sq.quantize_mx_transposed(DY[j % len(DY)], sq.ACT_IDENTITY,
+                                                      sq.E5M2, dyt, edyt)), 32)
+    sq.quantize_mx(DY[0], sq.ACT_IDENTITY, sq.E5M2, dy8, edy)
+    sq.quantize_mx_transposed(wt, sq.ACT_IDENTITY, sq.E4M3, wt8, ewt)
+    dg = timed(lambda: sq.fp8_gemm_mx(dy8, sq.E5M2, edy, wt8, sq.E4M3, ewt, dx, sq.ACCUM_EXACT), 8)
+    fl = 2.0 * M * N * K
+    tf = lambda ms: fl / (ms * 1e-3) / 1e12
+    out = {"cast_transposed_activation": {
+               "shape": f"H[{M}x{K}] relu2 -> e4m3^T [{K}x{M}] + E8M0 per 32 tokens",
+               "ms": round(ca, 5), "GB/s": round((3 * M * K + M * K // 32) / (ca * 1e-3) / 1e9, 1)},
+           "cast_transposed_gradient": {
+               "shape": f"dY[{M}x{N}] -> e5m2^T [{N}x{M}] + E8M0 per 32 tokens",
+               "ms": round(cg, 5), "GB/s": round((3 * M * N + M * N // 32) / (cg * 1e-3) / 1e9, 1)},
+           "dgrad": {"shape": f"dY8[{M}x{N}] e5m2 x (W^T)8[{K}x{N}] e4m3 -> [{M}x{K}], MX blocks along {N}",
+                     "ms": round(dg, 5), "TFLOP/s": round(tf(dg), 1),
+                     "frac_of_fp16_mfma_peak": round(tf(dg) / FP16_PEAK_TFLOPS, 4)},
+           "wgrad": {"shape": f"(dY^T)8[{N}x{M}] e5m2 x (A^T)8[{K}x{M}] e4m3 -> [{N}x{K}], MX blocks along the tokens"}}
+    for splits in (4, 5, 8):
+        ws = torch.empty(splits * N * K, dtype=torch.float32, device=dev)
+        ms = timed(lambda: sq.fp8_gemm_mx_splitk(dyt, sq.E5M2, edyt, at, sq.E4M3, eat, splits, ws,
+                                                 dw, sq.ACCUM_EXACT), 8)
+        out["wgrad"][f"splits_{splits}"] = {"ms": round(ms, 5), "TFLOP/s": round(tf(ms), 1)}
+        del ws
+    return out
 
 
 def per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms):

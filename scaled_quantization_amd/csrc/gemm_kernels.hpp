@@ -36,6 +36,8 @@ namespace fp8dp {
 
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 
 // Widens the 32 FP8 codes of an MFMA fragment into four groups of 8 FP16
 // values (exact: every E4M3 and E5M2 value is an FP16 value); group j holds
@@ -111,14 +113,41 @@ __device__ __forceinline__ v8h_t widen8s(const v8i_t& x, float scale) {
                                  7);
 }
 
+// The same 8 codes times a power of two `scale`, widened to BF16 with the
+// hardware convert: every code times 2^k is a BF16 value while it stays in
+// BF16's normal range (measured: all 256 codes of both formats, k = -100 ..
+// 100, bit for bit), which the microscaled exact GEMM ensures.
+template <int F, int Q>
+__device__ __forceinline__ v8bf_t widen8s_bf(const v8i_t& x, float scale) {
+  const uint32_t d0 = (uint32_t)x[2 * Q], d1 = (uint32_t)x[2 * Q + 1];
+  v2bf_t p0, p1, p2, p3;
+  if constexpr (F == 1) {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, scale, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, scale, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, scale, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, scale, true);
+  } else {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
+  }
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6,
+                                 7);
+}
+
 // Microscaled exact accumulation: each operand row's block exponents are
-// folded into its FP16 widening relative to the row's largest one, value *
-// 2^(e_block - e_rowmax + kMxFoldBias).  The largest block then reaches
-// 448 * 2^7 = 57344 (E4M3) or 57344 (E5M2), below FP16's 65504, and a block
-// stays exact down to e_rowmax - kMxSpan: the smallest subnormal code (2^-9
-// E4M3, 2^-16 E5M2) lands on FP16's grid (2^-24).
-template <int F> constexpr int kMxFoldBias = F == 0 ? 7 : 0;
-template <int F> constexpr int kMxSpan = F == 0 ? 22 : 8;
+// folded into its BF16 widening relative to the row's largest one, value *
+// 2^(e_block - e_rowmax + kMxFoldBias), and summed by the BF16 instruction
+// (every code is a BF16 value; products of two have at most 8 significant
+// bits, exact in FP32).  The largest block stays below 2^48 (448 * 2^39,
+// 57344 * 2^32), so products stay below 2^96 and sums of up to 2^30 of them
+// below 2^126; a block down to e_rowmax - kMxSpan keeps its smallest nonzero
+// code at 2^-60 (E4M3: 2^(-9 + 39 - 90)) or 2^-62 (E5M2: 2^(-16 + 32 - 78)),
+// so every product of two is at least 2^-122, a normal FP32 value.
+template <int F> constexpr int kMxFoldBias = F == 0 ? 39 : 32;
+template <int F> constexpr int kMxSpan = F == 0 ? 90 : 78;
 
 constexpr int kBM = 128, kBN = 128;
 constexpr int kGemmThreads = 256;
@@ -989,25 +1018,34 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     // (exact MX at 256 x 192 widens each slice just before its MFMAs: the
     // double-buffered widening's registers would spill beside the exponents)
     constexpr bool EXP = EX && !PG && !(MX && TN == 3);
-    v8h_t wa[EXP ? TM : 1], wb[EXP ? TN : 1];
+    // the widened operands: FP16 (per tensor) or BF16 (microscaled: the
+    // folded block exponents need its range)
+    using WV = std::conditional_t<MX, v8bf_t, v8h_t>;
+    auto mfma_w = [](const WV& a, const WV& b, const v16f_t& c) {
+      if constexpr (MX)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    };
+    WV wa[EXP ? TM : 1], wb[EXP ? TN : 1];
     // MX: slice q of substep h holds block 2 h + q / 2 of the stage (the
     // lane's bytes 0-15 are the first block's, 16-31 the second's); its codes
     // are widened times 2^(e_block - e_rowmax + kMxFoldBias), e_block from
     // the row's stage dword
     auto widen_slice = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa,
-                           const uint32_t* xb, int h, auto Q, v8h_t* oa, v8h_t* ob) {
+                           const uint32_t* xb, int h, auto Q, WV* oa, WV* ob) {
       constexpr int q = decltype(Q)::value;
       if constexpr (MX) {
         const int sh = 8 * (2 * h + q / 2);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int e = (int)((xa[i] >> sh) & 0xFFu) - ref_a[i] + kMxFoldBias<FA> + 127;
-          oa[i] = widen8s<FA, q>(fa[i], __uint_as_float((uint32_t)e << 23));
+          oa[i] = widen8s_bf<FA, q>(fa[i], __uint_as_float((uint32_t)e << 23));
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int e = (int)((xb[j] >> sh) & 0xFFu) - ref_b[j] + kMxFoldBias<FB> + 127;
-          ob[j] = widen8s<FB, q>(fb[j], __uint_as_float((uint32_t)e << 23));
+          ob[j] = widen8s_bf<FB, q>(fb[j], __uint_as_float((uint32_t)e << 23));
         }
       } else {
 #pragma unroll
@@ -1019,13 +1057,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
     auto mfmas_mx_direct = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa,
                                const uint32_t* xb, int h) {
       static_for<4>([&](auto Q) {
-        v8h_t ha[TM], hb[TN];
+        WV ha[TM], hb[TN];
         widen_slice(fa, fb, xa, xb, h, Q, ha, hb);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma_w(ha[i], hb[j], acc[i][j]);
       });
     };
     auto mfmas_ex = [&](const v8i_t* fa, const v8i_t* fb, const uint32_t* xa, const uint32_t* xb,
@@ -1034,7 +1071,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
       if constexpr (EXP) {
         static_for<4>([&](auto Q) {
           constexpr int q = decltype(Q)::value;
-          v8h_t na[TM], nb[TN];
+          WV na[TM], nb[TN];
           if constexpr (q < 3)
             widen_slice(fa, fb, xa, xb, h, std::integral_constant<int, q + 1>{}, na, nb);
           else
@@ -1043,7 +1080,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_big(const uint8_t* __restrict__
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[i], wb[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = mfma_w(wa[i], wb[j], acc[i][j]);
 #pragma unroll
           for (int i = 0; i < TM; ++i) wa[i] = na[i];
 #pragma unroll

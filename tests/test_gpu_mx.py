@@ -6,7 +6,7 @@ power-of-two scale.  quantize_mx is compared bit for bit with oracle
 quantize_mx (BF16 copy, codes, E8M0 block exponents); fp8_gemm_mx with the
 oracle's float64 MX GEMM to |y - ref| <= 2^-8 |ref| + 1e-5 sum|a b| on every
 element in exact mode (the default), both where a tile's block exponents fold
-into the FP16 widening (rows spanning at most 22 binades, E4M3, or 8, E5M2)
+into the BF16 widening (rows spanning at most 90 binades, E4M3, or 78, E5M2)
 and where a tile takes the per-block fallback (wider spans; tiles of both
 kinds in one launch).  The microscaled FP8 instructions' mode is held to the
 same bound and reported as an expected failure where their truncation takes
@@ -187,15 +187,16 @@ def _span(e):
     return int((e.max(axis=1) - e.min(axis=1)).max())
 
 
-# block exponent spreads: lo..hi binades of the inputs; E4M3 rows of +-12
-# span more than 22 binades in some tiles (fallback) and the E5M2 ones more
-# than 8 (fallback everywhere), +-4 folds everywhere
+# block exponent spreads: lo..hi binades of the inputs; rows of +-12 or less
+# fold everywhere, rows of +-55 span more than 90 (E4M3) or 78 (E5M2) binades
+# in some tiles, which take the per-block fallback
 @BOTH
 @pytest.mark.parametrize("M,N,K,fa,fb,spread", [(256, 128, 128, 0, 0, 12), (256, 384, 1024, 0, 0, 12),
                                                 (512, 512, 512, 1, 0, 12), (256, 640, 256, 0, 1, 12),
                                                 (768, 768, 3072, 0, 0, 12), (256, 256, 384, 1, 1, 12),
                                                 (512, 384, 1024, 0, 0, 9), (256, 256, 1024, 1, 1, 3),
-                                                (256, 384, 512, 0, 1, 3)])
+                                                (256, 384, 512, 0, 1, 3), (256, 384, 1024, 0, 0, 55),
+                                                (512, 256, 512, 1, 0, 55), (256, 256, 384, 1, 1, 55)])
 def test_gemm_mx_vs_oracle(M, N, K, fa, fb, spread, accum):
     rng = np.random.default_rng(M + 3 * N + 7 * K + fa + 2 * fb + spread)
     a8, ea, b8, eb = _gemm_case(rng, M, N, K, fa, fb, -spread, spread)
@@ -213,18 +214,21 @@ def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb, N):
     """Rows 0-255 (the first row tile) and columns 0-191 keep their blocks
     within the fold span; one A row of the second row tile and one B row of
     the second column tile (256 x 128 tiles at N = 256, 256 x 192 at N = 384)
-    spread over 40 binades, so three of the four tiles take the per-block
+    spread over 110 binades, so three of the four tiles take the per-block
     fallback and one folds.  Every output meets the plain bound."""
     M, K = 512, 1024
     rng = np.random.default_rng(31 + fa + 2 * fb + N)
     narrow = {0: 9, 1: 3}
     ha = _spread(rng, M, K, -narrow[fa], narrow[fa])
     hb = _spread(rng, N, K, -narrow[fb], narrow[fb])
-    ha[300] = _spread(rng, 1, K, -20, 20)[0]
-    hb[200] = _spread(rng, 1, K, -20, 20)[0]
+    # the wide rows: blocks alternately near 2^-55 and 2^55 (a span of ~110)
+    wide = np.exp2(np.where(np.arange(K // 32) % 2 == 0, -55.0, 55.0)).repeat(32).astype(np.float32)
+    for h, r in ((ha, 300), (hb, 200)):
+        x = rng.standard_normal(K).astype(np.float32) * wide
+        h[r] = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     ra = O.quantize_mx(ha, O.ACT_IDENTITY, fa, want_bf16=False)
     rb = O.quantize_mx(hb, O.ACT_IDENTITY, fb, want_bf16=False)
-    span_a, span_b = {0: 22, 1: 8}[fa], {0: 22, 1: 8}[fb]
+    span_a, span_b = {0: 90, 1: 78}[fa], {0: 90, 1: 78}[fb]
     assert _span(ra.scale[:256]) <= span_a and _span(rb.scale[:192]) <= span_b
     assert _span(ra.scale[300:301]) > span_a and _span(rb.scale[200:201]) > span_b
     y = _gemm_mx_dev(ra.fp8, fa, ra.scale, rb.fp8, fb, rb.scale, EXACT)
@@ -233,16 +237,20 @@ def test_gemm_mx_exact_fold_and_fallback_tiles_in_one_launch(fa, fb, N):
     check_gemm(y[rows], ref, absref, f"mixed tiles {fa}{fb} N={N}")
 
 
-def test_gemm_mx_exact_full_range_codes():
-    """Every finite code equally likely and block exponents over the whole
-    quantizer range: the fallback meets the bound on every element."""
-    rng = np.random.default_rng(77)
+@pytest.mark.parametrize("a_lo", [-40, -100])
+def test_gemm_mx_exact_full_range_codes(a_lo):
+    """Every finite code equally likely; block exponents over -40 .. 40
+    binades (A's rows span under 90 and fold, B's up to 80 and some take the
+    per-block fallback), then A's over -100 .. 0 (every A row past 90: the
+    fallback everywhere), results within BF16's range: every element meets
+    the bound."""
+    rng = np.random.default_rng(77 - a_lo)
     M, N, K = 256, 256, 2048
     ta = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E4M3)))
     tb = np.flatnonzero(np.isfinite(O.fp8_decode_table(O.E5M2)))
     a8 = rng.choice(ta, size=(M, K)).astype(np.uint8)
     b8 = rng.choice(tb, size=(N, K)).astype(np.uint8)
-    ea = rng.integers(127 - 40, 127 + 40, (M, K // 32)).astype(np.uint8)
+    ea = rng.integers(127 + a_lo, 127 + (40 if a_lo == -40 else 0), (M, K // 32)).astype(np.uint8)
     eb = rng.integers(127 - 40, 127 + 40, (N, K // 32)).astype(np.uint8)
     y = _gemm_mx_dev(a8, O.E4M3, ea, b8, O.E5M2, eb, EXACT)
     ref, absref = O.gemm_mx_f64(a8, O.E4M3, ea, b8, O.E5M2, eb)

@@ -193,11 +193,11 @@ def test_mx_splitk_one_split_equals_mx_gemm(N, accum):
     assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
 
 
-# uneven split ranges, fold-only (spread 3) and fallback tiles (spread 14) in
-# exact mode, every format pair
+# uneven split ranges, fold-only (spreads 3, 6) and fallback tiles (spread 55)
+# in exact mode, every format pair
 @BOTH
 @pytest.mark.parametrize("M,N,K,fa,fb,splits,spread", [(256, 384, 2048, 1, 0, 3, 3),
-                                                       (512, 256, 4096, 1, 0, 5, 14),
+                                                       (512, 256, 4096, 1, 0, 5, 55),
                                                        (256, 128, 1280, 0, 0, 7, 6),
                                                        (256, 384, 1536, 0, 1, 4, 3),
                                                        (256, 256, 1024, 1, 1, 8, 3)])
