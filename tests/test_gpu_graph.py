@@ -93,3 +93,23 @@ def test_step_graph_replays_equal_eager_steps(name, fused):
         # eager work between replays
         torch.cuda.synchronize()
     assert g_bufs[8].read()["steps"] == 5
+
+
+def test_calls_enqueue_on_the_current_stream():
+    """The binding passes the current stream's raw handle: the default stream,
+    a stream made current by torch.cuda.stream, and the capture stream."""
+    assert sq._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert sq._stream(None) == s.cuda_stream != torch.cuda.default_stream().cuda_stream
+    assert sq._stream(None) == torch.cuda.default_stream().cuda_stream
+    src = torch.arange(64 * 128, device=DEV).to(torch.uint8).view(64, 128)
+    dst = torch.zeros((128, 64), dtype=torch.uint8, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sq.fp8_transpose(src, dst)
+    torch.cuda.synchronize()
+    assert not dst.any()                     # captured, not run
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src.t().contiguous())
