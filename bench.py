@@ -229,6 +229,7 @@ def main():
     g8_mean = burst(gemm_fp8, "fp8_gemm_scaled_mfma_fp8")
     dy_mean = burst(dy_cast)
     up_mean = burst(update_a)
+    up_graph = graph_burst(torch, stream, lambda: update_a(0), args.steps)
     # the other form of each cast, for comparison (the pair as the step runs it)
     q_fused_upd = burst(lambda i: sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3,
                                                            st_a, A16[i % n_out], A8[i % n_out]))
@@ -282,7 +283,8 @@ def main():
                                               "GB/s": round(dy_bytes / (dy_mean * 1e-3) / 1e9, 1),
                                               "bytes_per_launch": dy_bytes,
                                               "quantize_fused_then_update_ms": round(dy_pair, 5)},
-            "amax_history_update": {"ms": round(up_mean, 5)},
+            "amax_history_update": {"ms": round(up_mean, 5),
+                                    "graph_replay_ms": round(up_graph, 5)},
         },
         "gemm_roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
                           "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -497,7 +499,9 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args, H, A16, DY):
     codes: dA = dY W (E5M2 x E4M3, needs W8^T) and dW = dY^T A (split-K,
     needs dY8^T and A8^T), with the transposes they need; and the casts that
     write the transposed codes themselves (quantize_fused_transposed) against
-    the cast followed by the transpose."""
+    the cast followed by the transpose.  Each kernel timed like the large
+    configuration's (BURST_WARM_MS of its own launches, then the median of 5
+    bursts)."""
     M, K, N = w.M, w.K, w.N
     stream = torch.cuda.current_stream()
     w8t = torch.empty((K, N), dtype=torch.uint8, device=dev)
@@ -508,27 +512,44 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args, H, A16, DY):
     ws = torch.empty(16 * N * K, dtype=torch.float32, device=dev)
     si_g, si_a = st_g.field_ptr("scale_inv_used"), st_a.field_ptr("scale_inv_used")
 
-    def timed(fn, reps=None):
-        reps = reps or args.steps
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+    def timed(fn):
+        return burst_median(torch, stream, fn, args.steps)
 
-    t_w = timed(lambda: sq.fp8_transpose(w8, w8t))
-    t_dy = timed(lambda: sq.fp8_transpose(dy8, dyt))
-    t_a = timed(lambda: sq.fp8_transpose(A8[0], at))
+    # The transposes with their sources and destinations rotated through
+    # more than the 256 MB last-level cache, as the step's kernels are (the
+    # step's 8 A8 buffers; 16 copies of dY8, 64 of W8), launched back to back
+    # and replayed from a graph of one pass over the rotation (the dY8 and W8
+    # kernels are shorter than a call's host time); and each repeated on one
+    # source and destination that stay in the cache (a transpose right after
+    # the cast that wrote its source).
+    def rotation(srcs, dsts):
+        i = [0]
+
+        def f():
+            sq.fp8_transpose(srcs[i[0] % len(srcs)], dsts[i[0] % len(dsts)])
+            i[0] += 1
+        return f
+
+    tr = {}
+    for name, srcs, dst in ((f"W8 [{N}x{K}]", [w8] * 64, w8t), (f"dY8 [{M}x{N}]", [dy8] * 16, dyt),
+                            (f"A8 [{M}x{K}]", A8, at)):
+        srcs = [srcs[0]] + [x.clone() for x in srcs[1:]] if srcs[1] is srcs[0] else srcs
+        dsts = [dst] + [torch.empty_like(dst) for _ in range(len(srcs) - 1)]
+        tr[name] = (timed(rotation(srcs, dsts)),
+                    graph_burst(torch, stream, rotation(srcs, dsts), len(srcs)),
+                    graph_burst(torch, stream, lambda: sq.fp8_transpose(srcs[0], dst), args.steps))
+        del srcs, dsts
+    sq.fp8_transpose(w8, w8t)
+    sq.fp8_transpose(dy8, dyt)
+    sq.fp8_transpose(A8[0], at)
+    t_dyc = tr[f"dY8 [{M}x{N}]"][2]
+    t_ac = tr[f"A8 [{M}x{K}]"][2]
     t_dgrad = timed(lambda: sq.fp8_gemm_scaled(dy8, sq.E5M2, w8t, sq.E4M3, sq.PER_TENSOR, si_g,
                                                wsc, dx))
     flops = 2.0 * M * N * K
-    res = {"transpose_ms": {"W8 [768x3072]": round(t_w, 5), "dY8 [16384x768]": round(t_dy, 5),
-                            "A8 [16384x3072]": round(t_a, 5)},
+    res = {"transpose_ms": {k: round(v[0], 5) for k, v in tr.items()},
+           "transpose_graph_replay_ms": {k: round(v[1], 5) for k, v in tr.items()},
+           "transpose_cache_resident_ms": {k: round(v[2], 5) for k, v in tr.items()},
            "dgrad": {"shape": f"dY8[{M}x{N}] e5m2 x W8^T[{K}x{N}] e4m3 -> [{M}x{K}]",
                      "ms": round(t_dgrad, 5), "TFLOP/s": round(flops / (t_dgrad * 1e-3) / 1e12, 1)},
            "wgrad": {"shape": f"dY8^T[{N}x{M}] e5m2 x A8^T[{K}x{M}] e4m3 -> [{N}x{K}]"}}
@@ -563,13 +584,13 @@ def backward(sq, torch, w, A8, w8, wsc, st_a, dy8, st_g, dev, args, H, A16, DY):
         "activation": {"shape": f"H[{M}x{K}] relu2 -> bf16 copy + e4m3 + e4m3^T [{K}x{M}]",
                        "ms": round(t_qa_t, 5),
                        "GB/s": round(M * K * 6 / (t_qa_t * 1e-3) / 1e9, 1),
-                       "cast_then_transpose_ms": round(t_qa + t_a, 5),
-                       "speedup": round((t_qa + t_a) / t_qa_t, 3)},
+                       "cast_then_transpose_ms": round(t_qa + t_ac, 5),
+                       "speedup": round((t_qa + t_ac) / t_qa_t, 3)},
         "gradient": {"shape": f"dY[{M}x{N}] -> e5m2 + e5m2^T [{N}x{M}]",
                      "ms": round(t_qg_t, 5),
                      "GB/s": round(M * N * 4 / (t_qg_t * 1e-3) / 1e9, 1),
-                     "cast_then_transpose_ms": round(t_qg + t_dy, 5),
-                     "speedup": round((t_qg + t_dy) / t_qg_t, 3)}}
+                     "cast_then_transpose_ms": round(t_qg + t_dyc, 5),
+                     "speedup": round((t_qg + t_dyc) / t_qg_t, 3)}}
     t_fused = timed(lambda: sq.fp8_gemm_relu2_backward(dy8, sq.E5M2, w8t, sq.E4M3, si_g, wsc,
                                                        A8[0], sq.CACHE_E4M3, si_a, sq.E5M2,
                                                        st_h, dh8))
@@ -626,7 +647,7 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms, DY)
                             "bytes_per_launch": q_bytes,
                             "vs_per_tensor_quantize": round(q_tensor_ms / q, 3)},
             "quantize_mx_weight_ms": round(qw, 5),
-            "fp8_gemm_mx": {"accum": "exact (block exponents folded into the FP16 widening)",
+            "fp8_gemm_mx": {"accum": "exact (block exponents folded into a BF16 widening, BF16 MFMA)",
                             "ms": round(g, 5), "TFLOP/s": round(tf, 1),
                             "frac_of_fp16_mfma_peak": round(tf / FP16_PEAK_TFLOPS, 4),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
@@ -913,6 +934,21 @@ def burst_median(torch, stream, fn, per_burst):
         torch.cuda.synchronize()
         per.append(a.elapsed_time(b) / per_burst)
     return sorted(per)[2]
+
+
+def graph_burst(torch, stream, fn, per_burst):
+    """ms per launch of fn with no host work between the launches: per_burst
+    launches captured once in a HIP graph, the graph replayed for
+    BURST_WARM_MS, then 5 replays each between two events; the median.  For
+    kernels shorter than a call's host time (a few microseconds), where
+    back-to-back eager launches time the host rather than the kernel."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_burst):
+            fn()
+    return burst_median(torch, stream, g.replay, 1) / per_burst
 
 
 def _upload_bf16(torch, bits, dev):
