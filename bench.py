@@ -649,7 +649,7 @@ def mxfp8(sq, torch, w, H, A16, A8, wt, dev, args, q_tensor_ms, g_tensor_ms, DY)
             "quantize_mx_weight_ms": round(qw, 5),
             "fp8_gemm_mx": {"accum": "exact (block exponents folded into a BF16 widening, BF16 MFMA)",
                             "ms": round(g, 5), "TFLOP/s": round(tf, 1),
-                            "frac_of_fp16_mfma_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+                            "frac_of_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                             "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "vs_per_tensor_gemm": round(g_tensor_ms / g, 3)},
             "fp8_gemm_mx_mfma_fp8": {"ms": round(g8, 5), "TFLOP/s": round(tf8, 1),
@@ -700,7 +700,7 @@ def mx_backward(sq, torch, w, H, A8, wt, DY, dev, args):
                "ms": round(cg, 5), "GB/s": round((3 * M * N + M * N // 32) / (cg * 1e-3) / 1e9, 1)},
            "dgrad": {"shape": f"dY8[{M}x{N}] e5m2 x (W^T)8[{K}x{N}] e4m3 -> [{M}x{K}], MX blocks along {N}",
                      "ms": round(dg, 5), "TFLOP/s": round(tf(dg), 1),
-                     "frac_of_fp16_mfma_peak": round(tf(dg) / FP16_PEAK_TFLOPS, 4)},
+                     "frac_of_bf16_mfma_peak": round(tf(dg) / BF16_PEAK_TFLOPS, 4)},
            "wgrad": {"shape": f"(dY^T)8[{N}x{M}] e5m2 x (A^T)8[{K}x{M}] e4m3 -> [{N}x{K}], MX blocks along the tokens"}}
     for splits in (4, 5, 8):
         ws = torch.empty(splits * N * K, dtype=torch.float32, device=dev)
