@@ -1233,7 +1233,7 @@ def _outside_bound(sq, torch, dev, a8, b8, mode, sa_inv, sb_inv, ref, absref):
     return res
 
 
-QSTEPS, GROWS = 5, 2048   # the timed oracle sample: about 10 s of one host thread
+QSTEPS, GROWS = 7, 4096   # the timed oracle sample: about 13 s of one host thread
 
 
 def cpu_baseline(w, sq, torch, dev):
