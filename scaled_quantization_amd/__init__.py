@@ -111,15 +111,17 @@ def _check(rc: int, name: str) -> None:
         raise Fp8dpError(f"{name} failed ({rc}): {msg}")
 
 
-# The current stream's raw handle without building a torch.cuda.Stream object
-# (that object costs about 3 us per call, half of a call's host time).
+# The current device and its current stream's raw handle without building a
+# torch.cuda.Stream object (that object costs about 3 us per call, half of a
+# call's host time).
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_current_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
 
 
 def _stream(stream) -> int:
     if stream is None:
         if _raw_stream is not None:
-            return _raw_stream(torch.cuda.current_device())
+            return _raw_stream(_current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -139,6 +141,11 @@ def _p(t: Ptr) -> Optional[int]:
         raise Fp8dpError("expected a device tensor")
     if not t.is_contiguous():
         raise Fp8dpError("expected a contiguous tensor")
+    # the kernels run on the current device's stream: a tensor elsewhere would
+    # be read or written across devices
+    if t.get_device() != _current_device():
+        raise Fp8dpError(f"tensor on device {t.get_device()}, the current device is "
+                         f"{_current_device()}: make its device current first")
     return t.data_ptr()
 
 
@@ -227,7 +234,7 @@ def _state_ptr(st) -> Optional[int]:
     if st is None:
         return None
     if isinstance(st, TensorState):
-        return st.ptr
+        return _p(st.buf)
     return _p(st)
 
 

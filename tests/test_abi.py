@@ -327,3 +327,25 @@ def test_binding_checks_every_entry_points_tensors(L):
         sq.fp8dp_convert_f32(torch.zeros(64), 5, u8(64))
     with pytest.raises(sq.Fp8dpError, match="fp8dp_scale_rule: scale: needs"):
         sq.fp8dp_scale_rule(torch.zeros(8), 1.0, sq.E4M3, torch.zeros(4))
+
+
+def test_binding_refuses_a_tensor_on_another_device(monkeypatch):
+    # the kernels run on the current device's stream; a tensor on another
+    # device is refused before any launch
+    class OnDevice1:
+        is_cuda = True
+
+        def is_contiguous(self):
+            return True
+
+        def get_device(self):
+            return 1
+
+        def data_ptr(self):
+            return 4096
+
+    monkeypatch.setattr(sq, "_current_device", lambda: 0)
+    with pytest.raises(sq.Fp8dpError, match="tensor on device 1, the current device is 0"):
+        sq._p(OnDevice1())
+    monkeypatch.setattr(sq, "_current_device", lambda: 1)
+    assert sq._p(OnDevice1()) == 4096
