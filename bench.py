@@ -103,7 +103,7 @@ def main():
     H = [(h0.float() * torch.tensor(f, dtype=torch.float32, device=dev)).to(torch.bfloat16)
          if f != 1.0 else h0.clone() for f in factors]
     del h0
-    n_dy = 4
+    n_dy = 16                     # 16 x 24 MiB of gradients, rotated like H
     dy0 = torch.from_numpy(w.dy().view(np.int16)).to(dev).view(torch.bfloat16)
     DY = [dy0.roll(i * 977, dims=0).contiguous() for i in range(n_dy)]
     del dy0
@@ -116,7 +116,8 @@ def main():
     A16 = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(n_out)]
     A8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(n_out)]
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    DY8 = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    DY8s = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(n_out)]
+    DY8 = DY8s[0]
     st_a = sq.TensorState(sq.E4M3, w.hist_len, w.margin, w.initial_amax, device=dev)
     st_g = sq.TensorState(sq.E5M2, w.hist_len, w.margin, w.initial_amax, device=dev)
     stream = torch.cuda.current_stream()
@@ -143,7 +144,8 @@ def main():
         sq.amax_history_update(st_a)
 
     def dy_cast(i):
-        sq.quantize_fused_update(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2, st_g, None, DY8)
+        sq.quantize_fused_update(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2, st_g, None,
+                                 DY8s[i % n_out])
 
     def step(i):
         quant(i)
@@ -235,7 +237,7 @@ def main():
                                                            st_a, A16[i % n_out], A8[i % n_out]))
     q_pair = burst(lambda i: (quant(i), update_a(i)))
     dy_pair = burst(lambda i: (sq.quantize_fused(DY[i % n_dy], sq.ACT_IDENTITY, sq.E5M2,
-                                                 sq.PER_TENSOR, st_g, None, DY8),
+                                                 sq.PER_TENSOR, st_g, None, DY8s[i % n_out]),
                                sq.amax_history_update(st_g)))
 
     elems = M * K
@@ -318,7 +320,7 @@ def main():
     out["per_group_128"] = per_group(sq, torch, w, H, A16, A8, wt, dev, args, q_mean, g_mean)
     out["fp8_cached_activation"] = fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args,
                                               q_mean)
-    out["graph_step"] = graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8, st_a, st_g, args,
+    out["graph_step"] = graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8s, st_a, st_g, args,
                                    total_ms / args.steps)
     out["recompute_on_overflow"] = recompute(sq, torch, w, H, A8, w8, wsc, Y, st_a, dev, args,
                                              total_ms / args.steps)
@@ -803,7 +805,7 @@ def fp8_cached(sq, torch, np, w, H, A16, A8, st_a, dev, args, q_with_copy_ms):
             "activation_bytes_kept": {"fp8": n, "bf16": 2 * n}}
 
 
-def graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8, st_a, st_g, args, eager_ms):
+def graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8s, st_a, st_g, args, eager_ms):
     """The same step captured in HIP graphs and replayed (no per-kernel host
     launch work): a graph of one step per input/output buffer set, replayed in
     the step's rotation, and one graph of all n steps of the rotation (one
@@ -818,7 +820,7 @@ def graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8, st_a, st_g, args, eag
         sq.fp8_gemm_scaled(A8[i], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
                            st_a.field_ptr("scale_inv"), wsc, Y, sq.ACCUM_EXACT)
         sq.amax_history_update(st_a)
-        sq.quantize_fused_update(DY[i], sq.ACT_IDENTITY, sq.E5M2, st_g, None, DY8)
+        sq.quantize_fused_update(DY[i], sq.ACT_IDENTITY, sq.E5M2, st_g, None, DY8s[i])
 
     graphs = []
     torch.cuda.synchronize()
