@@ -809,10 +809,11 @@ def graph_step(sq, torch, H, A16, A8, w8, wsc, Y, DY, DY8s, st_a, st_g, args, ea
     """The same step captured in HIP graphs and replayed (no per-kernel host
     launch work): a graph of one step per input/output buffer set, replayed in
     the step's rotation, and one graph of all n steps of the rotation (one
-    graph launch per n steps).  A replay is not faster than the eager stream
-    here: the eager launches are queued far ahead of the GPU (the host is not
-    the bottleneck), and the graph's kernel nodes are dispatched with a
-    dependency barrier between consecutive nodes."""
+    graph launch per n steps).  The eager launches are queued far ahead of
+    the GPU (the host is not the bottleneck), so a graph can remove only the
+    gaps between kernels: the graph of one step adds a launch of its own per
+    step and is slower than the eager stream; the graph of all n steps runs
+    about as fast or slightly faster."""
     n = min(len(H), len(A8), len(DY))
 
     def one(i):
