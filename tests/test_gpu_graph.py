@@ -113,3 +113,40 @@ def test_calls_enqueue_on_the_current_stream():
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(dst, src.t().contiguous())
+
+
+def test_step_on_a_side_stream_equals_default_stream():
+    """The step's calls issued inside torch.cuda.stream(s) give the same codes,
+    BF16 copy, GEMM output and state as on the default stream."""
+    rng = np.random.default_rng(5)
+    M, K, N = 512, 1024, 256
+    h = to_dev_bf16((rng.standard_normal((M, K)) * 3).astype(np.float32)
+                    .view(np.uint32).__rshift__(16).astype(np.uint16))
+    wt = to_dev_bf16((rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+                     .view(np.uint32).__rshift__(16).astype(np.uint16))
+
+    def run():
+        w8 = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+        wsc = torch.empty(2, dtype=torch.float32, device=DEV)
+        sq.quantize_weight(wt, sq.E4M3, sq.PER_TENSOR, w8, wsc)
+        st = sq.TensorState(sq.E4M3, 4, 1.25, 10.0)
+        a16 = torch.empty_like(h)
+        a8 = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        for _ in range(3):
+            sq.quantize_fused(h, sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st, a16, a8)
+            sq.fp8_gemm_scaled(a8, sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
+                               st.field_ptr("scale_inv"), wsc, y)
+            sq.amax_history_update(st)
+        return a16, a8, y, st
+
+    r0 = run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        r1 = run()
+    s.synchronize()
+    for a, b in zip(r0[:3], r1[:3]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    assert r0[3].read() == r1[3].read()
