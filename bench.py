@@ -232,6 +232,7 @@ def main():
     dy_mean = burst(dy_cast)
     up_mean = burst(update_a)
     up_graph = graph_burst(torch, stream, lambda: update_a(0), args.steps)
+    smm = scaled_mm_ms(torch, stream, A8, w8, args.steps)
     # the other form of each cast, for comparison (the pair as the step runs it)
     q_fused_upd = burst(lambda i: sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3,
                                                            st_a, A16[i % n_out], A8[i % n_out]))
@@ -301,7 +302,8 @@ def main():
             "accum": "FP8 MFMA (truncates small products in groups of 8)",
             "meets_bound_on_every_output": False,
             "outside_bound_fraction": None,
-            "traffic": measured_traffic("fp8_gemm_scaled_mfma_fp8_gpt2", "gemm.hip")},
+            "traffic": measured_traffic("fp8_gemm_scaled_mfma_fp8_gpt2", "gemm.hip"),
+            "hipblaslt_fp8_scaled_mm": _context_tflops(smm, flops)},
         "burst_ms": bursts,
         "burst_warmup_ms": BURST_WARM_MS,
         "step_clock_settle_steps": settle,
@@ -939,6 +941,32 @@ def burst_median(torch, stream, fn, per_burst):
     return sorted(per)[2]
 
 
+def scaled_mm_ms(torch, stream, A, w8, per_burst):
+    """ms per launch of torch._scaled_mm -- hipBLASLt's FP8 GEMM, the vendor
+    library's -- on the same E4M3 codes (the activations A rotated, the
+    weight w8 [N x K] as its column-major second operand, unit scales),
+    timed like the kernels here; context for the FP8-instruction mode, whose
+    products it truncates as well.  None where this torch build lacks it or
+    refuses the operands."""
+    if not hasattr(torch, "_scaled_mm") or not hasattr(torch, "float8_e4m3fn"):
+        return None
+    one = torch.ones((), dtype=torch.float32, device=w8.device)
+    af = [a.view(torch.float8_e4m3fn) for a in A]
+    wf = w8.view(torch.float8_e4m3fn).t()
+    i = [0]
+
+    def f():
+        torch._scaled_mm(af[i[0] % len(af)], wf, scale_a=one, scale_b=one,
+                         out_dtype=torch.bfloat16)
+        i[0] += 1
+    try:
+        f()
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError):
+        return None
+    return burst_median(torch, stream, f, per_burst)
+
+
 def graph_burst(torch, stream, fn, per_burst):
     """ms per launch of fn with no host work between the launches: per_burst
     launches captured once in a HIP graph, the graph replayed for
@@ -952,6 +980,15 @@ def graph_burst(torch, stream, fn, per_burst):
         for _ in range(per_burst):
             fn()
     return burst_median(torch, stream, g.replay, 1) / per_burst
+
+
+def _context_tflops(ms, flops):
+    """{ms, TFLOP/s, frac_of_fp8_peak} of a context timing, or None."""
+    if ms is None:
+        return None
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+            "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
 
 
 def _upload_bf16(torch, bits, dev):
@@ -1001,6 +1038,7 @@ def large_config(sq, torch, dev, args):
                                           sq.ACCUM_MFMA_FP8), 4)
     dy = timed(lambda: sq.quantize_fused(DY, sq.ACT_IDENTITY, sq.E5M2, sq.PER_TENSOR, st_g, None,
                                          DY8), 16)
+    smm = scaled_mm_ms(torch, stream, [A8], W8, 4)
     qb, dyb, fl = M * K * 5, M * N * 3, 2 * M * N * K
     tf = lambda ms: fl / (ms * 1e-3) / 1e12
     out = {"shape": f"H[{M}x{K}] relu2 -> bf16 copy + e4m3; Y[{M}x{N}] = A8 x W8[{N}x{K}]^T; "
@@ -1012,7 +1050,8 @@ def large_config(sq, torch, dev, args):
                                "frac_of_fp16_mfma_peak": round(tf(gm) / FP16_PEAK_TFLOPS, 4),
                                "frac_of_fp8_peak": round(tf(gm) / FP8_PEAK_TFLOPS, 4)},
            "fp8_gemm_scaled_mfma_fp8": {"ms": round(g8, 4), "TFLOP/s": round(tf(g8), 1),
-                                        "frac_of_fp8_peak": round(tf(g8) / FP8_PEAK_TFLOPS, 4)},
+                                        "frac_of_fp8_peak": round(tf(g8) / FP8_PEAK_TFLOPS, 4),
+                                        "hipblaslt_fp8_scaled_mm": _context_tflops(smm, fl)},
            "quantize_fused_dy_e5m2": {"ms": round(dy, 4),
                                       "GB/s": round(dyb / (dy * 1e-3) / 1e9, 1),
                                       "frac_of_hbm_peak": round(dyb / (dy * 1e-3) / 1e9
