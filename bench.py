@@ -70,7 +70,7 @@ def parse():
                         "one (65 tensors 4096 x 4096)")
     p.add_argument("--only", choices=("quantize", "quantize_update", "quantize_t", "gemm",
                                       "gemm_fp8", "copy", "quantize_mx", "gemm_mx", "relu2_bwd",
-                                      "gemm_pg"), default=None,
+                                      "gemm_pg", "transpose", "quantize_mx_t"), default=None,
                    help="launch only this kernel of the step, --steps times, on the same "
                         "inputs (for hardware counter runs), then exit")
     return p.parse_args()
@@ -341,7 +341,9 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
     """One kernel of the step, repeated with the step's own rotation of inputs
     and outputs; a profiler's per-dispatch counters then describe exactly the
     launches the timed steps make (the MX and activation-backward legs the
-    same way as their bench legs)."""
+    same way as their bench legs; the transpose of A8 and the MX cast with
+    the blocks down the columns into 8 rotating destination sets, like the
+    bench's transposes from HBM)."""
     M, K, N = w.M, w.K, w.N
     # one step first, so the delayed scale is the one this data produces (as in
     # the timed steps, which follow the warm-up)
@@ -364,6 +366,11 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
                               A8[j], GS[j])
     if args.only == "quantize_t":
         AT = [torch.empty((K, M), dtype=torch.uint8, device=dev) for _ in range(2)]
+    if args.only in ("transpose", "quantize_mx_t"):
+        AT8 = [torch.empty((K, M), dtype=torch.uint8, device=dev) for _ in range(n_out)]
+        ET = [torch.empty((K, M // 32), dtype=torch.uint8, device=dev) for _ in range(n_out)]
+        for j in range(n_out):
+            sq.quantize_fused(H[j % n_in], sq.ACT_RELU2, sq.E4M3, sq.PER_TENSOR, st_a, None, A8[j])
     if args.only == "relu2_bwd":
         dA = torch.from_numpy(w.da().view(np.int16)).to(dev).view(torch.bfloat16)
         dH8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(2)]
@@ -392,6 +399,11 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
         elif args.only == "quantize_t":
             sq.quantize_fused_transposed(H[i % n_in], sq.ACT_RELU2, sq.E4M3, st_a, AT[i % 2],
                                          A16[i % n_out], A8[i % n_out])
+        elif args.only == "transpose":
+            sq.fp8_transpose(A8[i % n_out], AT8[i % n_out])
+        elif args.only == "quantize_mx_t":
+            sq.quantize_mx_transposed(H[i % n_in], sq.ACT_RELU2, sq.E4M3, AT8[i % n_out],
+                                      ET[i % n_out])
         elif args.only == "quantize_update":
             sq.quantize_fused_update(H[i % n_in], sq.ACT_RELU2, sq.E4M3, st_a, A16[i % n_out],
                                      A8[i % n_out])
