@@ -411,9 +411,11 @@ def kernel_only(sq, torch, np, w, args, H, A16, A8, w8, wsc, wt, Y, st_a, n_in, 
             sq.fp8_gemm_scaled(A8[i % n_out], sq.E4M3, w8, sq.E4M3, sq.PER_TENSOR,
                                st_a.field_ptr("scale_inv"), wsc, Y,
                                sq.ACCUM_EXACT if args.only == "gemm" else sq.ACCUM_MFMA_FP8)
-        else:
+        elif args.only == "copy":
             copy_buffers(torch, dev)
             sq.fp8dp_bench_copy(*_COPY[i % 2])
+        else:
+            raise SystemExit(f"--only {args.only}: no launch defined")
     torch.cuda.synchronize()
     print(json.dumps({"only": args.only, "launches": args.warmup + args.steps}), flush=True)
 

@@ -73,3 +73,16 @@ def test_traffic_record_arithmetic(path):
     assert abs(r["ratio_to_algorithmic"] - r["bytes_per_launch"] / r["algorithmic_bytes_per_launch"]) < 1e-3
     # no kernel moves less than its algorithmic bytes
     assert r["ratio_to_algorithmic"] > 0.99
+
+
+def test_every_only_mode_has_its_own_launch():
+    # bench.py --only <mode> launches one kernel for counter runs; a mode
+    # without a branch of its own in kernel_only would stop with an error
+    import re
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    choices = re.search(r'"--only", choices=\(([^)]*)\)', src).group(1)
+    modes = [c.strip().strip('"') for c in choices.replace("\n", "").split(",") if c.strip()]
+    body = src[src.index("def kernel_only"):src.index("_COPY = []")]
+    assert len(modes) >= 12
+    for m in modes:
+        assert f'args.only == "{m}"' in body or re.search(rf'args\.only in \([^)]*"{m}"', body), m
