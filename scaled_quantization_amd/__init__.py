@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import struct
 from typing import Optional, Union
@@ -196,6 +197,15 @@ class TensorState:
         return self.buf.cpu().numpy().tobytes()
 
 
+def _rows_cols(t) -> tuple:
+    """(rows, cols) of a tensor read as rows of its trailing elements (1-D: one
+    row), without building a view (t[0] costs a microsecond per call)."""
+    if t.dim() == 1:
+        return 1, t.numel()
+    r = t.shape[0]
+    return r, (t.numel() // r if r else math.prod(t.shape[1:]))
+
+
 def _room(t, nbytes: int, what: str) -> None:
     """Refuse a tensor argument smaller than the nbytes the call writes or reads."""
     if isinstance(t, torch.Tensor) and t.numel() * t.element_size() < nbytes:
@@ -252,7 +262,7 @@ def quantize_fused(h: torch.Tensor, act: int, fmt: int, mode: int, st=None,
     _elem(h, (2,), "quantize_fused: h")
     _elem(bf16_out, (2,), "quantize_fused: bf16_out")
     _codes(fp8_out, "quantize_fused: fp8_out")
-    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    rows, cols = _rows_cols(h)
     _room(bf16_out, rows * cols * 2, "quantize_fused: bf16_out")
     _room(fp8_out, rows * cols, "quantize_fused: fp8_out")
     if mode == PER_GROUP128:
@@ -272,7 +282,7 @@ def quantize_fused_update(h: torch.Tensor, act: int, fmt: int, st, bf16_out: Ptr
     _elem(h, (2,), "quantize_fused_update: h")
     _elem(bf16_out, (2,), "quantize_fused_update: bf16_out")
     _codes(fp8_out, "quantize_fused_update: fp8_out")
-    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    rows, cols = _rows_cols(h)
     _room(bf16_out, rows * cols * 2, "quantize_fused_update: bf16_out")
     _room(fp8_out, rows * cols, "quantize_fused_update: fp8_out")
     _check(lib().quantize_fused_update(_p(h), rows, cols, act, fmt, _state_ptr(st), _p(bf16_out),
@@ -365,7 +375,7 @@ def relu2_backward_quantize(dA: torch.Tensor, a_cache: torch.Tensor, cache: int,
         _codes(a_cache, "relu2_backward_quantize: a_cache")
     _codes(fp8_out, "relu2_backward_quantize: fp8_out")
     _elem(bf16_out, (2,), "relu2_backward_quantize: bf16_out")
-    rows, cols = (1, dA.numel()) if dA.dim() == 1 else (dA.shape[0], dA[0].numel())
+    rows, cols = _rows_cols(dA)
     if a_cache.numel() != dA.numel() or fp8_out.numel() != dA.numel():
         raise Fp8dpError("relu2_backward_quantize: size mismatch")
     _room(bf16_out, rows * cols * 2, "relu2_backward_quantize: bf16_out")
@@ -397,7 +407,7 @@ def quantize_recompute(h: torch.Tensor, act: int, fmt: int, st, fp8_out: torch.T
     (decided on the GPU; otherwise nothing is written)."""
     _elem(h, (2,), "quantize_recompute: h")
     _codes(fp8_out, "quantize_recompute: fp8_out")
-    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    rows, cols = _rows_cols(h)
     _room(fp8_out, rows * cols, "quantize_recompute: fp8_out")
     _check(lib().quantize_recompute(_p(h), rows, cols, act, fmt, _state_ptr(st), _p(fp8_out),
                                     _stream(stream)), "quantize_recompute")
@@ -424,7 +434,7 @@ def quantize_mx(h: torch.Tensor, act: int, fmt: int, fp8_out: torch.Tensor,
     _codes(fp8_out, "quantize_mx: fp8_out")
     _codes(scale_out, "quantize_mx: scale_out")
     _elem(bf16_out, (2,), "quantize_mx: bf16_out")
-    rows, cols = (1, h.numel()) if h.dim() == 1 else (h.shape[0], h[0].numel())
+    rows, cols = _rows_cols(h)
     if fp8_out.numel() != rows * cols or scale_out.numel() * 32 != rows * cols:
         raise Fp8dpError("quantize_mx: output sizes do not match the input")
     _room(bf16_out, rows * cols * 2, "quantize_mx: bf16_out")

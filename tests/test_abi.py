@@ -349,3 +349,12 @@ def test_binding_refuses_a_tensor_on_another_device(monkeypatch):
         sq._p(OnDevice1())
     monkeypatch.setattr(sq, "_current_device", lambda: 1)
     assert sq._p(OnDevice1()) == 4096
+
+
+def test_rows_cols_of_a_tensor():
+    # rows x cols as the element-wise calls read a tensor: 1-D is one row,
+    # more dimensions are rows of their trailing elements; no view is built
+    import torch
+    cases = {(10,): (1, 10), (4, 6): (4, 6), (3, 2, 5): (3, 10), (0, 7): (0, 7), (0, 2, 3): (0, 6)}
+    for shape, want in cases.items():
+        assert sq._rows_cols(torch.empty(shape)) == want, shape
